@@ -1,0 +1,318 @@
+"""CPU oracle for the per-layer cached denoising step (plain C in fp64, ctypes binding).
+
+TEST INFRASTRUCTURE.  Only ``tests/``, the smoke check in ``__graft_entry__`` and the
+benchmark's ``cpu_baseline`` leg import this package.  It shares no code with the HIP library
+(``diffusion_kv_cache_amd``) and neither side imports the other; the only common module is the
+seeded input generator ``synth``.
+
+The low-level routines live in ``oracle.c`` (each cites the passage it follows).  This module
+composes them into the step the pages describe:
+
+* O1/O2  project the refreshed hidden rows and rotate q and k (``qkv_rows``);
+* O3     prefill: fill every cache row from the previous hidden states (``prefill``);
+* O4     cached step: recompute only the refresh rows from the current hidden states and
+         overwrite those cache rows, leaving every other row as it was (``cached_step``)
+         -- LaCache's lossless state memoisation: reusing rows whose inputs did not change
+         gives exactly the full recompute (LaCache Technical Summary, Methodology 1);
+* O5/O6  attention of the refreshed rows' queries over the whole cache, log-sum-exp and the
+         column attention mass (``attention``);
+* O8-O10 top-k tracking set, drift test and tracking-buffer refill (``drift``, ``topk``,
+         ``track``), after Elastic-Cache's core idea.
+
+"Storage" rounding: the cache holds K/V in its own dtype (fp32, bf16, or e4m3 codes with one
+fp32 scale per 128-value row) and Q is handed to attention in the activation dtype.  The oracle
+computes in fp64 and rounds exactly where the method stores a value.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+ROUND_MODE = {"f64": 0, "f32": 1, "bf16": 2}
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with the host C compiler (no HIP headers, no fused multiply-add)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+                               "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.orc_round_bf16.restype = f64
+        lib.orc_round_bf16.argtypes = [f64]
+        lib.orc_round.argtypes = [P, i64, i32]
+        lib.orc_e4m3_decode.restype = f64
+        lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.orc_e4m3_encode.restype = ctypes.c_uint8
+        lib.orc_e4m3_encode.argtypes = [f64]
+        lib.orc_e4m3_encode_array.argtypes = [P, i64, P]
+        lib.orc_e4m3_decode_array.argtypes = [P, i64, P]
+        lib.orc_fp8_quantize_rows.argtypes = [P, i64, i32, P, P, P]
+        lib.orc_linear.argtypes = [P, i64, i64, P, P, i64, P]
+        lib.orc_rope_rows.argtypes = [P, i64, i32, i32, P, f64]
+        lib.orc_attention.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f64, P, P, P]
+        lib.orc_topk.argtypes = [P, i64, i32, i32, P]
+        lib.orc_drift.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f64, P, P]
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------------------------------
+# Low-level routines
+# ------------------------------------------------------------------------------------------
+
+def round_bf16_scalar(x: float) -> float:
+    return _load().orc_round_bf16(float(x))
+
+
+def round_storage(x: np.ndarray, mode: str) -> np.ndarray:
+    """Copy of x (float64) rounded to fp32 / bf16 (round to nearest even)."""
+    y = _c(x, np.float64).copy()
+    _load().orc_round(_p(y), y.size, ROUND_MODE[mode])
+    return y
+
+
+def e4m3_encode(x) -> np.ndarray:
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_e4m3_encode_array(_p(x), x.size, _p(out))
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_e4m3_decode_array(_p(c), c.size, _p(out))
+    return out
+
+
+def fp8_quantize_rows(x: np.ndarray):
+    """x: [..., G] float64 -> (codes uint8 [..., G], scales float32 [...], dequant float64)."""
+    x = _c(x, np.float64)
+    G = x.shape[-1]
+    rows = x.size // G
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.empty(x.shape[:-1], np.float32)
+    deq = np.empty(x.shape, np.float64)
+    _load().orc_fp8_quantize_rows(_p(x), rows, G, _p(codes), _p(scales), _p(deq))
+    return codes, scales, deq
+
+
+def linear(x: np.ndarray, w: np.ndarray, wrows) -> np.ndarray:
+    """y[r, j] = sum_k x[r, k] w[wrows[j], k] (fp64, ascending k)."""
+    x = _c(x, np.float32)
+    w = _c(w, np.float32)
+    wrows = _c(wrows, np.int32)
+    R, H = x.shape
+    assert w.shape[1] == H and (wrows.size == 0 or (wrows.min() >= 0 and wrows.max() < w.shape[0]))
+    y = np.empty((R, wrows.size), np.float64)
+    _load().orc_linear(_p(x), R, H, _p(w), _p(wrows), wrows.size, _p(y))
+    return y
+
+
+def rope(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Rotate-half rotary embedding of x: [R, nh, D] at positions pos: [R] (returns a copy)."""
+    y = _c(x, np.float64).copy()
+    pos = _c(pos, np.int32)
+    R, nh, D = y.shape
+    assert pos.shape == (R,) and D % 2 == 0
+    _load().orc_rope_rows(_p(y), R, nh, D, _p(pos), float(base))
+    return y
+
+
+def attention(q, k, v, scale: float, want_lse=True, want_mass=False):
+    """q: [B, n, Hq, D]; k, v: [B, Hkv, S, D] -> (out [B,n,Hq,D], lse [B,Hq,n], mass [B,Hq,S])."""
+    q = _c(q, np.float64)
+    k = _c(k, np.float64)
+    v = _c(v, np.float64)
+    B, n, Hq, D = q.shape
+    _, Hkv, S, _ = k.shape
+    assert k.shape == v.shape == (B, Hkv, S, D) and Hq % Hkv == 0 and S >= 1
+    out = np.empty_like(q)
+    lse = np.empty((B, Hq, n), np.float64) if want_lse else None
+    mass = np.empty((B, Hq, S), np.float64) if want_mass else None
+    _load().orc_attention(_p(q), _p(k), _p(v), B, n, Hq, Hkv, S, D, float(scale), _p(out),
+                          _p(lse), _p(mass))
+    return out, lse, mass
+
+
+def topk(a: np.ndarray, k: int) -> np.ndarray:
+    """a: [..., S] -> [..., k] int32: the k largest by (value desc, index asc), index-sorted."""
+    a = _c(a, np.float64)
+    S = a.shape[-1]
+    P = a.size // S if S else 0
+    T = np.empty(a.shape[:-1] + (k,), np.int32)
+    _load().orc_topk(_p(a), P, S, k, _p(T))
+    return T
+
+
+def drift(buf, T, kc, vc, gamma: float):
+    """buf: [B,Hq,k,2,D], T: [B,Hq,k], kc/vc: [B,Hkv,S,D] -> (sigma [B,Hq], refresh [B] uint8)."""
+    buf = _c(buf, np.float64)
+    T = _c(T, np.int32)
+    kc = _c(kc, np.float64)
+    vc = _c(vc, np.float64)
+    B, Hq, k = T.shape
+    _, Hkv, S, D = kc.shape
+    assert buf.shape == (B, Hq, k, 2, D) and vc.shape == kc.shape
+    sigma = np.empty((B, Hq), np.float64)
+    refresh = np.empty((B,), np.uint8)
+    _load().orc_drift(_p(buf), _p(T), _p(kc), _p(vc), B, Hq, Hkv, S, D, k, float(gamma),
+                      _p(sigma), _p(refresh))
+    return sigma, refresh
+
+
+# ------------------------------------------------------------------------------------------
+# The step, composed
+# ------------------------------------------------------------------------------------------
+
+def head_rows(wl, part: str, heads=None) -> np.ndarray:
+    """Rows of W_qkv ([Q heads | K heads | V heads] x D) for the given heads of one part."""
+    D = wl.head_dim
+    base = {"q": 0, "k": wl.q_heads, "v": wl.q_heads + wl.kv_heads}[part]
+    count = wl.q_heads if part == "q" else wl.kv_heads
+    heads = range(count) if heads is None else heads
+    return np.concatenate([np.arange((base + h) * D, (base + h + 1) * D) for h in heads]) \
+        .astype(np.int32) if len(heads) else np.zeros(0, np.int32)
+
+
+def qkv_rows(x_rows: np.ndarray, pos, w: np.ndarray, wl, part: str, heads=None) -> np.ndarray:
+    """O1 + O2: the given part ('q', 'k' or 'v') of rows x_rows [R, H] at positions pos [R],
+    as [R, nheads, D] float64; q and k rotated, v as projected."""
+    count = wl.q_heads if part == "q" else wl.kv_heads
+    nh = count if heads is None else len(heads)
+    y = linear(x_rows, w, head_rows(wl, part, heads)).reshape(len(x_rows), nh, wl.head_dim)
+    if part in ("q", "k"):
+        y = rope(y, pos, wl.rope_base)
+    return y
+
+
+def store_rows(x: np.ndarray, dtype: str):
+    """Round K/V rows [..., D] as the cache stores them.  Returns (values, codes, scales);
+    codes/scales are None except for the fp8 cache."""
+    if dtype == "fp8":
+        codes, scales, deq = fp8_quantize_rows(x)
+        return deq, codes, scales
+    return round_storage(x, dtype), None, None
+
+
+class Cache:
+    """K and V [B, Hkv, S, D] as stored (float64 holding storage values), plus fp8 codes
+    and scales for the fp8 cache."""
+
+    def __init__(self, wl):
+        B, Hkv, S, D = wl.batch, wl.kv_heads, wl.seq, wl.head_dim
+        self.wl = wl
+        self.k = np.zeros((B, Hkv, S, D))
+        self.v = np.zeros((B, Hkv, S, D))
+        if wl.cache == "fp8":
+            self.k_codes = np.zeros((B, Hkv, S, D), np.uint8)
+            self.v_codes = np.zeros((B, Hkv, S, D), np.uint8)
+            self.k_scale = np.zeros((B, Hkv, S), np.float32)
+            self.v_scale = np.zeros((B, Hkv, S), np.float32)
+
+    def copy(self):
+        c = Cache.__new__(Cache)
+        c.__dict__ = {k: (v.copy() if isinstance(v, np.ndarray) else v)
+                      for k, v in self.__dict__.items()}
+        return c
+
+    def write_rows(self, b: int, rows, kx: np.ndarray, vx: np.ndarray):
+        """Write K/V rows for sequence b at positions rows; kx/vx: [R, Hkv, D] float64."""
+        rows = np.asarray(rows)
+        for name, x in (("k", kx), ("v", vx)):
+            vals, codes, scales = store_rows(x, self.wl.cache)
+            getattr(self, name)[b][:, rows] = vals.transpose(1, 0, 2)
+            if codes is not None:
+                getattr(self, name + "_codes")[b][:, rows] = codes.transpose(1, 0, 2)
+                getattr(self, name + "_scale")[b][:, rows] = scales.T
+
+
+def refresh_rows(cache: Cache, hidden: np.ndarray, w: np.ndarray, idx, batches=None,
+                 kv_heads=None):
+    """O4: recompute the K/V rows idx[b] of every sequence from hidden [B, S, H] and write
+    them into the cache.  Every other row is left as it is."""
+    wl = cache.wl
+    batches = range(wl.batch) if batches is None else batches
+    for b in batches:
+        rows = np.asarray(idx[b], dtype=np.int32)
+        x = hidden[b, rows]
+        kx = qkv_rows(x, rows, w, wl, "k", kv_heads)
+        vx = qkv_rows(x, rows, w, wl, "v", kv_heads)
+        if kv_heads is not None and len(kv_heads) != wl.kv_heads:
+            full_k = np.zeros((len(rows), wl.kv_heads, wl.head_dim))
+            full_v = np.zeros_like(full_k)
+            full_k[:, list(kv_heads)] = kx
+            full_v[:, list(kv_heads)] = vx
+            kx, vx = full_k, full_v
+        cache.write_rows(b, rows, kx, vx)
+    return cache
+
+
+def prefill(wl, hidden: np.ndarray, w: np.ndarray, batches=None, kv_heads=None) -> Cache:
+    """O3: fill every cache row from hidden [B, S, H] (the first step of a block)."""
+    cache = Cache(wl)
+    all_rows = np.tile(np.arange(wl.seq, dtype=np.int32), (wl.batch, 1))
+    return refresh_rows(cache, hidden, w, all_rows, batches, kv_heads)
+
+
+def queries(wl, hidden: np.ndarray, w: np.ndarray, idx, batches=None, q_heads=None):
+    """Q of the refreshed rows, [B, n, Hq, D], rounded to the activation dtype."""
+    B, n = idx.shape
+    nh = wl.q_heads if q_heads is None else len(q_heads)
+    q = np.zeros((B, n, nh, wl.head_dim))
+    batches = range(B) if batches is None else batches
+    for b in batches:
+        rows = np.asarray(idx[b], dtype=np.int32)
+        q[b] = qkv_rows(hidden[b, rows], rows, w, wl, "q", q_heads)
+    return round_storage(q, wl.act)
+
+
+def attend(wl, q: np.ndarray, cache: Cache, want_mass=False):
+    """O5/O6 over the stored cache values: (out, lse, mass); out is left in float64."""
+    return attention(q, cache.k, cache.v, 1.0 / math.sqrt(wl.head_dim), True, want_mass)
+
+
+def track(cache: Cache, mass: np.ndarray, k: int):
+    """O8 + O10: T = top-k of the mass per (b, h); buffer = the cache rows at T, [B,Hq,k,2,D]."""
+    wl = cache.wl
+    T = topk(mass, k)
+    B, Hq = T.shape[:2]
+    G = wl.q_heads // wl.kv_heads
+    buf = np.zeros((B, Hq, k, 2, wl.head_dim))
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(k):
+                j = T[b, h, t]
+                if j >= 0:
+                    buf[b, h, t, 0] = cache.k[b, h // G, j]
+                    buf[b, h, t, 1] = cache.v[b, h // G, j]
+    return T, buf
