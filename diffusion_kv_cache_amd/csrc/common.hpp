@@ -1,0 +1,107 @@
+// Device-side helpers shared by the gfx950 kernels of the cached denoising step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dllm_cache.h"
+
+namespace dllm {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+
+constexpr int kWave = 64;
+// Fixed number of K-partitions of the projection: every output element is
+// (((0 + P0) + P1) + ... + P7), each Pp an MFMA chain over its partition in ascending k.
+constexpr int kKSplit = 8;
+
+enum CacheKind : int { kCacheF32 = DLLM_F32, kCacheBF16 = DLLM_BF16, kCacheFP8 = DLLM_FP8_E4M3 };
+
+// ------------------------------------------------------------------------ conversions ---
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// fp32 -> OCP E4M3 ("fn") code: round to nearest even, saturate to +-448, NaN -> 0x7f|sign.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;            // |x| >= 448 (incl. inf)
+  if (a >= 0x3c800000u) {                               // |x| >= 2^-6: normal range
+    uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
+    uint32_t code = r - (120u << 3);                    // rebias exponent 127 -> 7
+    return sign | (code > 0x7eu ? 0x7eu : code);
+  }
+  float m = rintf(__uint_as_float(a) * 512.0f);         // subnormal: m * 2^-9, m in 0..8
+  return sign | (uint32_t)m;
+}
+
+// Four E4M3 codes (one 32-bit word, byte 0 first) -> four bf16 values (exact: every E4M3
+// value is a bf16 value), via the hardware packed conversion with unit scale.
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  lo = __builtin_bit_cast(uint32_t, a);
+  hi = __builtin_bit_cast(uint32_t, b);
+}
+
+// --------------------------------------------------------------------------- MFMA -------
+
+// D(16x16, fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l supplies A row l%16 and B column
+// l%16, eight K values each (slot group l/16); it receives D rows 4*(l/16)..+3 of column l%16.
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Same shape with K = 4 in fp32: lane l supplies A[l%16][l/16] and B[l/16][l%16].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ------------------------------------------------------------------------ reductions ----
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+// ------------------------------------------------------------------------ rotary --------
+
+// Turns of rotary pair i: t_i = base^(-2i/D) / (2 pi), split into two floats (hi + lo).
+__device__ __forceinline__ void rope_turns(int i, int D, double base, float& hi, float& lo) {
+  double t = pow(base, -2.0 * (double)i / (double)D) * 0.15915494309189533577;  // 1/(2 pi)
+  hi = (float)t;
+  lo = (float)(t - (double)hi);
+}
+
+// sin and cos of the angle 2 pi * pos * (hi + lo).  The product pos * hi is split exactly
+// (fma), its integer turns are dropped exactly, and the hardware sin/cos (argument in turns)
+// see a fraction in [-0.5, 0.5].
+__device__ __forceinline__ void rope_sincos(int pos, float hi, float lo, float& s, float& c) {
+  float p = (float)pos;
+  float a = p * hi;
+  float e = fmaf(p, hi, -a);
+  float f = (a - rintf(a)) + (e + p * lo);
+  s = __builtin_amdgcn_sinf(f);
+  c = __builtin_amdgcn_cosf(f);
+}
+
+}  // namespace dllm

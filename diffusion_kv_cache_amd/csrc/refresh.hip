@@ -1,0 +1,413 @@
+// Fused refresh kernel: gather the refreshed hidden rows, QKV projection on MFMA, rotary
+// embedding in registers, scatter of K/V rows into the flat cache (optionally as per-row FP8),
+// compact Q out.  One launch per layer step; no intermediate touches HBM.
+//
+// What it computes: Flash-dLLM news summary (skillfed.io), memory paragraph -- projection,
+// RoPE and cache write in one kernel with on-chip intermediates; LaCache (gist.science),
+// Technical Summary, Methodology 1 -- only rows outside the invariant region are recomputed,
+// RoPECache holds post-projection, post-RoPE states; Methodology 2 -- 1 x 128 FP8 groups.
+//
+// Reduction order (identical in both kernels below, for any M and tiling): each output
+// element is (((0 + P0) + P1) + ... + P7), where Pp is the chain of 16x16 MFMAs over the p-th
+// eighth of H in ascending k, each MFMA taking k0..k0+31 (bf16) or k0..k0+3 (fp32) with lane
+// group l/16 holding the slots k0 + 8(l/16) .. +7 (bf16) or k0 + l/16 (fp32).  A row's
+// result is therefore independent of n and of the other rows: a step stores exactly what a
+// refresh of all S rows would.
+//
+// Rotary pairing (i, i + D/2): every wave owns column tiles in pairs (c, c + D/2), so both
+// members of a pair sit in the same lane and register of the MFMA accumulator and the
+// rotation needs no data exchange.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dllm {
+namespace {
+
+__device__ __forceinline__ size_t hidden_row_offset(const RefreshArgs& a, int m) {
+  const int b = m / a.n;
+  return ((size_t)b * a.S + (size_t)a.idx[m]) * (size_t)a.H;
+}
+
+// Destination of output row m (= b * n + i) of head slot j; element type chosen by caller.
+__device__ __forceinline__ size_t out_row_offset(const RefreshArgs& a, int m, int j, int& which) {
+  const int b = m / a.n;
+  if (j < a.Hq) {
+    which = 0;
+    return ((size_t)m * a.Hq + j) * (size_t)a.D;
+  }
+  const int pos = a.idx[m];
+  const int g = (j < a.Hq + a.Hkv) ? j - a.Hq : j - a.Hq - a.Hkv;
+  which = (j < a.Hq + a.Hkv) ? 1 : 2;
+  return (((size_t)b * a.Hkv + g) * a.S + pos) * (size_t)a.D;
+}
+
+// ------------------------------------------------------------------------------------------
+// Skinny kernel (bf16 activations, bf16 cache, small M): one workgroup per 32-column strip
+// (16 rotary pairs) and 32 rows, eight waves, wave p reducing the p-th eighth of H straight
+// from global memory; partials combined in LDS in partition order.  Spreads the weight stream
+// of a small-M step over (N / 32) x 8 waves.
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(512) void refresh_skinny(RefreshArgs a) {
+  constexpr int STRIPS = D / 32;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int j = blockIdx.x / STRIPS, sub = blockIdx.x % STRIPS;
+  const int m0 = blockIdx.y * 32;
+  const int Lp = a.H / kKSplit;
+  const int kb = wave * Lp;
+
+  const bf16_t* hid = (const bf16_t*)a.hidden;
+  const bf16_t* w = (const bf16_t*)a.w;
+  const bf16_t* arow[2];
+  bool aval[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int m = m0 + rt * 16 + l16;
+    aval[rt] = m < a.M;
+    arow[rt] = hid + hidden_row_offset(a, aval[rt] ? m : 0) + kb + lg * 8;
+  }
+  const bf16_t* wrow[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+    wrow[ct] = w + (size_t)(j * D + ct * (D / 2) + sub * 16 + l16) * a.H + kb + lg * 8;
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  for (int k = 0; k < Lp; k += 32) {
+    uint4 av[2], bv[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) av[rt] = *(const uint4*)(arow[rt] + k);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) bv[ct] = *(const uint4*)(wrow[ct] + k);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const uint4 x = aval[rt] ? av[rt] : zero;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = mfma_bf16(as_bf16x8(x), as_bf16x8(bv[ct]), acc[rt][ct]);
+    }
+  }
+
+  __shared__ f32x4 red[kKSplit][2][2][64];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) red[wave][rt][ct][lane] = acc[rt][ct];
+  __syncthreads();
+  if (wave >= 2) return;
+
+  const int rt = wave;
+  f32x4 tot[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    tot[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < kKSplit; ++p) tot[ct] = tot[ct] + red[p][rt][ct][lane];
+  }
+
+  const bool rot = j < a.Hq + a.Hkv;
+  const int pair = sub * 16 + l16;
+  float th_hi = 0.f, th_lo = 0.f;
+  if (rot) rope_turns(pair, D, a.rope_base, th_hi, th_lo);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int m = m0 + rt * 16 + lg * 4 + v;
+    if (m >= a.M) continue;
+    float x = tot[0][v], y = tot[1][v];
+    if (rot) {
+      float s, c;
+      rope_sincos(a.idx[m], th_hi, th_lo, s, c);
+      const float x2 = x * c - y * s, y2 = y * c + x * s;
+      x = x2;
+      y = y2;
+    }
+    int which;
+    const size_t off = out_row_offset(a, m, j, which);
+    bf16_t* dst = which == 0 ? (bf16_t*)a.q_out : which == 1 ? (bf16_t*)a.kc : (bf16_t*)a.vc;
+    dst[off + pair] = f32_to_bf16(x);
+    dst[off + pair + D / 2] = f32_to_bf16(y);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Tiled kernel: one workgroup per (TM rows) x (one head = D columns), four waves as 2 (rows)
+// x 2 (rotary-pair column groups).  A (gathered hidden rows) and W tiles go through LDS,
+// double buffered, with chunk = c ^ (row % 8) swizzling.  The finished tile is rotated in
+// registers, staged as fp32 in LDS and written as whole cache rows (16-byte stores, or per-row
+// FP8 with its scale).
+// ------------------------------------------------------------------------------------------
+template <typename T, int KIND, int TM, int D, int BKC>
+__global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int BK = BKC * EPC;              // elements of K per stage
+  constexpr int RT = TM / 32;                // 16-row tiles per wave
+  constexpr int CT = D / 32;                 // 16-column tiles per wave
+  constexpr int CH = CT / 2;
+  constexpr int A_PER_T = TM * BKC / 256;
+  constexpr int W_PER_T = D * BKC / 256;
+  static_assert(A_PER_T >= 1 && W_PER_T >= 1, "tile too small for 256 threads");
+  constexpr int STAGE = (TM + D) * BKC * 16;
+  constexpr int EPI_STRIDE = D + 4;
+  constexpr int EPI = TM * EPI_STRIDE * 4;
+  constexpr int SMEM = (2 * STAGE > EPI) ? 2 * STAGE : EPI;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int j = blockIdx.x;
+  const int m0 = blockIdx.y * TM;
+
+  const T* hid = (const T*)a.hidden;
+  const T* w = (const T*)a.w;
+  const int cchunk = t % BKC;
+
+  // Global sources of this thread's chunks (fixed rows; k advances).
+  const T* asrc[A_PER_T];
+  bool aval[A_PER_T];
+#pragma unroll
+  for (int u = 0; u < A_PER_T; ++u) {
+    const int r = t / BKC + u * (256 / BKC);
+    const int m = m0 + r;
+    aval[u] = m < a.M;
+    asrc[u] = hid + hidden_row_offset(a, aval[u] ? m : 0) + cchunk * EPC;
+  }
+  const T* wsrc[W_PER_T];
+#pragma unroll
+  for (int u = 0; u < W_PER_T; ++u) {
+    const int c = t / BKC + u * (256 / BKC);
+    wsrc[u] = w + (size_t)(j * D + c) * a.H + cchunk * EPC;
+  }
+
+  uint4 areg[A_PER_T], wreg[W_PER_T];
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  auto load_stage = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < A_PER_T; ++u) {
+      const uint4 x = *(const uint4*)(asrc[u] + k0);
+      areg[u] = aval[u] ? x : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < W_PER_T; ++u) wreg[u] = *(const uint4*)(wsrc[u] + k0);
+  };
+  auto store_stage = [&](int buf) {
+    char* A = smem + buf * STAGE;
+    char* W = A + TM * BKC * 16;
+#pragma unroll
+    for (int u = 0; u < A_PER_T; ++u) {
+      const int r = t / BKC + u * (256 / BKC);
+      *(uint4*)(A + (r * BKC + (cchunk ^ (r & (BKC - 1)))) * 16) = areg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < W_PER_T; ++u) {
+      const int c = t / BKC + u * (256 / BKC);
+      *(uint4*)(W + (c * BKC + (cchunk ^ (c & (BKC - 1)))) * 16) = wreg[u];
+    }
+  };
+
+  int colv[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+    colv[ct] = (ct / CH) * (D / 2) + wn * (D / 4) + (ct % CH) * 16 + l16;
+
+  f32x4 acc[RT][CT], tot[RT][CT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tot[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int stages = a.H / BK;
+  const int per_part = stages / kKSplit;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int s = 0; s < stages; ++s) {
+    if (s + 1 < stages) load_stage((s + 1) * BK);
+    const char* A = smem + (s & 1) * STAGE;
+    const char* W = A + TM * BKC * 16;
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < BKC / 4; ++ks) {
+        const int c = ks * 4 + lg;
+        bf16x8 af[RT], bfr[CT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int r = wm * (TM / 2) + rt * 16 + l16;
+          af[rt] = as_bf16x8(*(const uint4*)(A + (r * BKC + (c ^ (r & (BKC - 1)))) * 16));
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int col = colv[ct];
+          bfr[ct] = as_bf16x8(*(const uint4*)(W + (col * BKC + (c ^ (col & (BKC - 1)))) * 16));
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma_bf16(af[rt], bfr[ct], acc[rt][ct]);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < BKC; ++ks) {  // four fp32 k per chunk = one MFMA step
+        float af[RT], bfr[CT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int r = wm * (TM / 2) + rt * 16 + l16;
+          af[rt] = *(const float*)(A + (r * BKC + (ks ^ (r & (BKC - 1)))) * 16 + lg * 4);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int col = colv[ct];
+          bfr[ct] = *(const float*)(W + (col * BKC + (ks ^ (col & (BKC - 1)))) * 16 + lg * 4);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma_f32(af[rt], bfr[ct], acc[rt][ct]);
+      }
+    }
+    if ((s + 1) % per_part == 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          tot[rt][ct] = tot[rt][ct] + acc[rt][ct];
+          acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    if (s + 1 < stages) store_stage((s + 1) & 1);
+    __syncthreads();
+  }
+
+  // Rotary embedding of Q and K heads, in registers.
+  if (j < a.Hq + a.Hkv) {
+    float hi[CH], lo[CH];
+#pragma unroll
+    for (int sb = 0; sb < CH; ++sb) rope_turns(wn * (D / 4) + sb * 16 + l16, D, a.rope_base, hi[sb], lo[sb]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * (TM / 2) + rt * 16 + lg * 4 + v;
+        const int pos = (m < a.M) ? a.idx[m] : 0;
+#pragma unroll
+        for (int sb = 0; sb < CH; ++sb) {
+          float s, c;
+          rope_sincos(pos, hi[sb], lo[sb], s, c);
+          const float x = tot[rt][sb][v], y = tot[rt][CH + sb][v];
+          tot[rt][sb][v] = x * c - y * s;
+          tot[rt][CH + sb][v] = y * c + x * s;
+        }
+      }
+  }
+
+  // Stage the fp32 tile in LDS (the loop's last barrier already retired the stage buffers).
+  float* tile = (float*)smem;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        tile[(wm * (TM / 2) + rt * 16 + lg * 4 + v) * EPI_STRIDE + colv[ct]] = tot[rt][ct][v];
+  __syncthreads();
+
+  // Whole rows out: D/8 threads per row, eight values each.
+  constexpr int TPR = D / 8;
+  const int cpos = (t % TPR) * 8;
+  for (int r = t / TPR; r < TM; r += 256 / TPR) {
+    const int m = m0 + r;
+    if (m >= a.M) continue;  // uniform over the TPR threads of a row
+    float x[8];
+    const float4 x0 = *(const float4*)(tile + r * EPI_STRIDE + cpos);
+    const float4 x1 = *(const float4*)(tile + r * EPI_STRIDE + cpos + 4);
+    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    int which;
+    const size_t off = out_row_offset(a, m, j, which);
+    if (which == 0 || KIND != kCacheFP8) {
+      void* base = which == 0 ? a.q_out : which == 1 ? a.kc : a.vc;
+      if constexpr (BF) {
+        uint4 o;
+        o.x = pack_bf16x2(x[0], x[1]);
+        o.y = pack_bf16x2(x[2], x[3]);
+        o.z = pack_bf16x2(x[4], x[5]);
+        o.w = pack_bf16x2(x[6], x[7]);
+        *(uint4*)((bf16_t*)base + off + cpos) = o;
+      } else {
+        float* dst = (float*)base + off + cpos;
+        *(float4*)dst = x0;
+        *(float4*)(dst + 4) = x1;
+      }
+    } else {
+      // Per-row FP8: amax over the row (TPR consecutive lanes), scale = amax / 448.
+      float am = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
+#pragma unroll
+      for (int msk = 1; msk < TPR; msk <<= 1) am = fmaxf(am, __shfl_xor(am, msk, kWave));
+      const float scale = (am == 0.f) ? 1.f : am / 448.f;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo |= e4m3_encode(x[e] / scale) << (8 * e);
+        hi |= e4m3_encode(x[4 + e] / scale) << (8 * e);
+      }
+      uint8_t* dst = (uint8_t*)(which == 1 ? a.kc : a.vc) + off + cpos;
+      *(uint2*)dst = make_uint2(lo, hi);
+      if ((t % TPR) == 0) (which == 1 ? a.ks : a.vs)[off / D] = scale;
+    }
+  }
+}
+
+template <typename T, int KIND, int D, int BKC>
+hipError_t launch_tiled(const RefreshArgs& a, int tm, hipStream_t s) {
+  const int heads = a.Hq + 2 * a.Hkv;
+  if (tm == 128) {
+    dim3 grid(heads, (a.M + 127) / 128);
+    refresh_tiled<T, KIND, 128, D, BKC><<<grid, 256, 0, s>>>(a);
+  } else {
+    dim3 grid(heads, (a.M + 63) / 64);
+    refresh_tiled<T, KIND, 64, D, BKC><<<grid, 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int KIND, int D>
+hipError_t launch_tiled_bk(const RefreshArgs& a, int tm, hipStream_t s) {
+  const int part = a.H / kKSplit;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  if (part % (8 * EPC) == 0) return launch_tiled<T, KIND, D, 8>(a, tm, s);
+  return launch_tiled<T, KIND, D, 4>(a, tm, s);
+}
+
+template <int D>
+hipError_t launch_d(const RefreshArgs& a, hipStream_t s) {
+  const int heads = a.Hq + 2 * a.Hkv;
+  if (a.act == DLLM_F32) return launch_tiled_bk<float, kCacheF32, D>(a, 64, s);
+  if (a.kind == kCacheBF16 && a.M <= 64) {
+    dim3 grid(heads * (D / 32), (a.M + 31) / 32);
+    refresh_skinny<D><<<grid, 512, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  const int tm = ((a.M + 127) / 128) * heads >= 512 ? 128 : 64;
+  if (a.kind == kCacheFP8) return launch_tiled_bk<bf16_t, kCacheFP8, D>(a, tm, s);
+  return launch_tiled_bk<bf16_t, kCacheBF16, D>(a, tm, s);
+}
+
+}  // namespace
+
+hipError_t launch_refresh(const RefreshArgs& a, hipStream_t s) {
+  if (a.D == 128) return launch_d<128>(a, s);
+  return launch_d<64>(a, s);
+}
+
+}  // namespace dllm

@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports every symbol its header declares, and rejects bad
+arguments on the host (no kernel is launched by any call here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dllm_cache.h")
+
+dkv = pytest.importorskip("diffusion_kv_cache_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"DLLM_API\s+[\w\s\*]*?\b(dllm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatter",
+                 "dllm_attention_workspace_bytes", "dllm_block_attention", "dllm_drift_check",
+                 "dllm_last_error"):
+        assert want in names
+    assert set(names) == set(dkv.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dkv.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _desc(B=1, Hkv=4, S=128, D=64, dt=dkv.DLLM_BF16, group=0):
+    return dkv.CacheDesc(B, Hkv, S, D, dt, group)
+
+
+def test_cache_bytes_layout():
+    d = _desc(B=2, Hkv=3, S=100, D=128, dt=dkv.DLLM_BF16)
+    kv = 2 * 3 * 100 * 128 * 2
+    assert dkv.dllm_cache_bytes(d) == 2 * ((kv + 255) // 256 * 256)
+    d8 = _desc(B=2, Hkv=3, S=100, D=128, dt=dkv.DLLM_FP8_E4M3, group=128)
+    kv8 = (2 * 3 * 100 * 128 + 255) // 256 * 256
+    sc = (2 * 3 * 100 * 4 + 255) // 256 * 256
+    assert dkv.dllm_cache_bytes(d8) == 2 * kv8 + 2 * sc
+    assert dkv.dllm_cache_bytes(_desc(D=96)) == 0
+
+
+def _alloc(d, base, nbytes):
+    c = dkv.CCache()
+    st = dkv.lib.dllm_cache_alloc(ctypes.byref(d), ctypes.c_void_p(base), nbytes, ctypes.byref(c))
+    return st, c
+
+
+def test_cache_alloc_carves_regions_without_touching_memory():
+    d = _desc(B=2, Hkv=2, S=64, D=128, dt=dkv.DLLM_FP8_E4M3, group=128)
+    need = dkv.dllm_cache_bytes(d)
+    base = 1 << 40                                   # never dereferenced
+    st, c = _alloc(d, base, need)
+    assert st == dkv.DLLM_OK
+    assert c.k == base and c.v == base + 2 * 2 * 64 * 128
+    assert c.k_scale == c.v + 2 * 2 * 64 * 128 and c.v_scale == c.k_scale + 1024
+    st, _ = _alloc(d, base, need - 1)
+    assert st == dkv.DLLM_ESIZE and "needs" in dkv.dllm_last_error()
+    st, _ = _alloc(d, base + 16, need)
+    assert st == dkv.DLLM_EINVAL
+    st, _ = _alloc(_desc(D=128, dt=dkv.DLLM_FP8_E4M3, group=64), base, 1 << 30)
+    assert st == dkv.DLLM_EUNSUPPORTED
+    st, _ = _alloc(_desc(B=0), base, 1 << 30)
+    assert st == dkv.DLLM_EINVAL
+    st, _ = _alloc(_desc(D=80), base, 1 << 30)
+    assert st == dkv.DLLM_EUNSUPPORTED
+
+
+def _fake_cache(dt=dkv.DLLM_BF16, D=128, Hkv=4):
+    d = _desc(B=2, Hkv=Hkv, S=64, D=D, dt=dt, group=D if dt == dkv.DLLM_FP8_E4M3 else 0)
+    st, c = _alloc(d, 1 << 40, dkv.dllm_cache_bytes(d))
+    assert st == 0
+    return c
+
+
+P = ctypes.c_void_p
+ADDR = P(1 << 41)
+
+
+def _refresh(c, H=256, act=dkv.DLLM_BF16, n=4, hq=4, base=10000.0, hidden=ADDR, q_out=ADDR):
+    return dkv.lib.dllm_refresh_qkv_rope_scatter(ctypes.byref(c), hidden, H, act, ADDR, n, ADDR,
+                                                 hq, base, q_out, None)
+
+
+def test_refresh_rejects_bad_arguments_on_host():
+    c = _fake_cache()
+    assert _refresh(c, H=200) == dkv.DLLM_EUNSUPPORTED             # H % 256
+    assert _refresh(c, hq=6) == dkv.DLLM_EINVAL                    # Hq % Hkv
+    assert _refresh(c, n=65) == dkv.DLLM_EINVAL                    # n > S
+    assert _refresh(c, n=-1) == dkv.DLLM_EINVAL
+    assert _refresh(c, act=dkv.DLLM_F32) == dkv.DLLM_EUNSUPPORTED  # fp32 act, bf16 cache
+    assert _refresh(c, act=7) == dkv.DLLM_EINVAL
+    assert _refresh(c, base=0.0) == dkv.DLLM_EINVAL
+    assert _refresh(c, hidden=None) == dkv.DLLM_EINVAL
+    assert _refresh(c, q_out=P((1 << 41) + 8)) == dkv.DLLM_EINVAL  # misaligned
+    assert _refresh(c, n=0) == dkv.DLLM_OK                         # nothing to do, no launch
+    assert dkv.lib.dllm_refresh_qkv_rope_scatter(None, ADDR, 256, 1, ADDR, 4, ADDR, 4, 1e4, ADDR,
+                                                 None) == dkv.DLLM_EINVAL
+
+
+def test_attention_and_drift_reject_bad_arguments_on_host():
+    c = _fake_cache()
+    L = dkv.lib
+    need = L.dllm_attention_workspace_bytes(ctypes.byref(c.desc), 4, 8)
+    assert need > 0
+    att = lambda **kw: L.dllm_block_attention(
+        ctypes.byref(c), kw.get("q", ADDR), kw.get("act", 1), kw.get("hq", 4), kw.get("n", 8),
+        kw.get("scale", 0.088), ADDR, None, None, ADDR, kw.get("ws", need), None)
+    assert att(ws=need - 1) == dkv.DLLM_ESIZE
+    assert att(hq=5) == dkv.DLLM_EINVAL
+    assert att(scale=0.0) == dkv.DLLM_EINVAL
+    assert att(act=dkv.DLLM_F32) == dkv.DLLM_EUNSUPPORTED
+    assert att(q=None) == dkv.DLLM_EINVAL
+    assert att(n=0) == dkv.DLLM_OK
+    dr = lambda cc, **kw: L.dllm_drift_check(ctypes.byref(cc), kw.get("hq", 4), kw.get("k", 32),
+                                             0.9, ADDR, ADDR, None, ADDR, ADDR, None)
+    assert dr(c, k=0) == dkv.DLLM_EINVAL and dr(c, k=65) == dkv.DLLM_EINVAL
+    assert dr(c, hq=3) == dkv.DLLM_EINVAL
+    assert dr(_fake_cache(dt=dkv.DLLM_FP8_E4M3)) == dkv.DLLM_EUNSUPPORTED
+    assert L.dllm_fp8_e4m3_roundtrip(ADDR, 10, ctypes.c_float(0.0), ADDR, None, None) == dkv.DLLM_EINVAL
+    assert L.dllm_fp8_e4m3_roundtrip(ADDR, 0, ctypes.c_float(1.0), ADDR, None, None) == dkv.DLLM_OK
