@@ -159,6 +159,10 @@ def run(args):
     mass = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     sigma = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     refresh = torch.empty((B,), dtype=torch.uint8, device=dev)
+    rws_bytes = dkv.dllm_refresh_workspace_bytes(layers[0].cache, wl.hidden,
+                                                 dkv.DLLM_F32 if wl.act == "f32" else dkv.DLLM_BF16,
+                                                 n, Hq)
+    rws = torch.empty(rws_bytes, dtype=torch.uint8, device=dev) if rws_bytes else None
     ws = torch.empty(max(1, dkv.dllm_attention_workspace_bytes(layers[0].cache, Hq, n)),
                      dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(D)
@@ -167,7 +171,8 @@ def run(args):
     # Previous step (untimed): tracking sets chosen from the mass of an attention pass.
     for ly in layers:
         if track:
-            dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_cur, idx_t, ly.w, Hq, wl.rope_base, q)
+            dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_cur, idx_t, ly.w, Hq, wl.rope_base, q,
+                                              rws)
             dkv.dllm_block_attention(ly.cache, q, Hq, scale, out, lse, mass, ws)
             dkv.dllm_drift_check(ly.cache, Hq, k, wl.gamma, ly.T, ly.buf, mass, sigma, refresh)
     torch.cuda.synchronize()
@@ -179,7 +184,7 @@ def run(args):
     def step(ly, evs=None):
         if evs:
             evs[0].record()
-        dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_cur, idx_t, ly.w, Hq, wl.rope_base, q)
+        dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_cur, idx_t, ly.w, Hq, wl.rope_base, q, rws)
         if evs:
             evs[1].record()
         dkv.dllm_block_attention(ly.cache, q, Hq, scale, out, lse, mass if track else None, ws)

@@ -23,8 +23,9 @@ DLLM_F32, DLLM_BF16, DLLM_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "DLLM_OK", 1: "DLLM_EINVAL", 2: "DLLM_ESIZE", 3: "DLLM_EUNSUPPORTED",
                 4: "DLLM_ELAUNCH"}
 EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatter",
-           "dllm_attention_workspace_bytes", "dllm_block_attention", "dllm_drift_check",
-           "dllm_fp8_e4m3_roundtrip", "dllm_last_error")
+           "dllm_refresh_workspace_bytes", "dllm_attention_workspace_bytes",
+           "dllm_block_attention", "dllm_drift_check", "dllm_fp8_e4m3_roundtrip",
+           "dllm_last_error")
 
 _TORCH_DTYPE = {DLLM_F32: torch.float32, DLLM_BF16: torch.bfloat16, DLLM_FP8_E4M3: torch.uint8}
 _DTYPE_CODE = {torch.float32: DLLM_F32, torch.bfloat16: DLLM_BF16}
@@ -59,7 +60,9 @@ def _load():
                                      ctypes.POINTER(CCache)]
     lib.dllm_refresh_qkv_rope_scatter.restype = i32
     lib.dllm_refresh_qkv_rope_scatter.argtypes = [ctypes.POINTER(CCache), P, i32, i32, P, i32, P,
-                                                  i32, ctypes.c_float, P, P]
+                                                  i32, ctypes.c_float, P, P, ctypes.c_size_t, P]
+    lib.dllm_refresh_workspace_bytes.restype = ctypes.c_size_t
+    lib.dllm_refresh_workspace_bytes.argtypes = [ctypes.POINTER(CacheDesc), i32, i32, i32, i32]
     lib.dllm_attention_workspace_bytes.restype = ctypes.c_size_t
     lib.dllm_attention_workspace_bytes.argtypes = [ctypes.POINTER(CacheDesc), i32, i32]
     lib.dllm_block_attention.restype = i32
@@ -149,10 +152,17 @@ def _expect(t: torch.Tensor, name: str, shape, dtype):
                                      f"got {t.device} {t.dtype} {tuple(t.shape)}")
 
 
+def dllm_refresh_workspace_bytes(cache: Cache, hidden_size: int, act_dtype: int, n: int,
+                                 num_q_heads: int) -> int:
+    return lib.dllm_refresh_workspace_bytes(ctypes.byref(cache.desc), hidden_size, act_dtype, n,
+                                            num_q_heads)
+
+
 def dllm_refresh_qkv_rope_scatter(cache: Cache, hidden: torch.Tensor, refresh_idx: torch.Tensor,
                                   w_qkv: torch.Tensor, num_q_heads: int, rope_base: float,
-                                  q_out: torch.Tensor, stream=None):
-    """hidden [B,S,H], refresh_idx [B,n] int32, w_qkv [(Hq+2Hkv)D, H], q_out [B,n,Hq,D]."""
+                                  q_out: torch.Tensor, workspace=None, stream=None):
+    """hidden [B,S,H], refresh_idx [B,n] int32, w_qkv [(Hq+2Hkv)D, H], q_out [B,n,Hq,D];
+    workspace a uint8 device tensor (allocated here when None and needed)."""
     d = cache.desc
     if hidden.dtype not in _DTYPE_CODE:
         raise DllmError(DLLM_EINVAL, f"hidden dtype {hidden.dtype}")
@@ -163,9 +173,14 @@ def dllm_refresh_qkv_rope_scatter(cache: Cache, hidden: torch.Tensor, refresh_id
     _expect(refresh_idx, "refresh_idx", (d.batch, n), torch.int32)
     _expect(w_qkv, "w_qkv", ((num_q_heads + 2 * d.num_kv_heads) * d.head_dim, H), hidden.dtype)
     _expect(q_out, "q_out", (d.batch, n, num_q_heads, d.head_dim), hidden.dtype)
+    if workspace is None:
+        need = dllm_refresh_workspace_bytes(cache, H, act, n, num_q_heads)
+        workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib.dllm_refresh_qkv_rope_scatter(
         ctypes.byref(cache.c), _ptr(hidden), H, act, _ptr(refresh_idx), n,
-        _ptr(w_qkv), num_q_heads, float(rope_base), _ptr(q_out), _stream(stream)))
+        _ptr(w_qkv), num_q_heads, float(rope_base), _ptr(q_out), _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def dllm_attention_workspace_bytes(cache: Cache, num_q_heads: int, n: int) -> int:

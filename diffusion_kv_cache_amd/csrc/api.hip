@@ -115,7 +115,8 @@ dllm_status dllm_refresh_qkv_rope_scatter(const dllm_cache* c, const void* hidde
                                           int32_t hidden_size, int32_t act_dtype,
                                           const int32_t* refresh_idx, int32_t n,
                                           const void* w_qkv, int32_t num_q_heads,
-                                          float rope_base, void* q_out, void* stream) {
+                                          float rope_base, void* q_out, void* workspace,
+                                          size_t ws_bytes, void* stream) {
   dllm_status st = check_cache(c);
   if (st) return st;
   const dllm_cache_desc& d = c->desc;
@@ -142,6 +143,11 @@ dllm_status dllm_refresh_qkv_rope_scatter(const dllm_cache* c, const void* hidde
     return fail(DLLM_EINVAL, "hidden, w_qkv and q_out must be 16-byte aligned");
   const long long M = (long long)d.batch * n;
   if (M > (1LL << 30)) return fail(DLLM_EINVAL, "too many rows");
+  const int N = (num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
+  const size_t need = dllm::refresh_workspace_bytes(act_dtype, (int)M, N, hidden_size);
+  if (ws_bytes < need) return fail(DLLM_ESIZE, "refresh workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (need && (!workspace || !aligned16(workspace)))
+    return fail(DLLM_EINVAL, "refresh workspace must be a 16-byte aligned device pointer");
   hipStream_t s = (hipStream_t)stream;
 
   if (debug_mode()) {
@@ -179,7 +185,19 @@ dllm_status dllm_refresh_qkv_rope_scatter(const dllm_cache* c, const void* hidde
   a.act = act_dtype;
   a.kind = d.kv_dtype;
   a.rope_base = (double)rope_base;
+  a.ws = (float*)workspace;
   return finish(dllm::launch_refresh(a, s), s, "refresh");
+}
+
+size_t dllm_refresh_workspace_bytes(const dllm_cache_desc* d, int32_t hidden_size,
+                                    int32_t act_dtype, int32_t n, int32_t num_q_heads) {
+  if (check_desc(d) != DLLM_OK || n < 0 || num_q_heads <= 0 || num_q_heads % d->num_kv_heads ||
+      hidden_size <= 0)
+    return 0;
+  const long long M = (long long)d->batch * n;
+  if (M > (1LL << 30)) return 0;
+  const int N = (num_q_heads + 2 * d->num_kv_heads) * d->head_dim;
+  return dllm::refresh_workspace_bytes(act_dtype, (int)M, N, hidden_size);
 }
 
 size_t dllm_attention_workspace_bytes(const dllm_cache_desc* d, int32_t num_q_heads, int32_t n) {
@@ -262,6 +280,9 @@ dllm_status dllm_drift_check(const dllm_cache* c, int32_t num_q_heads, int32_t k
   if (!(gamma == gamma)) return fail(DLLM_EINVAL, "gamma is NaN");
   if (!track_idx || !track_buf || !sigma_out || !refresh_out)
     return fail(DLLM_EINVAL, "null tracking / output pointer");
+  if (!aligned16(track_buf)) return fail(DLLM_EINVAL, "track_buf must be 16-byte aligned");
+  if (attn_mass && d.max_seq > 16384)
+    return fail(DLLM_EUNSUPPORTED, "tracking update supports S <= 16384 (S=%d)", d.max_seq);
   dllm::DriftArgs a;
   a.kc = c->k;
   a.vc = c->v;

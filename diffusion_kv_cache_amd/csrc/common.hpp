@@ -95,13 +95,24 @@ __device__ __forceinline__ void rope_turns(int i, int D, double base, float& hi,
 // sin and cos of the angle 2 pi * pos * (hi + lo).  The product pos * hi is split exactly
 // (fma), its integer turns are dropped exactly, and the hardware sin/cos (argument in turns)
 // see a fraction in [-0.5, 0.5].
+// Every multiply-add is written as an explicit fmaf so that all kernels using these helpers
+// round identically, whatever the compiler contracts elsewhere.
 __device__ __forceinline__ void rope_sincos(int pos, float hi, float lo, float& s, float& c) {
-  float p = (float)pos;
-  float a = p * hi;
-  float e = fmaf(p, hi, -a);
-  float f = (a - rintf(a)) + (e + p * lo);
+  const float p = (float)pos;
+  const float a = p * hi;
+  const float e = fmaf(p, hi, -a);
+  const float f = (a - rintf(a)) + fmaf(p, lo, e);
   s = __builtin_amdgcn_sinf(f);
   c = __builtin_amdgcn_cosf(f);
+}
+
+// Rotate the pair (x, y) = (x_i, x_{i+D/2}) by the angle with sine s and cosine c.
+__device__ __forceinline__ void rope_rotate(float& x, float& y, float s, float c) {
+  const float ys = y * s, xs = x * s;
+  const float x2 = fmaf(x, c, -ys);
+  const float y2 = fmaf(y, c, xs);
+  x = x2;
+  y = y2;
 }
 
 }  // namespace dllm

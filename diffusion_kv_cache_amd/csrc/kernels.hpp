@@ -22,10 +22,20 @@ struct RefreshArgs {
   int act;               // DLLM_F32 / DLLM_BF16
   int kind;              // cache dtype
   double rope_base;
+  float* ws;             // split-K partials [8][M][N] (small-M path only)
 };
 
-// Picks the tile shape for (M, N, dtypes) and launches the fused refresh kernel.
+// Rows (B * n) up to which a bf16 refresh takes the split-K path.
+constexpr int kSplitKMaxRows = 64;
+// Largest hidden size of the split-K path (its LDS slice is 32 x H/8 bf16).
+constexpr int kSplitKMaxHidden = 16384;
+bool refresh_uses_splitk(int act, int M, int H);
+size_t refresh_workspace_bytes(int act, int M, int N, int H);
+size_t splitk_workspace_bytes(int M, int N);
+
+// Picks the path and tile shape for (M, N, dtypes) and launches the refresh.
 hipError_t launch_refresh(const RefreshArgs& a, hipStream_t s);
+hipError_t launch_refresh_splitk(const RefreshArgs& a, float* part, hipStream_t s);
 
 struct AttnArgs {
   const void* q;         // [B, n, Hq, D] act dtype

@@ -1,13 +1,14 @@
-// Fused refresh kernel: gather the refreshed hidden rows, QKV projection on MFMA, rotary
-// embedding in registers, scatter of K/V rows into the flat cache (optionally as per-row FP8),
-// compact Q out.  One launch per layer step; no intermediate touches HBM.
+// Fused refresh kernel for large M: gather the refreshed hidden rows, QKV projection on MFMA,
+// rotary embedding in registers, scatter of K/V rows into the flat cache (optionally as
+// per-row FP8), compact Q out -- one launch, no intermediate in HBM.  Small M (a block step)
+// takes the split-K path of refresh_splitk.hip instead.
 //
 // What it computes: Flash-dLLM news summary (skillfed.io), memory paragraph -- projection,
 // RoPE and cache write in one kernel with on-chip intermediates; LaCache (gist.science),
 // Technical Summary, Methodology 1 -- only rows outside the invariant region are recomputed,
 // RoPECache holds post-projection, post-RoPE states; Methodology 2 -- 1 x 128 FP8 groups.
 //
-// Reduction order (identical in both kernels below, for any M and tiling): each output
+// Reduction order (identical here and in the split-K path, for any M and tiling): each output
 // element is (((0 + P0) + P1) + ... + P7), where Pp is the chain of 16x16 MFMAs over the p-th
 // eighth of H in ascending k, each MFMA taking k0..k0+31 (bf16) or k0..k0+3 (fp32) with lane
 // group l/16 holding the slots k0 + 8(l/16) .. +7 (bf16) or k0 + l/16 (fp32).  A row's
@@ -39,99 +40,6 @@ __device__ __forceinline__ size_t out_row_offset(const RefreshArgs& a, int m, in
   const int g = (j < a.Hq + a.Hkv) ? j - a.Hq : j - a.Hq - a.Hkv;
   which = (j < a.Hq + a.Hkv) ? 1 : 2;
   return (((size_t)b * a.Hkv + g) * a.S + pos) * (size_t)a.D;
-}
-
-// ------------------------------------------------------------------------------------------
-// Skinny kernel (bf16 activations, bf16 cache, small M): one workgroup per 32-column strip
-// (16 rotary pairs) and 32 rows, eight waves, wave p reducing the p-th eighth of H straight
-// from global memory; partials combined in LDS in partition order.  Spreads the weight stream
-// of a small-M step over (N / 32) x 8 waves.
-// ------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(512) void refresh_skinny(RefreshArgs a) {
-  constexpr int STRIPS = D / 32;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int j = blockIdx.x / STRIPS, sub = blockIdx.x % STRIPS;
-  const int m0 = blockIdx.y * 32;
-  const int Lp = a.H / kKSplit;
-  const int kb = wave * Lp;
-
-  const bf16_t* hid = (const bf16_t*)a.hidden;
-  const bf16_t* w = (const bf16_t*)a.w;
-  const bf16_t* arow[2];
-  bool aval[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int m = m0 + rt * 16 + l16;
-    aval[rt] = m < a.M;
-    arow[rt] = hid + hidden_row_offset(a, aval[rt] ? m : 0) + kb + lg * 8;
-  }
-  const bf16_t* wrow[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-    wrow[ct] = w + (size_t)(j * D + ct * (D / 2) + sub * 16 + l16) * a.H + kb + lg * 8;
-
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const uint4 zero = {0u, 0u, 0u, 0u};
-  for (int k = 0; k < Lp; k += 32) {
-    uint4 av[2], bv[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) av[rt] = *(const uint4*)(arow[rt] + k);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) bv[ct] = *(const uint4*)(wrow[ct] + k);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const uint4 x = aval[rt] ? av[rt] : zero;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = mfma_bf16(as_bf16x8(x), as_bf16x8(bv[ct]), acc[rt][ct]);
-    }
-  }
-
-  __shared__ f32x4 red[kKSplit][2][2][64];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) red[wave][rt][ct][lane] = acc[rt][ct];
-  __syncthreads();
-  if (wave >= 2) return;
-
-  const int rt = wave;
-  f32x4 tot[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    tot[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < kKSplit; ++p) tot[ct] = tot[ct] + red[p][rt][ct][lane];
-  }
-
-  const bool rot = j < a.Hq + a.Hkv;
-  const int pair = sub * 16 + l16;
-  float th_hi = 0.f, th_lo = 0.f;
-  if (rot) rope_turns(pair, D, a.rope_base, th_hi, th_lo);
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int m = m0 + rt * 16 + lg * 4 + v;
-    if (m >= a.M) continue;
-    float x = tot[0][v], y = tot[1][v];
-    if (rot) {
-      float s, c;
-      rope_sincos(a.idx[m], th_hi, th_lo, s, c);
-      const float x2 = x * c - y * s, y2 = y * c + x * s;
-      x = x2;
-      y = y2;
-    }
-    int which;
-    const size_t off = out_row_offset(a, m, j, which);
-    bf16_t* dst = which == 0 ? (bf16_t*)a.q_out : which == 1 ? (bf16_t*)a.kc : (bf16_t*)a.vc;
-    dst[off + pair] = f32_to_bf16(x);
-    dst[off + pair + D / 2] = f32_to_bf16(y);
-  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -302,9 +210,10 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
         for (int sb = 0; sb < CH; ++sb) {
           float s, c;
           rope_sincos(pos, hi[sb], lo[sb], s, c);
-          const float x = tot[rt][sb][v], y = tot[rt][CH + sb][v];
-          tot[rt][sb][v] = x * c - y * s;
-          tot[rt][CH + sb][v] = y * c + x * s;
+          float x = tot[rt][sb][v], y = tot[rt][CH + sb][v];
+          rope_rotate(x, y, s, c);
+          tot[rt][sb][v] = x;
+          tot[rt][CH + sb][v] = y;
         }
       }
   }
@@ -393,11 +302,6 @@ template <int D>
 hipError_t launch_d(const RefreshArgs& a, hipStream_t s) {
   const int heads = a.Hq + 2 * a.Hkv;
   if (a.act == DLLM_F32) return launch_tiled_bk<float, kCacheF32, D>(a, 64, s);
-  if (a.kind == kCacheBF16 && a.M <= 64) {
-    dim3 grid(heads * (D / 32), (a.M + 31) / 32);
-    refresh_skinny<D><<<grid, 512, 0, s>>>(a);
-    return hipGetLastError();
-  }
   const int tm = ((a.M + 127) / 128) * heads >= 512 ? 128 : 64;
   if (a.kind == kCacheFP8) return launch_tiled_bk<bf16_t, kCacheFP8, D>(a, tm, s);
   return launch_tiled_bk<bf16_t, kCacheBF16, D>(a, tm, s);
@@ -405,7 +309,16 @@ hipError_t launch_d(const RefreshArgs& a, hipStream_t s) {
 
 }  // namespace
 
+bool refresh_uses_splitk(int act, int M, int H) {
+  return act == DLLM_BF16 && M <= kSplitKMaxRows && H <= kSplitKMaxHidden;
+}
+
+size_t refresh_workspace_bytes(int act, int M, int N, int H) {
+  return refresh_uses_splitk(act, M, H) ? splitk_workspace_bytes(M, N) : 0;
+}
+
 hipError_t launch_refresh(const RefreshArgs& a, hipStream_t s) {
+  if (refresh_uses_splitk(a.act, a.M, a.H)) return launch_refresh_splitk(a, a.ws, s);
   if (a.D == 128) return launch_d<128>(a, s);
   return launch_d<64>(a, s);
 }

@@ -1,0 +1,171 @@
+// Refresh for small M (a block step of one or a few sequences): the weight stream dominates,
+// so the projection is split over the eight fixed K-partitions across workgroups.
+//
+//   refresh_partial: workgroup (128 output columns, partition p, 32 rows).  The 32 x H/8 slice
+//     of the gathered hidden rows is staged once in LDS with coalesced 16-byte loads; each of
+//     the eight waves streams 16 W rows of that partition from global memory with a deep
+//     register prefetch and chains 16x16x32 MFMAs over the partition in ascending k.  The
+//     partition's fp32 result goes to the workspace.
+//   refresh_reduce: adds the eight partitions in order ((0 + P0) + P1) + ... + P7 -- exactly the
+//     arithmetic of the tiled kernel -- rotates the Q and K pairs (i, i + D/2), and writes Q,
+//     K and V rows (bf16, or per-row FP8 with its fp32 scale).
+//
+// What it computes: Flash-dLLM news summary (skillfed.io), memory paragraph -- projection,
+// RoPE and cache write of the refreshed rows; LaCache (gist.science), Technical Summary,
+// Methodology 1 (RoPECache: post-projection, post-RoPE states) and 2 (1 x 128 FP8 groups).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dllm {
+namespace {
+
+constexpr int kPrefetch = 6;   // k-steps of W in flight per wave
+
+// Three workgroups per CU (6 waves per SIMD) keep all 768 workgroups of a 4096-hidden,
+// 12288-column step resident at once.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6)))
+void refresh_partial(RefreshArgs a, float* part) {
+  extern __shared__ uint4 As[];                  // [32 rows][cpr chunks], swizzled
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
+  const int N = (a.Hq + 2 * a.Hkv) * a.D;
+  const int p = blockIdx.y;
+  const int m0 = blockIdx.z * 32;
+  const int Lp = a.H / kKSplit, kb = p * Lp;
+  const int cpr = Lp / 8;                        // 16-byte chunks per staged row
+  const int mask = (cpr % 8 == 0) ? 7 : 3;
+
+  const bf16_t* hid = (const bf16_t*)a.hidden;
+  for (int q = t; q < 32 * cpr; q += 512) {
+    const int r = q / cpr, c = q % cpr, m = m0 + r;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (m < a.M) {
+      const int b = m / a.n;
+      v = *(const uint4*)(hid + ((size_t)b * a.S + a.idx[m]) * a.H + kb + c * 8);
+    }
+    As[r * cpr + (c ^ (r & mask))] = v;
+  }
+
+  const int col = blockIdx.x * 128 + wave * 16 + l16;
+  const bool col_ok = col < N;
+  const bf16_t* wr = (const bf16_t*)a.w + (size_t)(col_ok ? col : N - 1) * a.H + kb + lg * 8;
+  const int steps = Lp / 32;
+  uint4 wv[kPrefetch];
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u)
+    if (u < steps) wv[u] = *(const uint4*)(wr + u * 32);
+  __syncthreads();
+
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int s0 = 0; s0 < steps; s0 += kPrefetch) {
+    uint4 wn[kPrefetch];
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u)
+      if (s0 + kPrefetch + u < steps) wn[u] = *(const uint4*)(wr + (s0 + kPrefetch + u) * 32);
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u) {
+      if (s0 + u < steps) {
+        const int c = (s0 + u) * 4 + lg;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int r = rt * 16 + l16;
+          const bf16x8 af = as_bf16x8(As[r * cpr + (c ^ (r & mask))]);
+          acc[rt] = mfma_bf16(af, as_bf16x8(wv[u]), acc[rt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u) wv[u] = wn[u];
+  }
+
+  if (!col_ok) return;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = m0 + rt * 16 + lg * 4 + v;
+      if (m < a.M) part[((size_t)p * a.M + m) * N + col] = acc[rt][v];
+    }
+}
+
+// One wave per (row, head): lane i < D/2 owns the rotary pair (i, i + D/2); for D = 64 the
+// two half-waves take two rows.
+template <int D, int KIND>
+__global__ __launch_bounds__(256) void refresh_reduce(RefreshArgs a, const float* part) {
+  constexpr int HALF = D / 2;
+  constexpr int RPW = 64 / HALF;                 // rows per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane % HALF;
+  const int j = blockIdx.x;
+  const int N = (a.Hq + 2 * a.Hkv) * D;
+  const int m = (blockIdx.y * 4 + wave) * RPW + lane / HALF;
+  const bool ok = m < a.M;
+  const int mm = ok ? m : 0;
+  float x = 0.f, y = 0.f;
+#pragma unroll
+  for (int p = 0; p < kKSplit; ++p) {
+    const float* row = part + ((size_t)p * a.M + mm) * N + j * D;
+    x = x + row[i];
+    y = y + row[i + HALF];
+  }
+  if (j < a.Hq + a.Hkv) {
+    float hi, lo, s, c;
+    rope_turns(i, D, a.rope_base, hi, lo);
+    rope_sincos(a.idx[mm], hi, lo, s, c);
+    rope_rotate(x, y, s, c);
+  }
+  const int b = mm / a.n;
+  if (j < a.Hq) {
+    if (ok) {
+      bf16_t* q = (bf16_t*)a.q_out + ((size_t)mm * a.Hq + j) * D;
+      q[i] = f32_to_bf16(x);
+      q[i + HALF] = f32_to_bf16(y);
+    }
+    return;
+  }
+  const bool is_k = j < a.Hq + a.Hkv;
+  const int g = is_k ? j - a.Hq : j - a.Hq - a.Hkv;
+  const size_t row = ((size_t)b * a.Hkv + g) * a.S + a.idx[mm];
+  if constexpr (KIND == kCacheFP8) {
+    float am = fmaxf(fabsf(x), fabsf(y));
+#pragma unroll
+    for (int msk = 1; msk < HALF; msk <<= 1) am = fmaxf(am, __shfl_xor(am, msk, kWave));
+    const float scale = (am == 0.f) ? 1.f : am / 448.f;
+    if (ok) {
+      uint8_t* dst = (uint8_t*)(is_k ? a.kc : a.vc) + row * D;
+      dst[i] = (uint8_t)e4m3_encode(x / scale);
+      dst[i + HALF] = (uint8_t)e4m3_encode(y / scale);
+      if (i == 0) (is_k ? a.ks : a.vs)[row] = scale;
+    }
+  } else {
+    if (ok) {
+      bf16_t* dst = (bf16_t*)(is_k ? a.kc : a.vc) + row * D;
+      dst[i] = f32_to_bf16(x);
+      dst[i + HALF] = f32_to_bf16(y);
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_reduce(const RefreshArgs& a, const float* part, hipStream_t s) {
+  constexpr int RPB = 4 * (128 / D);             // rows per workgroup
+  dim3 grid(a.Hq + 2 * a.Hkv, (a.M + RPB - 1) / RPB);
+  if (a.kind == kCacheFP8) refresh_reduce<D, kCacheFP8><<<grid, 256, 0, s>>>(a, part);
+  else refresh_reduce<D, kCacheBF16><<<grid, 256, 0, s>>>(a, part);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t splitk_workspace_bytes(int M, int N) { return (size_t)kKSplit * M * N * sizeof(float); }
+
+hipError_t launch_refresh_splitk(const RefreshArgs& a, float* part, hipStream_t s) {
+  const int N = (a.Hq + 2 * a.Hkv) * a.D;
+  dim3 grid((N + 127) / 128, kKSplit, (a.M + 31) / 32);
+  const size_t lds = (size_t)32 * (a.H / kKSplit) * sizeof(bf16_t);
+  refresh_partial<<<grid, 512, lds, s>>>(a, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return a.D == 128 ? launch_reduce<128>(a, part, s) : launch_reduce<64>(a, part, s);
+}
+
+}  // namespace dllm

@@ -118,6 +118,9 @@ DLLM_API dllm_status dllm_cache_alloc(const dllm_cache_desc *d, void *base, size
  *   rope_base    theta_i = rope_base^(-2i/D) for i < D/2; the pair (i, i + D/2) of each Q
  *                and K head of row s is rotated by s * theta_i (rotate-half convention)
  *   q_out        device, [B, n, Hq, D] of act_dtype: rotated queries of the refreshed rows
+ *   workspace    device scratch of ws_bytes >= dllm_refresh_workspace_bytes(...) (may be NULL
+ *                when that is 0): small steps split the projection over K across workgroups
+ *                and keep the eight partial sums here; contents need no initialisation
  * Writes exactly the K/V rows (b, :, refresh_idx[b, i], :) (and their scales) and q_out;
  * every other cache row is left untouched.  Each output element is the fp32 sum of eight
  * fixed, equal K-partitions of H, each accumulated in ascending order and added in
@@ -125,12 +128,21 @@ DLLM_API dllm_status dllm_cache_alloc(const dllm_cache_desc *d, void *base, size
  * refreshed: a step reproduces, bit for bit, what a full refresh of all rows would store.
  * FP8 cache: per cache row, amax -> scale = amax / 448 (1 if amax = 0) -> codes = e4m3
  * (round to nearest even, saturating) of x / scale.
- * q_out must not alias hidden or the cache. */
+ * q_out must not alias hidden or the cache.
+ * Errors: DLLM_EINVAL, DLLM_ESIZE (workspace too small), DLLM_EUNSUPPORTED, DLLM_ELAUNCH. */
 DLLM_API dllm_status dllm_refresh_qkv_rope_scatter(const dllm_cache *c, const void *hidden,
                                           int32_t hidden_size, int32_t act_dtype,
                                           const int32_t *refresh_idx, int32_t n,
                                           const void *w_qkv, int32_t num_q_heads,
-                                          float rope_base, void *q_out, void *stream);
+                                          float rope_base, void *q_out, void *workspace,
+                                          size_t ws_bytes, void *stream);
+
+/* Workspace bytes the refresh call needs for n rows per sequence (0 when the step runs as a
+ * single fused kernel; 8 * B * n * (Hq + 2 Hkv) * D * 4 for the split-K path of small
+ * bf16 steps, B * n <= 64).  Returns 0 also for invalid arguments. */
+DLLM_API size_t dllm_refresh_workspace_bytes(const dllm_cache_desc *d, int32_t hidden_size,
+                                             int32_t act_dtype, int32_t n,
+                                             int32_t num_q_heads);
 
 /* Workspace bytes dllm_block_attention needs for this shape: the split-KV partial states
  * (running max, normaliser and unnormalised output per query row and split) and, for the

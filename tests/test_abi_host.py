@@ -84,9 +84,10 @@ P = ctypes.c_void_p
 ADDR = P(1 << 41)
 
 
-def _refresh(c, H=256, act=dkv.DLLM_BF16, n=4, hq=4, base=10000.0, hidden=ADDR, q_out=ADDR):
+def _refresh(c, H=256, act=dkv.DLLM_BF16, n=4, hq=4, base=10000.0, hidden=ADDR, q_out=ADDR,
+             ws=ADDR, ws_bytes=1 << 30):
     return dkv.lib.dllm_refresh_qkv_rope_scatter(ctypes.byref(c), hidden, H, act, ADDR, n, ADDR,
-                                                 hq, base, q_out, None)
+                                                 hq, base, q_out, ws, ws_bytes, None)
 
 
 def test_refresh_rejects_bad_arguments_on_host():
@@ -102,7 +103,17 @@ def test_refresh_rejects_bad_arguments_on_host():
     assert _refresh(c, q_out=P((1 << 41) + 8)) == dkv.DLLM_EINVAL  # misaligned
     assert _refresh(c, n=0) == dkv.DLLM_OK                         # nothing to do, no launch
     assert dkv.lib.dllm_refresh_qkv_rope_scatter(None, ADDR, 256, 1, ADDR, 4, ADDR, 4, 1e4, ADDR,
-                                                 None) == dkv.DLLM_EINVAL
+                                                 None, 0, None) == dkv.DLLM_EINVAL
+    # small bf16 steps split K over workgroups and need 8 fp32 partials per output
+    L = dkv.lib
+    need = L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_BF16, 4, 4)
+    assert need == 8 * (2 * 4) * ((4 + 2 * 4) * 128) * 4
+    assert _refresh(c, ws_bytes=need - 1) == dkv.DLLM_ESIZE
+    assert _refresh(c, ws=None, ws_bytes=need) == dkv.DLLM_EINVAL
+    # large steps and fp32 run as one fused kernel: no workspace
+    assert L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_BF16, 64, 4) == 0
+    assert L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_F32, 4, 4) == 0
+    assert L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_BF16, 4, 5) == 0
 
 
 def test_attention_and_drift_reject_bad_arguments_on_host():

@@ -40,6 +40,10 @@ REFRESH_CASES = {
                            seed=16),
     "f32_d64": C(batch=2, hidden=256, q_heads=4, kv_heads=4, head_dim=64, seq=70, prompt=30,
                  act="f32", cache="f32", block_start=31, block_len=9, seed=17),
+    "splitk_fp8_h768_m64": C(batch=4, hidden=768, q_heads=6, kv_heads=3, head_dim=128, seq=64,
+                             prompt=30, cache="fp8", block_start=40, block_len=16, seed=21),
+    "splitk_bf16_h768_d64": C(batch=1, hidden=768, q_heads=3, kv_heads=1, head_dim=64, seq=90,
+                              prompt=40, block_start=45, block_len=45, seed=22),
     "f32_d128_gqa": C(batch=1, hidden=512, q_heads=4, kv_heads=2, head_dim=128, seq=40,
                       prompt=20, act="f32", cache="f32", block_start=3, block_len=30, seed=18),
 }
@@ -71,8 +75,10 @@ def test_refresh_parity_and_untouched_rows(name):
     for key, t in (("k", c.k), ("v", c.v), ("ks", c.k_scale), ("vs", c.v_scale)):
         if t is None:
             continue
-        now = t.cpu()
-        old = before[key].cpu()
+        as_int = {torch.bfloat16: torch.int16, torch.float32: torch.int32,
+                  torch.uint8: torch.uint8}[t.dtype]        # bitwise: the poison holds NaNs
+        now = t.cpu().view(as_int)
+        old = before[key].cpu().view(as_int)
         m = torch.from_numpy(mask)[:, None, :].expand(now.shape[:3])
         assert torch.equal(now[~m], old[~m]), f"{key}: a row outside the refresh set changed"
 
@@ -97,7 +103,7 @@ def test_refresh_parity_and_untouched_rows(name):
 
 @pytest.mark.parametrize("name", ["skinny_bf16_d128", "skinny_gqa_d64_scattered",
                                   "tiled64_bf16_ragged", "fp8_tiled_d128", "f32_d64",
-                                  "f32_d128_gqa"])
+                                  "f32_d128_gqa", "splitk_fp8_h768_m64", "splitk_bf16_h768_d64"])
 def test_step_reproduces_full_refresh_bitwise(name):
     """Cached step (prefill on H_prev, refresh of R on H_cur) stores exactly what a full
     refresh on H_cur stores -- on the GPU too, whichever kernel each call picks."""
