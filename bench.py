@@ -151,7 +151,6 @@ def run(args):
     L = args.layers or max(3, math.ceil(3 * MALL_BYTES / per_layer))
     log(f"[bench] {L} layer instances x {per_layer / 2**20:.1f} MiB")
     layers = [Layer(dkv, torch, wl, w, h_prev, idx_t) for _ in range(L)]
-    del h_prev
 
     q = torch.empty((B, n, Hq, D), dtype=act, device=dev)
     out = torch.empty_like(q)
@@ -168,10 +167,10 @@ def run(args):
     scale = 1.0 / math.sqrt(D)
     track = layers[0].track
 
-    # Previous step (untimed): tracking sets chosen from the mass of an attention pass.
+    # Previous step (untimed, on H_prev): the tracking sets come from its attention mass.
     for ly in layers:
         if track:
-            dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_cur, idx_t, ly.w, Hq, wl.rope_base, q,
+            dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_prev, idx_t, ly.w, Hq, wl.rope_base, q,
                                               rws)
             dkv.dllm_block_attention(ly.cache, q, Hq, scale, out, lse, mass, ws)
             dkv.dllm_drift_check(ly.cache, Hq, k, wl.gamma, ly.T, ly.buf, mass, sigma, refresh)

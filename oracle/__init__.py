@@ -225,8 +225,8 @@ def store_rows(x: np.ndarray, dtype: str):
 
 
 class Cache:
-    """K and V [B, Hkv, S, D] as stored (float64 holding storage values), plus fp8 codes
-    and scales for the fp8 cache."""
+    """K and V [B, Hkv, S, D] as stored (float64 holding storage values), plus, for the fp8
+    cache, the codes, the scales and the exact values before quantisation."""
 
     def __init__(self, wl):
         B, Hkv, S, D = wl.batch, wl.kv_heads, wl.seq, wl.head_dim
@@ -238,6 +238,8 @@ class Cache:
             self.v_codes = np.zeros((B, Hkv, S, D), np.uint8)
             self.k_scale = np.zeros((B, Hkv, S), np.float32)
             self.v_scale = np.zeros((B, Hkv, S), np.float32)
+            self.k_exact = np.zeros((B, Hkv, S, D))
+            self.v_exact = np.zeros((B, Hkv, S, D))
 
     def copy(self):
         c = Cache.__new__(Cache)
@@ -254,6 +256,7 @@ class Cache:
             if codes is not None:
                 getattr(self, name + "_codes")[b][:, rows] = codes.transpose(1, 0, 2)
                 getattr(self, name + "_scale")[b][:, rows] = scales.T
+                getattr(self, name + "_exact")[b][:, rows] = x.transpose(1, 0, 2)
 
 
 def refresh_rows(cache: Cache, hidden: np.ndarray, w: np.ndarray, idx, batches=None,

@@ -113,3 +113,92 @@ def e4m3_step_distance(a: np.ndarray, b: np.ndarray) -> int:
         mag = c & 0x7F
         return np.where(c & 0x80, -mag, mag)
     return int(np.abs(ordinal(a) - ordinal(b)).max()) if a.size else 0
+
+
+def run_workload_gpu(wl, inp, snapshot_prefill: bool = True):
+    """The bench's launch sequence on one layer: prefill(H_prev); previous step (refresh of
+    R from H_prev, attention with mass, drift check from an empty tracking set); current step
+    (refresh of R from H_cur, attention with mass, drift check).  Returns host copies."""
+    m = dkv()
+    act = ACT_TORCH[wl.act]
+    B, n, S, Hq, D, k = wl.batch, wl.n_refresh, wl.seq, wl.q_heads, wl.head_dim, wl.track_k
+    track = wl.cache != "fp8"
+    say(f"[{wl.name}] gpu prefill")
+    h_prev = to_dev(inp.hidden_prev, act)
+    layer = GpuLayer(wl, inp.w, guard=0)
+    layer.prefill(h_prev)
+    torch.cuda.synchronize()
+    res = {}
+    if snapshot_prefill:
+        res["region_prefill"] = layer.cache.region.clone()
+    idx_t = torch.from_numpy(inp.idx).cuda()
+    h_cur = h_prev.clone()
+    h_cur[torch.arange(B, device="cuda")[:, None], idx_t.long()] = to_dev(inp.new_rows, act)
+    scale = 1.0 / math.sqrt(D)
+    q = torch.empty((B, n, Hq, D), dtype=act, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, n), dtype=torch.float32, device="cuda")
+    mass = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    sigma = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    refresh = torch.empty((B,), dtype=torch.uint8, device="cuda")
+    if track:
+        tdt = torch.float32 if wl.cache == "f32" else torch.bfloat16
+        T = torch.full((B, Hq, k), -1, dtype=torch.int32, device="cuda")
+        buf = torch.zeros((B, Hq, k, 2, D), dtype=tdt, device="cuda")
+        say(f"[{wl.name}] gpu previous step")
+        m.dllm_refresh_qkv_rope_scatter(layer.cache, h_prev, idx_t, layer.w, Hq, wl.rope_base, q)
+        m.dllm_block_attention(layer.cache, q, Hq, scale, out, lse, mass)
+        m.dllm_drift_check(layer.cache, Hq, k, wl.gamma, T, buf, mass, sigma, refresh)
+        torch.cuda.synchronize()
+        res["mass_prev"] = mass.cpu().numpy()
+        res["T_prev"] = T.cpu().numpy()
+    say(f"[{wl.name}] gpu step")
+    m.dllm_refresh_qkv_rope_scatter(layer.cache, h_cur, idx_t, layer.w, Hq, wl.rope_base, q)
+    m.dllm_block_attention(layer.cache, q, Hq, scale, out, lse, mass if track else None)
+    if track:
+        m.dllm_drift_check(layer.cache, Hq, k, wl.gamma, T, buf, mass, sigma, refresh)
+    torch.cuda.synchronize()
+    res.update(layer=layer, q=q.float().cpu().numpy(), out=out.float().cpu().numpy(),
+               lse=lse.cpu().numpy())
+    if track:
+        res.update(mass=mass.cpu().numpy(), sigma=sigma.cpu().numpy(),
+                   refresh=refresh.cpu().numpy(), T=T.cpu().numpy())
+    return res
+
+
+def topk_margin(a: np.ndarray, k: int) -> np.ndarray:
+    """Relative gap between the k-th and (k+1)-th largest values of each row of a [..., S]."""
+    s = -np.sort(-a, axis=-1)
+    if a.shape[-1] <= k:
+        return np.full(a.shape[:-1], np.inf)
+    return (s[..., k - 1] - s[..., k]) / np.maximum(np.abs(s[..., k - 1]), 1e-300)
+
+
+# FP8 cache bar.  One e4m3 step near zero (2^-9 of the row scale) is smaller than the error of
+# an fp32 dot product over H terms, so codes are compared as the correct rounding of a value
+# within DELTA * (row amax) of the oracle's exact value; DELTA = 2^-13 is 80x tighter than
+# the 1e-2 bar on bf16 K/V rows.
+FP8_DELTA = 2.0 ** -13
+
+
+def e4m3_halfstep(mag: np.ndarray) -> np.ndarray:
+    """Half the e4m3 step at magnitude `mag` (in units of the scale)."""
+    e = np.floor(np.log2(np.maximum(mag, 2.0 ** -6)))
+    return 2.0 ** (np.minimum(e, 8) - 3) / 2
+
+
+def check_fp8_rows(codes: np.ndarray, scales: np.ndarray, exact: np.ndarray, ocodes: np.ndarray):
+    """codes [..., D] uint8 and scales [...] from the GPU; exact [..., D] float64 values before
+    quantisation and ocodes the oracle's codes.  Returns the number of codes more than one
+    step from the oracle's (allowed only where the bound below holds)."""
+    amax = np.abs(exact).max(axis=-1, keepdims=True)
+    s = scales.astype(np.float64)[..., None]
+    deq = oracle.e4m3_decode(codes) * s
+    delta = FP8_DELTA * amax
+    bound = (e4m3_halfstep((np.abs(exact) + delta) / np.where(s == 0, 1, s)) * s + delta)
+    bad = np.abs(deq - exact) > bound * (1 + 1e-12)
+    assert not bad.any(), f"{int(bad.sum())} FP8 codes off by more than the bound"
+    def ordinal(c):
+        c = c.astype(np.int32)
+        return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+    return int((np.abs(ordinal(codes) - ordinal(ocodes)) > 1).sum())
