@@ -237,6 +237,17 @@ def run(args):
     }
     del layers
     torch.cuda.empty_cache()
+    if args.copy_calibration:
+        # A plain device copy of known size, so HBM byte counters read under a profiler can be
+        # scaled by what they report for a copy (reads = writes = the buffer size).
+        nb = args.copy_calibration << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = nb
+        del src, dst
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
     print(json.dumps(result), flush=True)
@@ -290,6 +301,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="layer instances to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="after timing, run a plain device copy of this size (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (--gpus {args.gpus} "

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int qtiles, int spl
 
   // Q^T fragments for the wave's 32 packed rows (two 16-column tiles).
   const bf16_t* q = (const bf16_t*)a.q;
-  uint4 qf[2][DS];
+  u32x4 qf[2][DS];
   const int row0 = qt * QT + qw * 32;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
@@ -76,8 +76,8 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int qtiles, int spl
     const bf16_t* src = q + (((size_t)b * a.n + i) * a.Hq + g * G + hh) * D + lg * 8;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      const uint4 x = *(const uint4*)(src + ds * 32);
-      qf[ct][ds] = ok ? x : uint4{0u, 0u, 0u, 0u};
+      const u32x4 x = *(const u32x4*)(src + ds * 32);
+      qf[ct][ds] = ok ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int qtiles, int spl
   constexpr int ELT = (KIND == kCacheFP8) ? 1 : 2;
 
   // Register-staged loads of one tile (this thread's units of K and V, plus scales).
-  uint4 kreg[UPT], vreg[UPT];
+  u32x4 kreg[UPT], vreg[UPT];
   float sreg = 0.f;
   auto load_tile = [&](int tile) {
     const int key0 = kbeg + tile * kKeys;
@@ -106,18 +106,15 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int qtiles, int spl
       if constexpr (KIND == kCacheFP8) {
         const uint2 kx = *(const uint2*)(kc + off);
         const uint2 vx = *(const uint2*)(vc + off);
-        uint4 k8, v8;
-        e4m3x4_to_bf16x4(kx.x, k8.x, k8.y);
-        e4m3x4_to_bf16x4(kx.y, k8.z, k8.w);
-        e4m3x4_to_bf16x4(vx.x, v8.x, v8.y);
-        e4m3x4_to_bf16x4(vx.y, v8.z, v8.w);
-        kreg[u] = ok ? k8 : uint4{0u, 0u, 0u, 0u};
-        vreg[u] = ok ? v8 : uint4{0u, 0u, 0u, 0u};
+        const u32x4 k8 = e4m3x8_to_bf16x8(kx.x, kx.y);
+        const u32x4 v8 = e4m3x8_to_bf16x8(vx.x, vx.y);
+        kreg[u] = ok ? k8 : u32x4{0u, 0u, 0u, 0u};
+        vreg[u] = ok ? v8 : u32x4{0u, 0u, 0u, 0u};
       } else {
-        const uint4 kx = *(const uint4*)(kc + off);
-        const uint4 vx = *(const uint4*)(vc + off);
-        kreg[u] = ok ? kx : uint4{0u, 0u, 0u, 0u};
-        vreg[u] = ok ? vx : uint4{0u, 0u, 0u, 0u};
+        const u32x4 kx = *(const u32x4*)(kc + off);
+        const u32x4 vx = *(const u32x4*)(vc + off);
+        kreg[u] = ok ? kx : u32x4{0u, 0u, 0u, 0u};
+        vreg[u] = ok ? vx : u32x4{0u, 0u, 0u, 0u};
       }
     }
     if constexpr (KIND == kCacheFP8) {
@@ -138,7 +135,7 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int qtiles, int spl
       const int unit = gt + u * 64 * QW;
       const int r = unit / DC, ch = unit % DC;
       const int pr = perm_row(r);
-      *(uint4*)(KT + (pr * DC + (ch ^ (pr & 7))) * 16) = kreg[u];
+      *(u32x4*)(KT + (pr * DC + (ch ^ (pr & 7))) * 16) = kreg[u];
       const uint32_t vw[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -178,12 +175,12 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int qtiles, int spl
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
           const int row = kt * 16 + l16, ch = ds * 4 + lg;
-          kf[kt][ds] = as_bf16x8(*(const uint4*)(R + (row * DC + (ch ^ (row & 7))) * 16));
+          kf[kt][ds] = as_bf16x8(*(const u32x4*)(R + (row * DC + (ch ^ (row & 7))) * 16));
         }
       bf16x8 vf[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        vf[dt] = as_bf16x8(*(const uint4*)(VT + (dt * 16 + l16) * kVtStride + lg * 8));
+        vf[dt] = as_bf16x8(*(const u32x4*)(VT + (dt * 16 + l16) * kVtStride + lg * 8));
       float ksc[8], vsc[8];
       bool kval[8];
 #pragma unroll
@@ -227,7 +224,7 @@ __global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int qtiles, int spl
 #pragma unroll
           for (int e = 0; e < 8; ++e) p[e] *= vsc[e];
         }
-        uint4 pw;
+        u32x4 pw;
         pw.x = pack_bf16x2(p[0], p[1]);
         pw.y = pack_bf16x2(p[2], p[3]);
         pw.z = pack_bf16x2(p[4], p[5]);
@@ -387,15 +384,14 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a) {
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
       const size_t off = ((head_base + (ok ? key : 0)) * D + ds * 32 + lg * 8) * ELT;
-      uint4 x;
+      u32x4 x;
       if constexpr (KIND == kCacheFP8) {
         const uint2 w8 = *(const uint2*)(kc + off);
-        e4m3x4_to_bf16x4(w8.x, x.x, x.y);
-        e4m3x4_to_bf16x4(w8.y, x.z, x.w);
+        x = e4m3x8_to_bf16x8(w8.x, w8.y);
       } else {
-        x = *(const uint4*)(kc + off);
+        x = *(const u32x4*)(kc + off);
       }
-      kf[kt][ds] = as_bf16x8(ok ? x : uint4{0u, 0u, 0u, 0u});
+      kf[kt][ds] = as_bf16x8(ok ? x : u32x4{0u, 0u, 0u, 0u});
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -415,8 +411,8 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a) {
     bf16x8 qf[DS];
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      const uint4 x = *(const uint4*)(src + ds * 32);
-      qf[ds] = as_bf16x8(ok ? x : uint4{0u, 0u, 0u, 0u});
+      const u32x4 x = *(const u32x4*)(src + ds * 32);
+      qf[ds] = as_bf16x8(ok ? x : u32x4{0u, 0u, 0u, 0u});
     }
     const float lse2 = ok ? a.lse[((size_t)b * a.Hq + h) * a.n + i] * kLog2e : 0.f;
 #pragma unroll

@@ -12,6 +12,9 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+// 16 bytes as a native vector: arrays of these stay in registers (arrays of HIP's uint4,
+// a union-based struct, were left in scratch memory by the compiler).
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef uint16_t bf16_t;  // raw bf16 bits in memory
 
 constexpr int kWave = 64;
@@ -62,6 +65,14 @@ __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint3
   hi = __builtin_bit_cast(uint32_t, b);
 }
 
+// Eight E4M3 codes (two words) -> eight bf16 values packed in 16 bytes.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  uint32_t a, b, c, d;
+  e4m3x4_to_bf16x4(w0, a, b);
+  e4m3x4_to_bf16x4(w1, c, d);
+  return u32x4{a, b, c, d};
+}
+
 // --------------------------------------------------------------------------- MFMA -------
 
 // D(16x16, fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l supplies A row l%16 and B column
@@ -76,6 +87,7 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ------------------------------------------------------------------------ reductions ----
 

@@ -93,31 +93,32 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
     wsrc[u] = w + (size_t)(j * D + c) * a.H + cchunk * EPC;
   }
 
-  uint4 areg[A_PER_T], wreg[W_PER_T];
-  const uint4 zero = {0u, 0u, 0u, 0u};
-  auto load_stage = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < A_PER_T; ++u) {
-      const uint4 x = *(const uint4*)(asrc[u] + k0);
-      areg[u] = aval[u] ? x : zero;
-    }
-#pragma unroll
-    for (int u = 0; u < W_PER_T; ++u) wreg[u] = *(const uint4*)(wsrc[u] + k0);
-  };
-  auto store_stage = [&](int buf) {
-    char* A = smem + buf * STAGE;
-    char* W = A + TM * BKC * 16;
-#pragma unroll
-    for (int u = 0; u < A_PER_T; ++u) {
-      const int r = t / BKC + u * (256 / BKC);
-      *(uint4*)(A + (r * BKC + (cchunk ^ (r & (BKC - 1)))) * 16) = areg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < W_PER_T; ++u) {
-      const int c = t / BKC + u * (256 / BKC);
-      *(uint4*)(W + (c * BKC + (cchunk ^ (c & (BKC - 1)))) * 16) = wreg[u];
-    }
-  };
+  // Stage loads and stores are written out as macros, not lambdas: a lambda capturing these
+  // per-thread arrays by reference left them in scratch memory.
+  u32x4 areg[A_PER_T], wreg[W_PER_T];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#define DLLM_LOAD_STAGE(k0)                                                   \
+  do {                                                                        \
+    _Pragma("unroll") for (int u = 0; u < A_PER_T; ++u) {                     \
+      const u32x4 x_ = *(const u32x4*)(asrc[u] + (k0));                       \
+      areg[u] = aval[u] ? x_ : zero;                                          \
+    }                                                                         \
+    _Pragma("unroll") for (int u = 0; u < W_PER_T; ++u)                       \
+      wreg[u] = *(const u32x4*)(wsrc[u] + (k0));                              \
+  } while (0)
+#define DLLM_STORE_STAGE(buf)                                                 \
+  do {                                                                        \
+    char* A_ = smem + (buf) * STAGE;                                          \
+    char* W_ = A_ + TM * BKC * 16;                                            \
+    _Pragma("unroll") for (int u = 0; u < A_PER_T; ++u) {                     \
+      const int r_ = t / BKC + u * (256 / BKC);                               \
+      *(u32x4*)(A_ + (r_ * BKC + (cchunk ^ (r_ & (BKC - 1)))) * 16) = areg[u]; \
+    }                                                                         \
+    _Pragma("unroll") for (int u = 0; u < W_PER_T; ++u) {                     \
+      const int c_ = t / BKC + u * (256 / BKC);                               \
+      *(u32x4*)(W_ + (c_ * BKC + (cchunk ^ (c_ & (BKC - 1)))) * 16) = wreg[u]; \
+    }                                                                         \
+  } while (0)
 
   int colv[CT];
 #pragma unroll
@@ -135,11 +136,11 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
 
   const int stages = a.H / BK;
   const int per_part = stages / kKSplit;
-  load_stage(0);
-  store_stage(0);
+  DLLM_LOAD_STAGE(0);
+  DLLM_STORE_STAGE(0);
   __syncthreads();
   for (int s = 0; s < stages; ++s) {
-    if (s + 1 < stages) load_stage((s + 1) * BK);
+    if (s + 1 < stages) DLLM_LOAD_STAGE((s + 1) * BK);
     const char* A = smem + (s & 1) * STAGE;
     const char* W = A + TM * BKC * 16;
     if constexpr (BF) {
@@ -150,12 +151,12 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int r = wm * (TM / 2) + rt * 16 + l16;
-          af[rt] = as_bf16x8(*(const uint4*)(A + (r * BKC + (c ^ (r & (BKC - 1)))) * 16));
+          af[rt] = as_bf16x8(*(const u32x4*)(A + (r * BKC + (c ^ (r & (BKC - 1)))) * 16));
         }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int col = colv[ct];
-          bfr[ct] = as_bf16x8(*(const uint4*)(W + (col * BKC + (c ^ (col & (BKC - 1)))) * 16));
+          bfr[ct] = as_bf16x8(*(const u32x4*)(W + (col * BKC + (c ^ (col & (BKC - 1)))) * 16));
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
           acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    if (s + 1 < stages) store_stage((s + 1) & 1);
+    if (s + 1 < stages) DLLM_STORE_STAGE((s + 1) & 1);
     __syncthreads();
   }
 
@@ -245,12 +246,12 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
     if (which == 0 || KIND != kCacheFP8) {
       void* base = which == 0 ? a.q_out : which == 1 ? a.kc : a.vc;
       if constexpr (BF) {
-        uint4 o;
+        u32x4 o;
         o.x = pack_bf16x2(x[0], x[1]);
         o.y = pack_bf16x2(x[2], x[3]);
         o.z = pack_bf16x2(x[4], x[5]);
         o.w = pack_bf16x2(x[6], x[7]);
-        *(uint4*)((bf16_t*)base + off + cpos) = o;
+        *(u32x4*)((bf16_t*)base + off + cpos) = o;
       } else {
         float* dst = (float*)base + off + cpos;
         *(float4*)dst = x0;

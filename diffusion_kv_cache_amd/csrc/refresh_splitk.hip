@@ -25,7 +25,7 @@ constexpr int kPrefetch = 6;   // k-steps of W in flight per wave
 // 12288-column step resident at once.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6)))
 void refresh_partial(RefreshArgs a, float* part) {
-  extern __shared__ uint4 As[];                  // [32 rows][cpr chunks], swizzled
+  extern __shared__ u32x4 As[];                  // [32 rows][cpr chunks], swizzled
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
   const int N = (a.Hq + 2 * a.Hkv) * a.D;
   const int p = blockIdx.y;
@@ -37,10 +37,10 @@ void refresh_partial(RefreshArgs a, float* part) {
   const bf16_t* hid = (const bf16_t*)a.hidden;
   for (int q = t; q < 32 * cpr; q += 512) {
     const int r = q / cpr, c = q % cpr, m = m0 + r;
-    uint4 v = {0u, 0u, 0u, 0u};
+    u32x4 v = {0u, 0u, 0u, 0u};
     if (m < a.M) {
       const int b = m / a.n;
-      v = *(const uint4*)(hid + ((size_t)b * a.S + a.idx[m]) * a.H + kb + c * 8);
+      v = *(const u32x4*)(hid + ((size_t)b * a.S + a.idx[m]) * a.H + kb + c * 8);
     }
     As[r * cpr + (c ^ (r & mask))] = v;
   }
@@ -49,18 +49,18 @@ void refresh_partial(RefreshArgs a, float* part) {
   const bool col_ok = col < N;
   const bf16_t* wr = (const bf16_t*)a.w + (size_t)(col_ok ? col : N - 1) * a.H + kb + lg * 8;
   const int steps = Lp / 32;
-  uint4 wv[kPrefetch];
+  u32x4 wv[kPrefetch];
 #pragma unroll
   for (int u = 0; u < kPrefetch; ++u)
-    if (u < steps) wv[u] = *(const uint4*)(wr + u * 32);
+    if (u < steps) wv[u] = *(const u32x4*)(wr + u * 32);
   __syncthreads();
 
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   for (int s0 = 0; s0 < steps; s0 += kPrefetch) {
-    uint4 wn[kPrefetch];
+    u32x4 wn[kPrefetch];
 #pragma unroll
     for (int u = 0; u < kPrefetch; ++u)
-      if (s0 + kPrefetch + u < steps) wn[u] = *(const uint4*)(wr + (s0 + kPrefetch + u) * 32);
+      if (s0 + kPrefetch + u < steps) wn[u] = *(const u32x4*)(wr + (s0 + kPrefetch + u) * 32);
 #pragma unroll
     for (int u = 0; u < kPrefetch; ++u) {
       if (s0 + u < steps) {
