@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdllm_cache.so")
-SOURCES = ["api.hip", "refresh.hip", "refresh_splitk.hip", "attention.hip", "drift.hip"]
+SOURCES = ["api.hip", "refresh.hip", "refresh_splitk.hip", "attention.hip", "attention_fwd.hip", "drift.hip"]
 ARCH = os.environ.get("DLLM_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -1,21 +1,11 @@
-// Bidirectional block attention over the whole cache, its split-KV merge, and the column
-// attention-mass pass.
+// Split-KV merge and the column attention-mass pass of the block attention, the fp32 path,
+// and the launcher (the MFMA forward pass is in attention_fwd.hip).
 //
 // What it computes: softmax(q k^T * scale) v with no mask (Flash-Cache article, section 3.1;
 // LaCache Technical Summary, Problem Statement: bidirectional attention over the full
 // context); the online-softmax state (m, l, O~) and its merge over disjoint key ranges
 // (LaCache Methodology 1, FACache); the column mass sum_i p_ij that ranks the most-attended
 // tokens (Flash-dLLM summary, selective cache tracking).
-//
-// MFMA formulation (bf16 / fp8 caches).  A workgroup owns (b, KV head g, a tile of packed
-// query rows r = i * G + (h - g * G), one key split).  Scores are computed transposed,
-// S^T = K Q^T (A = K rows from LDS, B = Q^T held in registers), so each lane owns one query
-// and eight keys; the key rows of the two 16-row MFMA tiles are permuted so those eight keys
-// are consecutive.  Then O^T += V^T P^T takes P^T straight from the score registers and V^T
-// from a transposed LDS copy (one 16-byte read per MFMA).  The running max needs two lane
-// exchanges per tile; the normaliser is reduced once at the end.  FP8: K and V are converted
-// to bf16 exactly (every E4M3 value is a bf16 value); the K row scale multiplies the score
-// column and the V row scale is folded into P.
 #include <math.h>
 
 #include "common.hpp"
@@ -27,299 +17,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kKeys = 32;          // keys per tile
-constexpr int kVtStride = 40;      // bf16 per transposed-V row (32 keys + 8 pad)
-
-__device__ __forceinline__ int perm_row(int r) {  // key r of a 32-key tile -> LDS row
-  return ((r >> 2) & 1) * 16 + ((r >> 3) << 2) + (r & 3);
-}
-
-template <int KIND, int QW, int D>
-__global__ __launch_bounds__(256) void attn_mfma(AttnArgs a, int qtiles, int splits, int kps) {
-  constexpr int KW = 4 / QW;
-  constexpr int QT = 32 * QW;
-  constexpr int DC = D / 8;          // bf16 chunks per key row
-  constexpr int DT = D / 16;         // output d tiles
-  constexpr int DS = D / 32;         // score d steps
-  constexpr int K_BYTES = kKeys * D * 2;
-  constexpr int VT_BYTES = D * kVtStride * 2;
-  constexpr int REGION = K_BYTES + VT_BYTES + 2 * kKeys * 4;
-  constexpr int UNITS = kKeys * DC;                 // 8-element units per tile per tensor
-  constexpr int UPT = UNITS / (64 * QW);            // units per thread
-  constexpr int MERGE = (KW - 1) * QW * (2 * DT * 4 * 64 + 4 * 64) * 4;
-  constexpr int SMEM = (KW * REGION > MERGE) ? KW * REGION : MERGE;
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
-
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int qw = wave % QW, kw = wave / QW;
-  const int gt = qw * 64 + lane;                    // thread index within the kw group
-
-  int id = blockIdx.x;
-  const int split = id % splits;
-  id /= splits;
-  const int qt = id % qtiles;
-  const int bg = id / qtiles;
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int G = a.Hq / a.Hkv;
-  const int rows = a.n * G;
-  const float c = a.scale * kLog2e;
-
-  // Q^T fragments for the wave's 32 packed rows (two 16-column tiles).
-  const bf16_t* q = (const bf16_t*)a.q;
-  u32x4 qf[2][DS];
-  const int row0 = qt * QT + qw * 32;
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int r = row0 + ct * 16 + l16;
-    const bool ok = r < rows;
-    const int i = ok ? r / G : 0, hh = ok ? r % G : 0;
-    const bf16_t* src = q + (((size_t)b * a.n + i) * a.Hq + g * G + hh) * D + lg * 8;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const u32x4 x = *(const u32x4*)(src + ds * 32);
-      qf[ct][ds] = ok ? x : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  const int kbeg = split * kps;
-  const int kend = min(a.S, kbeg + kps);
-  const int ntiles = (kend - kbeg + kKeys - 1) / kKeys;
-  const int iters = (ntiles + KW - 1) / KW;
-
-  const size_t head_base = ((size_t)b * a.Hkv + g) * a.S;
-  const char* kc = (const char*)a.kc;
-  const char* vc = (const char*)a.vc;
-  constexpr int ELT = (KIND == kCacheFP8) ? 1 : 2;
-
-  // Register-staged loads of one tile (this thread's units of K and V, plus scales).
-  u32x4 kreg[UPT], vreg[UPT];
-  float sreg = 0.f;
-  auto load_tile = [&](int tile) {
-    const int key0 = kbeg + tile * kKeys;
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = gt + u * 64 * QW;
-      const int r = unit / DC, ch = unit % DC;
-      const int key = key0 + r;
-      const bool ok = tile < ntiles && key < kend;
-      const size_t off = ((head_base + (ok ? key : kbeg)) * D + ch * 8) * ELT;
-      if constexpr (KIND == kCacheFP8) {
-        const uint2 kx = *(const uint2*)(kc + off);
-        const uint2 vx = *(const uint2*)(vc + off);
-        const u32x4 k8 = e4m3x8_to_bf16x8(kx.x, kx.y);
-        const u32x4 v8 = e4m3x8_to_bf16x8(vx.x, vx.y);
-        kreg[u] = ok ? k8 : u32x4{0u, 0u, 0u, 0u};
-        vreg[u] = ok ? v8 : u32x4{0u, 0u, 0u, 0u};
-      } else {
-        const u32x4 kx = *(const u32x4*)(kc + off);
-        const u32x4 vx = *(const u32x4*)(vc + off);
-        kreg[u] = ok ? kx : u32x4{0u, 0u, 0u, 0u};
-        vreg[u] = ok ? vx : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    if constexpr (KIND == kCacheFP8) {
-      if (gt < 2 * kKeys) {
-        const int r = gt % kKeys, key = key0 + r;
-        const bool ok = tile < ntiles && key < kend;
-        const float* sp = gt < kKeys ? a.ks : a.vs;
-        sreg = ok ? sp[head_base + key] : 0.f;
-      }
-    }
-  };
-  auto store_tile = [&]() {
-    char* R = smem + kw * REGION;
-    char* KT = R;
-    bf16_t* VT = (bf16_t*)(R + K_BYTES);
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = gt + u * 64 * QW;
-      const int r = unit / DC, ch = unit % DC;
-      const int pr = perm_row(r);
-      *(u32x4*)(KT + (pr * DC + (ch ^ (pr & 7))) * 16) = kreg[u];
-      const uint32_t vw[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        VT[(ch * 8 + 2 * e) * kVtStride + r] = (bf16_t)(vw[e] & 0xffffu);
-        VT[(ch * 8 + 2 * e + 1) * kVtStride + r] = (bf16_t)(vw[e] >> 16);
-      }
-    }
-    if constexpr (KIND == kCacheFP8) {
-      if (gt < 2 * kKeys) ((float*)(R + K_BYTES + VT_BYTES))[gt] = sreg;
-    }
-  };
-
-  f32x4 oacc[2][DT];
-  float m[2], lsum[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    m[ct] = -INFINITY;
-    lsum[ct] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  load_tile(kw);
-  for (int it = 0; it < iters; ++it) {
-    const int tile = it * KW + kw;
-    store_tile();
-    __syncthreads();
-    if (it + 1 < iters) load_tile(tile + KW);
-    if (tile < ntiles) {
-      const char* R = smem + kw * REGION;
-      const bf16_t* VT = (const bf16_t*)(R + K_BYTES);
-      const float* SC = (const float*)(R + K_BYTES + VT_BYTES);
-      const int key0 = kbeg + tile * kKeys;
-      bf16x8 kf[2][DS];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          const int row = kt * 16 + l16, ch = ds * 4 + lg;
-          kf[kt][ds] = as_bf16x8(*(const u32x4*)(R + (row * DC + (ch ^ (row & 7))) * 16));
-        }
-      bf16x8 vf[DT];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        vf[dt] = as_bf16x8(*(const u32x4*)(VT + (dt * 16 + l16) * kVtStride + lg * 8));
-      float ksc[8], vsc[8];
-      bool kval[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kval[e] = key0 + lg * 8 + e < kend;
-        if constexpr (KIND == kCacheFP8) {
-          ksc[e] = SC[lg * 8 + e];
-          vsc[e] = SC[kKeys + lg * 8 + e];
-        }
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int ds = 0; ds < DS; ++ds) sacc[kt] = mfma_bf16(kf[kt][ds], as_bf16x8(qf[ct][ds]), sacc[kt]);
-        float y[8];
-        float mt = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float sv = sacc[e >> 2][e & 3];
-          if constexpr (KIND == kCacheFP8) sv *= ksc[e];
-          y[e] = kval[e] ? sv * c : -INFINITY;
-          mt = fmaxf(mt, y[e]);
-        }
-        mt = wave_max_xor(mt, 16);
-        mt = wave_max_xor(mt, 32);
-        const float mnew = fmaxf(m[ct], mt);
-        const bool none = (mnew == -INFINITY);
-        const float alpha = none ? 1.f : exp2f(m[ct] - mnew);
-        float p[8], ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = none ? 0.f : exp2f(y[e] - mnew);
-          ps += p[e];
-        }
-        lsum[ct] = lsum[ct] * alpha + ps;
-        m[ct] = mnew;
-        if constexpr (KIND == kCacheFP8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] *= vsc[e];
-        }
-        u32x4 pw;
-        pw.x = pack_bf16x2(p[0], p[1]);
-        pw.y = pack_bf16x2(p[2], p[3]);
-        pw.z = pack_bf16x2(p[4], p[5]);
-        pw.w = pack_bf16x2(p[6], p[7]);
-        const bf16x8 pb = as_bf16x8(pw);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          oacc[ct][dt] = oacc[ct][dt] * alpha;
-          oacc[ct][dt] = mfma_bf16(vf[dt], pb, oacc[ct][dt]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // Normaliser: each lane group held its own keys' share.
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    lsum[ct] += __shfl_xor(lsum[ct], 16, kWave);
-    lsum[ct] += __shfl_xor(lsum[ct], 32, kWave);
-  }
-
-  // Merge the KW key groups in order (their ranges are disjoint).
-  if constexpr (KW > 1) {
-    float* mb = (float*)smem;
-    constexpr int BLK = 2 * DT * 4 * 64 + 4 * 64;
-    if (kw > 0) {
-      float* dst = mb + ((kw - 1) * QW + qw) * BLK;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) dst[((ct * DT + dt) * 4 + v) * 64 + lane] = oacc[ct][dt][v];
-        dst[2 * DT * 4 * 64 + (ct * 2) * 64 + lane] = m[ct];
-        dst[2 * DT * 4 * 64 + (ct * 2 + 1) * 64 + lane] = lsum[ct];
-      }
-    }
-    __syncthreads();
-    if (kw > 0) return;
-    for (int w2 = 1; w2 < KW; ++w2) {
-      const float* src = mb + ((w2 - 1) * QW + qw) * BLK;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const float m2 = src[2 * DT * 4 * 64 + (ct * 2) * 64 + lane];
-        const float l2 = src[2 * DT * 4 * 64 + (ct * 2 + 1) * 64 + lane];
-        const float mm = fmaxf(m[ct], m2);
-        const float a0 = (m[ct] == -INFINITY) ? 0.f : exp2f(m[ct] - mm);
-        const float a1 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mm);
-        lsum[ct] = lsum[ct] * a0 + l2 * a1;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            oacc[ct][dt][v] = oacc[ct][dt][v] * a0 + src[((ct * DT + dt) * 4 + v) * 64 + lane] * a1;
-        m[ct] = mm;
-      }
-    }
-  }
-
-  // Write: final output when unsplit, else the partial state of this split.
-  const size_t nrows_all = (size_t)a.B * a.Hkv * rows;
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const int r = row0 + ct * 16 + l16;
-    if (r >= rows) continue;
-    const int i = r / G, h = g * G + r % G;
-    if (splits == 1) {
-      const float inv = 1.f / lsum[ct];
-      bf16_t* o = (bf16_t*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 16 + lg * 4;
-        uint2 w2;
-        w2.x = pack_bf16x2(oacc[ct][dt][0] * inv, oacc[ct][dt][1] * inv);
-        w2.y = pack_bf16x2(oacc[ct][dt][2] * inv, oacc[ct][dt][3] * inv);
-        *(uint2*)(o + d) = w2;
-      }
-      if (lg == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = (m[ct] + log2f(lsum[ct])) * kLn2;
-    } else {
-      const size_t pr = (size_t)split * nrows_all + (size_t)bg * rows + r;
-      float* po = a.part + pr * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 16 + lg * 4;
-        *(float4*)(po + d) = make_float4(oacc[ct][dt][0], oacc[ct][dt][1], oacc[ct][dt][2], oacc[ct][dt][3]);
-      }
-      if (lg == 0) {
-        float* ml = a.part + (size_t)splits * nrows_all * D + pr * 2;
-        ml[0] = m[ct];
-        ml[1] = lsum[ct];
-      }
-    }
-  }
-}
 
 // Combine split partial states in split order: one wave per packed query row.
 template <typename OutT, int D>
@@ -496,11 +193,7 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int rows = a.n * G;
   const int qtiles = (rows + p.qt - 1) / p.qt;
-  const int grid = a.B * a.Hkv * qtiles * p.splits;
-  if (p.qt == 128) attn_mfma<KIND, 4, D><<<grid, 256, 0, s>>>(a, qtiles, p.splits, p.kps);
-  else if (p.qt == 64) attn_mfma<KIND, 2, D><<<grid, 256, 0, s>>>(a, qtiles, p.splits, p.kps);
-  else attn_mfma<KIND, 1, D><<<grid, 256, 0, s>>>(a, qtiles, p.splits, p.kps);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_attn_fwd<KIND, D>(a, p, qtiles, s);
   if (e != hipSuccess) return e;
   if (p.splits > 1) {
     attn_merge<bf16_t, D><<<a.B * a.Hkv * rows, 64, 0, s>>>(a, p.splits);

@@ -1,0 +1,462 @@
+// Bidirectional block attention, forward pass (MFMA, split over keys).
+//
+// What it computes: softmax(q k^T * scale) v with no mask over every cache row (Flash-Cache
+// article, section 3.1; LaCache Technical Summary, Problem Statement: bidirectional attention
+// over the full context), plus the online-softmax state (m, l, O~) of each key split, merged
+// in a fixed order (the FACache identity, LaCache Methodology 1).
+//
+// A workgroup owns (b, KV head g, a tile of packed query rows r = i * G + (h - g * G), one
+// key split).  Its four waves form KW groups of QW waves; each wave holds 32 query rows, each
+// group streams its own share of the split's 32-key tiles through a two-stage LDS ring.
+//
+// Layout of a tile in LDS: K and V rows as in the cache (row-major, bf16), 16-byte chunks
+// XOR-swizzled per row.  bf16 caches are copied global -> LDS by the DMA path of the vector
+// memory unit (no registers); FP8 caches go through registers, are converted to bf16 (exact)
+// and stored in the same layout.
+//
+// Scores are computed transposed, S^T = K Q^T (A = K rows, read with their key order
+// permuted so that each lane's eight score slots are eight consecutive keys; B = Q^T held in
+// registers).  O^T += V^T P^T takes P^T straight from the score registers; V^T comes from two
+// transposing LDS reads (ds_read_b64_tr_b16), which hand each lane four consecutive keys of
+// one column.  Softmax rescaling is lazy: the running maximum used for the exponentials only
+// moves when a score exceeds it by more than 2^8 (in base 2), so most tiles skip the rescale
+// of the accumulators.  FP8: the K row scale multiplies the score column and the V row scale
+// is folded into P.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dllm {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kKeys = 32;          // keys per tile
+constexpr float kLazy = 8.0f;      // log2 headroom before the running max is moved
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Per-row chunk swizzles (chunk index XOR f(row)).  K: the 16 rows one MFMA operand read
+// touches hit 16 (D = 128) or 8 (D = 64) distinct chunk slots.  V: the four rows of one
+// transposing read hit distinct 32-byte slot pairs.
+// Workgroup barrier for the DMA ring: LDS reads of this wave are complete (lgkmcnt 0) and
+// the DMA blocks it must wait for were waited on explicitly beforehand (vmcnt), so the
+// barrier itself need not drain the prefetch still in flight, which the release fence of
+// __syncthreads would.  The empty asm keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return D == 128 ? ((r & 3) | (((r >> 3) & 3) << 2)) : ((r & 3) | (((r >> 3) & 1) << 2));
+}
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+
+// Key r of a 32-key tile that MFMA row rho of key-subtile kt reads: the eight score slots of
+// lane group lg are then keys 8 lg .. 8 lg + 7.
+__device__ __forceinline__ int perm_key(int kt, int rho) { return ((rho >> 2) << 3) + (kt << 2) + (rho & 3); }
+
+template <int KIND, int QW, int D>
+struct Cfg {
+  static constexpr int KW = 4 / QW;              // key groups
+  static constexpr int RB = D * 2;               // bytes per LDS row
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int TILE = kKeys * RB;        // bytes of one K (or V) tile
+  static constexpr int SC = (KIND == kCacheFP8) ? 2 * kKeys * 4 : 0;
+  static constexpr int STAGE = 2 * TILE + SC;    // K, V, scales
+  static constexpr int DS = D / 32, DT = D / 16;
+  static constexpr int GT = 64 * QW;             // threads per group
+  static constexpr int DMA_T = TILE / 1024;      // 1 KB DMA blocks per tensor tile
+  static constexpr int DMA_W = DMA_T / QW;       // ... per wave
+  static constexpr int MERGE = (KW - 1) * QW * (DT * 4 * 64 + 2 * 64) * 4;  // one column tile
+};
+
+// One LDS-DMA instruction: lane l copies 16 bytes from its global address g to
+// lds_block + 16 l (lds_block is wave-uniform).  Issued from inline asm so that the
+// compiler's wait insertion, which cannot tell the two ring stages apart, does not drain the
+// prefetch before every LDS read; the ring waits on the vector-memory counter itself.
+__device__ __forceinline__ void dma_16B(const char* g, const char* lds_block) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_block);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(base)
+               : "memory");
+}
+
+// bf16: this wave's share of the DMA blocks of one tile (K and V) into stage memory `st`.
+template <int KIND, int QW, int D>
+__device__ __forceinline__ void dma_tile(char* st, const char* kc, const char* vc, size_t head_base,
+                                         int key0, int kbeg, int kend, int qw, int lane) {
+  using C = Cfg<KIND, QW, D>;
+  constexpr int RPI = 1024 / C::RB;              // rows per DMA block
+#pragma unroll
+  for (int u = 0; u < C::DMA_W; ++u) {
+    const int blk = qw + QW * u;
+    const int r = blk * RPI + lane / C::CPR, s = lane % C::CPR;
+    const int key = key0 + r;
+    const size_t row = head_base + (key < kend ? key : kbeg);
+    const char* ks = kc + (row * D + (size_t)((s ^ swz_k<D>(r)) * 8)) * 2;
+    const char* vs = vc + (row * D + (size_t)((s ^ swz_v(r)) * 8)) * 2;
+    dma_16B(ks, st + blk * 1024);
+    dma_16B(vs, st + C::TILE + blk * 1024);
+  }
+}
+
+// FP8: registers for this thread's units of one tile (16 codes each) and its scale.
+template <int KIND, int QW, int D>
+struct Fp8Stage {
+  static constexpr int UNITS = kKeys * D / 16;   // 16-byte units per tensor tile
+  static constexpr int UPT = (UNITS + 64 * QW - 1) / (64 * QW);
+  u32x4 k[UPT], v[UPT];
+  float sc;
+};
+
+template <int KIND, int QW, int D>
+__device__ __forceinline__ void fp8_load(Fp8Stage<KIND, QW, D>& f, const AttnArgs& a, const char* kc,
+                                         const char* vc, size_t head_base, int key0, int kbeg,
+                                         int kend, int gt) {
+  constexpr int UPR = D / 16;                    // units per row
+#pragma unroll
+  for (int u = 0; u < Fp8Stage<KIND, QW, D>::UPT; ++u) {
+    const int unit = gt + u * 64 * QW;
+    if (unit >= Fp8Stage<KIND, QW, D>::UNITS) break;
+    const int r = unit / UPR, c = unit % UPR;
+    const int key = key0 + r;
+    const size_t off = (head_base + (key < kend ? key : kbeg)) * D + c * 16;
+    f.k[u] = *(const u32x4*)(kc + off);
+    f.v[u] = *(const u32x4*)(vc + off);
+  }
+  if (gt < 2 * kKeys) {
+    const int r = gt % kKeys, key = key0 + r;
+    const float* sp = gt < kKeys ? a.ks : a.vs;
+    f.sc = key < kend ? sp[head_base + key] : 0.f;
+  }
+}
+
+template <int KIND, int QW, int D>
+__device__ __forceinline__ void fp8_store(const Fp8Stage<KIND, QW, D>& f, char* st, int gt) {
+  using C = Cfg<KIND, QW, D>;
+  constexpr int UPR = D / 16;
+#pragma unroll
+  for (int u = 0; u < Fp8Stage<KIND, QW, D>::UPT; ++u) {
+    const int unit = gt + u * 64 * QW;
+    if (unit >= Fp8Stage<KIND, QW, D>::UNITS) break;
+    const int r = unit / UPR, c0 = 2 * (unit % UPR);
+    const u32x4 k0 = e4m3x8_to_bf16x8(f.k[u].x, f.k[u].y), k1 = e4m3x8_to_bf16x8(f.k[u].z, f.k[u].w);
+    const u32x4 v0 = e4m3x8_to_bf16x8(f.v[u].x, f.v[u].y), v1 = e4m3x8_to_bf16x8(f.v[u].z, f.v[u].w);
+    *(u32x4*)(st + r * C::RB + ((c0 ^ swz_k<D>(r)) << 4)) = k0;
+    *(u32x4*)(st + r * C::RB + (((c0 + 1) ^ swz_k<D>(r)) << 4)) = k1;
+    *(u32x4*)(st + C::TILE + r * C::RB + ((c0 ^ swz_v(r)) << 4)) = v0;
+    *(u32x4*)(st + C::TILE + r * C::RB + (((c0 + 1) ^ swz_v(r)) << 4)) = v1;
+  }
+  if (gt < 2 * kKeys) ((float*)(st + 2 * C::TILE))[gt] = f.sc;
+}
+
+// One 32-key tile for one wave: scores, lazy online softmax, O^T update.
+template <int KIND, int QW, int D>
+__device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2][D / 32],
+                                             f32x4 (&oacc)[2][D / 16], float (&m)[2],
+                                             float (&lsum)[2], int key0, int kend, float c,
+                                             int l16, int lg) {
+  using C = Cfg<KIND, QW, D>;
+  const char* K = st;
+  const char* V = st + C::TILE;
+  const float* SC = (const float*)(st + 2 * C::TILE);
+  f32x4 sacc[2][2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) sacc[ct][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ds = 0; ds < C::DS; ++ds) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int R = perm_key(kt, l16), ch = ds * 4 + lg;
+      const bf16x8 kf = as_bf16x8(*(const u32x4*)(K + R * C::RB + ((ch ^ swz_k<D>(R)) << 4)));
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) sacc[ct][kt] = mfma_bf16(kf, as_bf16x8(qf[ct][ds]), sacc[ct][kt]);
+    }
+  }
+  float ksc[8], vsc[8];
+  bool kval[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kval[e] = key0 + lg * 8 + e < kend;
+    if constexpr (KIND == kCacheFP8) {
+      ksc[e] = SC[lg * 8 + e];
+      vsc[e] = SC[kKeys + lg * 8 + e];
+    }
+  }
+  bf16x8 pb[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    float y[8], mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float sv = sacc[ct][e >> 2][e & 3];
+      if constexpr (KIND == kCacheFP8) sv *= ksc[e];
+      y[e] = kval[e] ? sv * c : -INFINITY;
+      mt = fmaxf(mt, y[e]);
+    }
+    mt = wave_max_xor(mt, 16);
+    mt = wave_max_xor(mt, 32);
+    // Lazy rescale: move the running max only when a score would exceed it by 2^kLazy.
+    if (__any(mt > m[ct] + kLazy)) {
+      const float mn = fmaxf(m[ct], mt);
+      const float alpha = (mn == -INFINITY || m[ct] == -INFINITY) ? 0.f : exp2f(m[ct] - mn);
+      lsum[ct] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) oacc[ct][dt] = oacc[ct][dt] * alpha;
+      m[ct] = mn;
+    }
+    const bool none = (m[ct] == -INFINITY);
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = none ? 0.f : exp2f(y[e] - m[ct]);
+      ps += p[e];
+    }
+    lsum[ct] += ps;
+    if constexpr (KIND == kCacheFP8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] *= vsc[e];
+    }
+    u32x4 pw;
+    pw.x = pack_bf16x2(p[0], p[1]);
+    pw.y = pack_bf16x2(p[2], p[3]);
+    pw.z = pack_bf16x2(p[4], p[5]);
+    pw.w = pack_bf16x2(p[6], p[7]);
+    pb[ct] = as_bf16x8(pw);
+  }
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    s16x4 h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int R = 8 * lg + 4 * hh + (l16 >> 2);
+      const int d0 = 16 * dt + 4 * (l16 & 3);
+      const int ch = d0 >> 3;
+      const char* addr = V + R * C::RB + ((ch ^ swz_v(R)) << 4) + ((d0 & 4) ? 8 : 0);
+      h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)addr);
+    }
+    const u32x4 vw = {(uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16),
+                      (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16),
+                      (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16),
+                      (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16)};
+    const bf16x8 vf = as_bf16x8(vw);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) oacc[ct][dt] = mfma_bf16(vf, pb[ct], oacc[ct][dt]);
+  }
+}
+
+template <int KIND, int QW, int D>
+__global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int splits, int kps) {
+  using C = Cfg<KIND, QW, D>;
+  constexpr int KW = C::KW, QT = 32 * QW;
+  // Two stage arrays per key group: distinct allocations, so a DMA into one stage is known
+  // not to alias the reads of the other.
+  __shared__ __attribute__((aligned(16))) char stage0[KW * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[KW * C::STAGE];
+
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int qw = wave % QW, kw = wave / QW;
+  const int gt = qw * 64 + lane;
+
+  int id = blockIdx.x;
+  const int split = id % splits;
+  id /= splits;
+  const int qt = id % qtiles;
+  const int bg = id / qtiles;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int rows = a.n * G;
+  const float c = a.scale * kLog2e;
+
+  const bf16_t* q = (const bf16_t*)a.q;
+  u32x4 qf[2][C::DS];
+  const int row0 = qt * QT + qw * 32;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int r = row0 + ct * 16 + l16;
+    const bool ok = r < rows;
+    const int i = ok ? r / G : 0, hh = ok ? r % G : 0;
+    const bf16_t* src = q + (((size_t)b * a.n + i) * a.Hq + g * G + hh) * D + lg * 8;
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+      const u32x4 x = *(const u32x4*)(src + ds * 32);
+      qf[ct][ds] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const int kbeg = split * kps;
+  const int kend = min(a.S, kbeg + kps);
+  const int ntiles = (kend - kbeg + kKeys - 1) / kKeys;
+  const int iters = (ntiles + KW - 1) / KW;
+  const size_t head_base = ((size_t)b * a.Hkv + g) * a.S;
+  const char* kc = (const char*)a.kc;
+  const char* vc = (const char*)a.vc;
+  char* st0 = stage0 + kw * C::STAGE;
+  char* st1 = stage1 + kw * C::STAGE;
+
+  f32x4 oacc[2][C::DT];
+  float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) oacc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (KIND == kCacheFP8) {
+    Fp8Stage<KIND, QW, D> f;
+    fp8_load<KIND, QW, D>(f, a, kc, vc, head_base, kbeg + kw * kKeys, kbeg, kend, gt);
+    fp8_store<KIND, QW, D>(f, st0, gt);
+    for (int it = 0; it < iters; ++it) {
+      const int tile = it * KW + kw;
+      __syncthreads();
+      if (it + 1 < iters) fp8_load<KIND, QW, D>(f, a, kc, vc, head_base, kbeg + (tile + KW) * kKeys, kbeg, kend, gt);
+      if (tile < ntiles)
+        tile_compute<KIND, QW, D>((it & 1) ? st1 : st0, qf, oacc, m, lsum, kbeg + tile * kKeys, kend, c, l16, lg);
+      if (it + 1 < iters) fp8_store<KIND, QW, D>(f, (it & 1) ? st0 : st1, gt);
+    }
+  } else {
+    constexpr int PEND = 2 * C::DMA_W;           // DMA ops of one tile per wave
+    constexpr int WAIT_PREV = (PEND & 15) | (7 << 4) | (15 << 8) | ((PEND >> 4) << 14);
+    constexpr int WAIT_ALL = (7 << 4) | (15 << 8);
+    dma_tile<KIND, QW, D>(st0, kc, vc, head_base, kbeg + kw * kKeys, kbeg, kend, qw, lane);
+    for (int it = 0; it < iters; it += 2) {
+      // even iteration: compute stage 0 while stage 1 fills
+      {
+        const int tile = it * KW + kw;
+        if (it + 1 < iters) {
+          dma_tile<KIND, QW, D>(st1, kc, vc, head_base, kbeg + (tile + KW) * kKeys, kbeg, kend, qw, lane);
+          __builtin_amdgcn_s_waitcnt(WAIT_PREV);
+        } else {
+          __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+        }
+        ring_barrier();
+        if (tile < ntiles) tile_compute<KIND, QW, D>(st0, qf, oacc, m, lsum, kbeg + tile * kKeys, kend, c, l16, lg);
+        ring_barrier();
+      }
+      if (it + 1 >= iters) break;
+      // odd iteration: compute stage 1 while stage 0 fills
+      {
+        const int tile = (it + 1) * KW + kw;
+        if (it + 2 < iters) {
+          dma_tile<KIND, QW, D>(st0, kc, vc, head_base, kbeg + (tile + KW) * kKeys, kbeg, kend, qw, lane);
+          __builtin_amdgcn_s_waitcnt(WAIT_PREV);
+        } else {
+          __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+        }
+        ring_barrier();
+        if (tile < ntiles) tile_compute<KIND, QW, D>(st1, qf, oacc, m, lsum, kbeg + tile * kKeys, kend, c, l16, lg);
+        ring_barrier();
+      }
+    }
+  }
+
+  // Normaliser: each lane group held its own keys' share.
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    lsum[ct] += __shfl_xor(lsum[ct], 16, kWave);
+    lsum[ct] += __shfl_xor(lsum[ct], 32, kWave);
+  }
+
+  // Merge the KW key groups in order (their key ranges are disjoint), one column tile at a
+  // time through the (now idle) stage memory.
+  if constexpr (KW > 1) {
+    constexpr int BLK = C::DT * 4 * 64 + 2 * 64;
+    static_assert(C::MERGE <= KW * C::STAGE, "merge buffer does not fit");
+    float* mb = (float*)stage0;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      __syncthreads();
+      if (kw > 0) {
+        float* dst = mb + ((kw - 1) * QW + qw) * BLK;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) dst[(dt * 4 + v) * 64 + lane] = oacc[ct][dt][v];
+        dst[C::DT * 4 * 64 + lane] = m[ct];
+        dst[C::DT * 4 * 64 + 64 + lane] = lsum[ct];
+      }
+      __syncthreads();
+      if (kw == 0) {
+        for (int w2 = 1; w2 < KW; ++w2) {
+          const float* src = mb + ((w2 - 1) * QW + qw) * BLK;
+          const float m2 = src[C::DT * 4 * 64 + lane];
+          const float l2 = src[C::DT * 4 * 64 + 64 + lane];
+          const float mm = fmaxf(m[ct], m2);
+          const float a0 = (m[ct] == -INFINITY) ? 0.f : exp2f(m[ct] - mm);
+          const float a1 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mm);
+          lsum[ct] = lsum[ct] * a0 + l2 * a1;
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              oacc[ct][dt][v] = oacc[ct][dt][v] * a0 + src[(dt * 4 + v) * 64 + lane] * a1;
+          m[ct] = mm;
+        }
+      }
+    }
+    if (kw > 0) return;
+  }
+
+  // Final output when unsplit, else this split's partial state.
+  const size_t nrows_all = (size_t)a.B * a.Hkv * rows;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int r = row0 + ct * 16 + l16;
+    if (r >= rows) continue;
+    const int i = r / G, h = g * G + r % G;
+    if (splits == 1) {
+      const float inv = 1.f / lsum[ct];
+      bf16_t* o = (bf16_t*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int d = dt * 16 + lg * 4;
+        uint2 w2;
+        w2.x = pack_bf16x2(oacc[ct][dt][0] * inv, oacc[ct][dt][1] * inv);
+        w2.y = pack_bf16x2(oacc[ct][dt][2] * inv, oacc[ct][dt][3] * inv);
+        *(uint2*)(o + d) = w2;
+      }
+      if (lg == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = (m[ct] + log2f(lsum[ct])) * kLn2;
+    } else {
+      const size_t pr = (size_t)split * nrows_all + (size_t)bg * rows + r;
+      float* po = a.part + pr * D;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int d = dt * 16 + lg * 4;
+        *(float4*)(po + d) = make_float4(oacc[ct][dt][0], oacc[ct][dt][1], oacc[ct][dt][2], oacc[ct][dt][3]);
+      }
+      if (lg == 0) {
+        float* ml = a.part + (size_t)splits * nrows_all * D + pr * 2;
+        ml[0] = m[ct];
+        ml[1] = lsum[ct];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+template <int KIND, int D>
+hipError_t launch_attn_fwd(const AttnArgs& a, const AttnPlan& p, int qtiles, hipStream_t s) {
+  const int grid = a.B * a.Hkv * qtiles * p.splits;
+  if (p.qt == 128) attn_fwd<KIND, 4, D><<<grid, 256, 0, s>>>(a, qtiles, p.splits, p.kps);
+  else if (p.qt == 64) attn_fwd<KIND, 2, D><<<grid, 256, 0, s>>>(a, qtiles, p.splits, p.kps);
+  else attn_fwd<KIND, 1, D><<<grid, 256, 0, s>>>(a, qtiles, p.splits, p.kps);
+  return hipGetLastError();
+}
+
+template hipError_t launch_attn_fwd<kCacheBF16, 128>(const AttnArgs&, const AttnPlan&, int, hipStream_t);
+template hipError_t launch_attn_fwd<kCacheBF16, 64>(const AttnArgs&, const AttnPlan&, int, hipStream_t);
+template hipError_t launch_attn_fwd<kCacheFP8, 128>(const AttnArgs&, const AttnPlan&, int, hipStream_t);
+template hipError_t launch_attn_fwd<kCacheFP8, 64>(const AttnArgs&, const AttnPlan&, int, hipStream_t);
+
+}  // namespace dllm

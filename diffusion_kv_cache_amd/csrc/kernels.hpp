@@ -62,6 +62,9 @@ struct AttnPlan {
 AttnPlan plan_attention(int B, int n, int Hq, int Hkv, int S, int D, int act, int kind);
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+// Forward pass of the MFMA attention (bf16 queries; bf16 or FP8 cache), one launch.
+template <int KIND, int D>
+hipError_t launch_attn_fwd(const AttnArgs& a, const AttnPlan& p, int qtiles, hipStream_t s);
 
 struct DriftArgs {
   const void* kc;
