@@ -55,18 +55,45 @@ __global__ __launch_bounds__(64) void attn_merge(AttnArgs a, int splits) {
   if (threadIdx.x == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = (mm + log2f(L)) * kLn2;
 }
 
+// Largest packed-row count (n * G) whose log-sum-exp the fused merge + mass kernel stages in
+// LDS (32 KB); larger problems merge in attn_merge first.
+constexpr int kFusedMergeRows = 8192;
+
+// Merged state of packed row pr0 from the split partials, in split order (the same arithmetic
+// as attn_merge): running max mm and normaliser L.
+__device__ __forceinline__ void merged_ml(const float* ml, size_t nrows_all, size_t pr0, int splits,
+                                          float& mm, float& L) {
+  mm = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp) mm = fmaxf(mm, ml[((size_t)sp * nrows_all + pr0) * 2]);
+  L = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const size_t pr = (size_t)sp * nrows_all + pr0;
+    const float ms = ml[pr * 2], ls = ml[pr * 2 + 1];
+    L += ls * ((ms == -INFINITY) ? 0.f : exp2f(ms - mm));
+  }
+}
+
 // Column attention mass, second pass after the log-sum-exp is known:
 //   mass[b, h, j] = sum_i exp(<q_i, k_j> * scale - lse_i).
-// One workgroup per (b, h) and 128 keys; each wave keeps 32 keys' K rows as MFMA operands,
-// streams the n queries of head h, and each lane sums its own query's share; the 16 lanes of
-// a key are added at the end in a fixed butterfly order.
-template <int KIND, int D>
-__global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a) {
+// One workgroup per (b, KV head g) and 128 keys, so each K row is read once for all G query
+// heads of its group: each wave keeps 32 keys' K rows as MFMA A operands (S^T = K Q^T), then
+// for each query head streams its n queries in tiles of 16 (the next tile's loads in flight
+// during the current one's MFMAs and exponentials).  Lane (l16, lg) sums query column l16 over
+// the tiles in order; the 16 lanes of a key are added at the end in a fixed butterfly order.
+//
+// MERGE (the attention was split over keys): the kernel first forms every packed row's
+// log-sum-exp from the split partials (staged in LDS), the workgroups of key chunk 0 write
+// it, and the rows' outputs are merged here too (rows dealt round-robin over the key chunks),
+// so no separate merge launch is needed.
+template <int KIND, int D, bool MERGE>
+__global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
+  extern __shared__ float lse2_s[];              // MERGE: [n * G] log2-domain LSE
   constexpr int DS = D / 32;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.y, b = bh / a.Hq, h = bh % a.Hq;
-  const int g = h / (a.Hq / a.Hkv);
+  const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int rows = a.n * G;
   const int key0 = blockIdx.x * 128 + wave * 32;
   const size_t head_base = ((size_t)b * a.Hkv + g) * a.S;
   constexpr int ELT = (KIND == kCacheFP8) ? 1 : 2;
@@ -98,41 +125,101 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a) {
     }
   }
 
-  const float c = a.scale * kLog2e;
-  float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  const bf16_t* q = (const bf16_t*)a.q;
-  for (int i0 = 0; i0 < a.n; i0 += 16) {
-    const int i = i0 + l16;
-    const bool ok = i < a.n;
-    const bf16_t* src = q + (((size_t)b * a.n + (ok ? i : 0)) * a.Hq + h) * D + lg * 8;
-    bf16x8 qf[DS];
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const u32x4 x = *(const u32x4*)(src + ds * 32);
-      qf[ds] = as_bf16x8(ok ? x : u32x4{0u, 0u, 0u, 0u});
+  const size_t nrows_all = (size_t)a.B * a.Hkv * rows;
+  const float* ml = a.part + (size_t)splits * nrows_all * D;
+  if constexpr (MERGE) {
+    for (int r = t; r < rows; r += 256) {
+      float mm, L;
+      merged_ml(ml, nrows_all, (size_t)bg * rows + r, splits, mm, L);
+      const float l2 = mm + log2f(L);
+      lse2_s[r] = l2;
+      if (blockIdx.x == 0) {
+        const int i = r / G, h = g * G + r % G;
+        a.lse[((size_t)b * a.Hq + h) * a.n + i] = l2 * kLn2;
+      }
     }
-    const float lse2 = ok ? a.lse[((size_t)b * a.Hq + h) * a.n + i] * kLog2e : 0.f;
+    __syncthreads();
+  }
+
+  const float c = a.scale * kLog2e;
+  const bf16_t* q = (const bf16_t*)a.q;
+  const int ntq = (a.n + 15) / 16;
+  const int iters = G * ntq;
+  // Q^T fragments of tile `it` = (query head g*G + it / ntq, queries 16 (it % ntq) ...).
+  // Rows past n read row 0 (finite data) and are masked out of the sums.
+  // Without MERGE the row's log-sum-exp comes from global memory and is fetched with Q.
+  auto load_q = [&](int it, u32x4 (&qf)[DS], float& l) {
+    const int hh = it / ntq, i = (it % ntq) * 16 + l16;
+    const int ic = i < a.n ? i : 0;
+    const bf16_t* src = q + (((size_t)b * a.n + ic) * a.Hq + g * G + hh) * D + lg * 8;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[ds] = *(const u32x4*)(src + ds * 32);
+    if constexpr (!MERGE) l = a.lse[((size_t)b * a.Hq + g * G + hh) * a.n + ic];
+  };
+  u32x4 qcur[DS], qnext[DS];
+  float lcur = 0.f, lnext = 0.f;
+  if (iters > 0) load_q(0, qcur, lcur);
+  float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int it = 0; it < iters; ++it) {
+    if (it + 1 < iters) load_q(it + 1, qnext, lnext);
+    const int hh = it / ntq, i = (it % ntq) * 16 + l16;
+    const bool ok = i < a.n;
+    float lse2;
+    if constexpr (MERGE) lse2 = ok ? lse2_s[i * G + hh] : 0.f;
+    else lse2 = ok ? lcur * kLog2e : 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      f32x4 sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) s = mfma_bf16(kf[kt][ds], qf[ds], s);
+      for (int ds = 0; ds < DS; ++ds) sv = mfma_bf16(kf[kt][ds], as_bf16x8(qcur[ds]), sv);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[kt][v] += ok ? exp2f(s[v] * ksc[kt][v] * c - lse2) : 0.f;
+      for (int v = 0; v < 4; ++v) acc[kt][v] += ok ? exp2f(sv[v] * ksc[kt][v] * c - lse2) : 0.f;
+    }
+    if ((it + 1) % ntq == 0) {                   // last tile of this head: reduce and store
+      const int h = g * G + hh;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = acc[kt][v];
+          x += __shfl_xor(x, 1, kWave);
+          x += __shfl_xor(x, 2, kWave);
+          x += __shfl_xor(x, 4, kWave);
+          x += __shfl_xor(x, 8, kWave);
+          const int key = key0 + kt * 16 + lg * 4 + v;
+          if (l16 == 0 && key < a.S) a.mass[((size_t)b * a.Hq + h) * a.S + key] = x;
+          acc[kt][v] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qcur[ds] = qnext[ds];
+    lcur = lnext;
+  }
+
+  if constexpr (MERGE) {
+    // outputs of the rows r = blockIdx.x + gridDim.x * (4 it + wave), one wave per row
+    constexpr int PER = D / 64;
+    for (int r = blockIdx.x + gridDim.x * wave; r < rows; r += 4 * gridDim.x) {
+      const size_t pr0 = (size_t)bg * rows + r;
+      float mm, L;
+      merged_ml(ml, nrows_all, pr0, splits, mm, L);
+      float o[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] = 0.f;
+      for (int sp = 0; sp < splits; ++sp) {
+        const size_t pr = (size_t)sp * nrows_all + pr0;
+        const float ms = ml[pr * 2];
+        const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - mm);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] += a.part[pr * D + lane + 64 * e] * wgt;
+      }
+      const int i = r / G, h = g * G + r % G;
+      bf16_t* out = (bf16_t*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) out[lane + 64 * e] = f32_to_bf16(o[e] * inv);
     }
   }
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float x = acc[kt][v];
-      x += __shfl_xor(x, 1, kWave);
-      x += __shfl_xor(x, 2, kWave);
-      x += __shfl_xor(x, 4, kWave);
-      x += __shfl_xor(x, 8, kWave);
-      const int key = key0 + kt * 16 + lg * 4 + v;
-      if (l16 == 0 && key < a.S) a.mass[((size_t)b * a.Hq + h) * a.S + key] = x;
-    }
 }
 
 // ---------------------------------------------------------------- fp32 (small shapes) ---
@@ -195,14 +282,18 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   const int qtiles = (rows + p.qt - 1) / p.qt;
   hipError_t e = launch_attn_fwd<KIND, D>(a, p, qtiles, s);
   if (e != hipSuccess) return e;
-  if (p.splits > 1) {
+  const bool fuse = a.mass && p.splits > 1 && rows <= kFusedMergeRows;
+  if (p.splits > 1 && !fuse) {
     attn_merge<bf16_t, D><<<a.B * a.Hkv * rows, 64, 0, s>>>(a, p.splits);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.mass) {
-    dim3 grid2((a.S + 127) / 128, a.B * a.Hq);
-    attn_mass_mfma<KIND, D><<<grid2, 256, 0, s>>>(a);
+    dim3 grid2((a.S + 127) / 128, a.B * a.Hkv);
+    if (fuse)
+      attn_mass_mfma<KIND, D, true><<<grid2, 256, (size_t)rows * sizeof(float), s>>>(a, p.splits);
+    else
+      attn_mass_mfma<KIND, D, false><<<grid2, 256, 0, s>>>(a, p.splits);
     e = hipGetLastError();
   }
   return e;

@@ -40,17 +40,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // Per-row chunk swizzles (chunk index XOR f(row)).  K: the 16 rows one MFMA operand read
 // touches hit 16 (D = 128) or 8 (D = 64) distinct chunk slots.  V: the four rows of one
 // transposing read hit distinct 32-byte slot pairs.
-// Workgroup barrier for the DMA ring: LDS reads of this wave are complete (lgkmcnt 0) and
-// the DMA blocks it must wait for were waited on explicitly beforehand (vmcnt), so the
-// barrier itself need not drain the prefetch still in flight, which the release fence of
-// __syncthreads would.  The empty asm keeps the compiler from moving memory accesses across.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
   return D == 128 ? ((r & 3) | (((r >> 3) & 3) << 2)) : ((r & 3) | (((r >> 3) & 1) << 2));
@@ -75,19 +64,6 @@ struct Cfg {
   static constexpr int DMA_W = DMA_T / QW;       // ... per wave
   static constexpr int MERGE = (KW - 1) * QW * (DT * 4 * 64 + 2 * 64) * 4;  // one column tile
 };
-
-// One LDS-DMA instruction: lane l copies 16 bytes from its global address g to
-// lds_block + 16 l (lds_block is wave-uniform).  Issued from inline asm so that the
-// compiler's wait insertion, which cannot tell the two ring stages apart, does not drain the
-// prefetch before every LDS read; the ring waits on the vector-memory counter itself.
-__device__ __forceinline__ void dma_16B(const char* g, const char* lds_block) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_block);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(base)
-               : "memory");
-}
 
 // bf16: this wave's share of the DMA blocks of one tile (K and V) into stage memory `st`.
 template <int KIND, int QW, int D>
@@ -288,11 +264,10 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     const bool ok = r < rows;
     const int i = ok ? r / G : 0, hh = ok ? r % G : 0;
     const bf16_t* src = q + (((size_t)b * a.n + i) * a.Hq + g * G + hh) * D + lg * 8;
+    // Rows past the end read row 0 (finite data): their score columns are never stored, and
+    // not selecting here keeps these loads in flight together with the first tile's.
 #pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) {
-      const u32x4 x = *(const u32x4*)(src + ds * 32);
-      qf[ct][ds] = ok ? x : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int ds = 0; ds < C::DS; ++ds) qf[ct][ds] = *(const u32x4*)(src + ds * 32);
   }
 
   const int kbeg = split * kps;
@@ -326,8 +301,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     }
   } else {
     constexpr int PEND = 2 * C::DMA_W;           // DMA ops of one tile per wave
-    constexpr int WAIT_PREV = (PEND & 15) | (7 << 4) | (15 << 8) | ((PEND >> 4) << 14);
-    constexpr int WAIT_ALL = (7 << 4) | (15 << 8);
+
     dma_tile<KIND, QW, D>(st0, kc, vc, head_base, kbeg + kw * kKeys, kbeg, kend, qw, lane);
     for (int it = 0; it < iters; it += 2) {
       // even iteration: compute stage 0 while stage 1 fills
@@ -335,13 +309,13 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
         const int tile = it * KW + kw;
         if (it + 1 < iters) {
           dma_tile<KIND, QW, D>(st1, kc, vc, head_base, kbeg + (tile + KW) * kKeys, kbeg, kend, qw, lane);
-          __builtin_amdgcn_s_waitcnt(WAIT_PREV);
+          DLLM_WAIT_VMCNT(PEND);
         } else {
-          __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+          DLLM_WAIT_VMCNT(0);
         }
-        ring_barrier();
+        lds_barrier();
         if (tile < ntiles) tile_compute<KIND, QW, D>(st0, qf, oacc, m, lsum, kbeg + tile * kKeys, kend, c, l16, lg);
-        ring_barrier();
+        lds_barrier();
       }
       if (it + 1 >= iters) break;
       // odd iteration: compute stage 1 while stage 0 fills
@@ -349,13 +323,13 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
         const int tile = (it + 1) * KW + kw;
         if (it + 2 < iters) {
           dma_tile<KIND, QW, D>(st0, kc, vc, head_base, kbeg + (tile + KW) * kKeys, kbeg, kend, qw, lane);
-          __builtin_amdgcn_s_waitcnt(WAIT_PREV);
+          DLLM_WAIT_VMCNT(PEND);
         } else {
-          __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+          DLLM_WAIT_VMCNT(0);
         }
-        ring_barrier();
+        lds_barrier();
         if (tile < ntiles) tile_compute<KIND, QW, D>(st1, qf, oacc, m, lsum, kbeg + tile * kKeys, kend, c, l16, lg);
-        ring_barrier();
+        lds_barrier();
       }
     }
   }

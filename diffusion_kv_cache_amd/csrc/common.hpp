@@ -89,6 +89,38 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+// ------------------------------------------------------------------ LDS staging -------
+
+// Workgroup barrier for data exchanged through LDS only: this wave's LDS operations are
+// complete (lgkmcnt 0), but vector-memory loads still in flight stay in flight (the release
+// fence of __syncthreads would wait for them too).  Callers wait for LDS-DMA transfers
+// explicitly.  The empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory count set (N outstanding allowed, 0..63).
+#define DLLM_WAIT_VMCNT(N) \
+  __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
+
+// One LDS-DMA instruction: lane l copies 16 bytes from its global address g to
+// lds_block + 16 l (lds_block is the same for the whole wave).  Issued from inline asm so
+// that the compiler's wait insertion, which cannot tell apart LDS regions written this way,
+// does not drain every transfer in flight before each LDS read; callers wait on the
+// vector-memory counter themselves (DLLM_WAIT_VMCNT) before a barrier.  M0 is written here
+// and nowhere else in the kernels that use it.
+__device__ __forceinline__ void dma_16B(const void* g, const void* lds_block) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_block);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(base)
+               : "memory");
+}
+
 // ------------------------------------------------------------------------ reductions ----
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

@@ -27,9 +27,8 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-// Block-wide exclusive scan of one count per thread (256 threads); returns this thread's
-// exclusive prefix and writes the block total to *total.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+// Block-wide exclusive scan of one value per thread (256 threads), through LDS only.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t inc = v;
 #pragma unroll
@@ -37,12 +36,10 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
     const uint32_t o = __shfl_up(inc, off, kWave);
     if (lane >= off) inc += o;
   }
-  __syncthreads();
   if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
+  lds_barrier();
   uint32_t base = inc - v;
   for (int q = 0; q < wave; ++q) base += wsum[q];
-  *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
   return base;
 }
 
@@ -52,30 +49,38 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Elements of type E in one 16-byte chunk, read as fp64.
+// Elements of type E in one 16-byte chunk (held in registers), as fp64.
 template <typename E>
-__device__ __forceinline__ void load_chunk_f64(const E* p, double* out) {
+__device__ __forceinline__ void chunk_f64(const u32x4& w, double* out) {
   if constexpr (sizeof(E) == 2) {
-    const uint4 w = *(const uint4*)p;
-    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      out[2 * e] = (double)__uint_as_float(x[e] << 16);
-      out[2 * e + 1] = (double)__uint_as_float(x[e] & 0xffff0000u);
+      out[2 * e] = (double)__uint_as_float(w[e] << 16);
+      out[2 * e + 1] = (double)__uint_as_float(w[e] & 0xffff0000u);
     }
   } else {
-    const float4 w = *(const float4*)p;
-    out[0] = w.x; out[1] = w.y; out[2] = w.z; out[3] = w.w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = (double)__uint_as_float(w[e]);
   }
 }
 
+// Mass values per thread loaded ahead of everything else (four 16-byte loads): S <= 4096
+// needs one round, longer rows take further rounds after it.
+constexpr int kMassAhead = 4;
+
 // One workgroup per (b, h): the drift of the previous tracked set, then (do_update) the new
-// top-k set and the tracking-buffer refill.  All reads of the old set happen before the
-// barrier that precedes the first write.
-template <typename E>
+// top-k set and the tracking-buffer refill.  The old set and the buffer are read before any
+// write.  Global loads that do not depend on each other are issued together (old positions,
+// buffer rows, this step's mass), the cache rows of the cosine stay in flight while the
+// top-k runs on LDS, and the refill costs one more round trip.
+// CH: 16-byte chunks of the tracked K||V rows per thread (k * 2 * D / elements per chunk /
+// 256, rounded up to a power of two).  Chunk indices past the end are clamped to the last
+// chunk, so every load is issued unconditionally, back to back.
+template <typename E, int CH>
 __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   extern __shared__ uint32_t keys[];             // [S] order keys of this head's mass
   constexpr int EPC = 16 / (int)sizeof(E);       // elements per 16-byte chunk
+  constexpr int kMaxChunks = CH;
   const int h = blockIdx.x, b = blockIdx.y;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int G = a.Hq / a.Hkv, g = h / G;
@@ -85,24 +90,163 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   const E* kc = (const E*)a.kc;
   const E* vc = (const E*)a.vc;
   const size_t head_base = ((size_t)b * a.Hkv + g) * S;
-  const int cpr = D / EPC;                       // chunks per K (or V) row
+  const int cpr = D / EPC;                       // chunks per K (or V) row (power of 2)
+  const int cs = __builtin_ctz(cpr);
+  const int nch = k * 2 * cpr;                   // chunks of the tracked rows
 
   __shared__ double red[3][4];
   __shared__ int sflag[4];
-  __shared__ int32_t sT[64];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_digit, s_rem, wsum[4];
+  __shared__ int32_t sT[64], sTn[64];            // old and new tracked positions
+  __shared__ uint32_t hist[4][256];              // one digit histogram per radix pass
+  __shared__ uint32_t wsum[4];
+
+  // ---- loads issued together: old positions, buffer rows, the first round of mass ----
+  const int told = (t < k) ? T[t] : -1;
+  u32x4 ub[kMaxChunks];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = min(t + 256 * i, nch - 1);
+    ub[i] = *(const u32x4*)(buf + (size_t)c * EPC);
+  }
+  const float* mass = a.mass + ((size_t)b * a.Hq + h) * S;
+  const bool vec_mass = do_update && (S % 4 == 0) && (((uintptr_t)a.mass & 15) == 0);
+  float4 mr[kMassAhead];
+  if (vec_mass) {
+#pragma unroll
+    for (int u = 0; u < kMassAhead; ++u) {
+      const int q = t + 256 * u;
+      if (q < S / 4) mr[u] = ((const float4*)mass)[q];
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) hist[p][t] = 0;
+  if (t < k) sT[t] = told;
+  if (vec_mass) {
+#pragma unroll
+    for (int u = 0; u < kMassAhead; ++u) {
+      const int q = t + 256 * u;
+      if (q < S / 4) {
+        keys[4 * q] = order_key(mr[u].x);
+        keys[4 * q + 1] = order_key(mr[u].y);
+        keys[4 * q + 2] = order_key(mr[u].z);
+        keys[4 * q + 3] = order_key(mr[u].w);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- cache rows of the old set: in flight during the top-k ----
+  u32x4 uc[kMaxChunks];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = min(t + 256 * i, nch - 1);
+    const int slot = c >> (cs + 1), part = (c >> cs) & 1, d0 = (c & (cpr - 1)) * EPC;
+    const int j = sT[slot];
+    const int jc = (j >= 0 && j < S) ? j : 0;    // empty slots read row 0, unused below
+    uc[i] = *(const u32x4*)((part ? vc : kc) + (head_base + jc) * D + d0);
+  }
+
+  if (do_update) {
+    // the rest of the mass (rows longer than the first round, or not a multiple of 4)
+    if (vec_mass) {
+      for (int q = t + 256 * kMassAhead; q < S / 4; q += 256) {
+        const float4 m4 = ((const float4*)mass)[q];
+        keys[4 * q] = order_key(m4.x);
+        keys[4 * q + 1] = order_key(m4.y);
+        keys[4 * q + 2] = order_key(m4.z);
+        keys[4 * q + 3] = order_key(m4.w);
+      }
+    } else {
+      for (int j = t; j < S; j += 256) keys[j] = order_key(mass[j]);
+    }
+    lds_barrier();
+
+    // ---- top-k of this step's mass: the k-th largest key by four 8-bit radix passes ----
+    // Every wave scans the pass's histogram itself, so a pass costs one barrier.
+    const uint32_t want = (uint32_t)min(k, S);
+    uint32_t prefix = 0, pmask = 0, rem = want;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      uint32_t* hp = hist[pass];
+#pragma unroll 4
+      for (int j = t; j < S; j += 256) {
+        const uint32_t u = keys[j];
+        if ((u & pmask) == prefix) atomicAdd(&hp[(u >> shift) & 255u], 1u);
+      }
+      lds_barrier();
+      // lane L owns digits 255-4L .. 252-4L (descending); inclusive scan over lanes
+      uint32_t cnt[4], own = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cnt[e] = hp[255 - 4 * lane - e];
+        own += cnt[e];
+      }
+      uint32_t inc = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += o;
+      }
+      const uint32_t exc = inc - own;
+      // the digit holding the rem-th largest candidate, and how many of it are taken
+      uint32_t digit = 0, left = 0, above = exc;
+      bool found = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!found && above + cnt[e] >= rem) {
+          digit = 255u - 4u * lane - e;
+          left = rem - above;
+          found = true;
+        }
+        above += cnt[e];
+      }
+      const int src = __ffsll((unsigned long long)__ballot(exc < rem && rem <= inc)) - 1;
+      digit = __shfl(digit, src, kWave);
+      left = __shfl(left, src, kWave);
+      prefix |= digit << shift;
+      pmask |= 0xffu << shift;
+      rem = left;
+    }
+
+    // prefix is the k-th largest key; `rem` of the keys equal to it are taken, lowest
+    // positions first.  One scan of (greater, equal) counts over contiguous position ranges
+    // gives every taken key its slot in ascending position order.
+    const int per = (S + 255) / 256;
+    const int j0 = min(S, t * per), j1 = min(S, j0 + per);
+    uint32_t gt = 0, eq = 0;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t u = keys[j];
+      gt += (u > prefix);
+      eq += (u == prefix);
+    }
+    const uint32_t base = block_exclusive_scan(gt | (eq << 16), wsum);  // S <= 16384
+    uint32_t gb = base & 0xffffu, eb = base >> 16;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t u = keys[j];
+      if (u > prefix) {
+        const uint32_t slot = gb + min(eb, rem);
+        if (slot < (uint32_t)k) sTn[slot] = j;
+        ++gb;
+      } else if (u == prefix) {
+        if (eb < rem && gb + eb < (uint32_t)k) sTn[gb + eb] = j;
+        ++eb;
+      }
+    }
+    for (int sl = (int)want + t; sl < k; sl += 256) sTn[sl] = -1;
+  }
 
   // ---- sigma over the previous tracked set (fp64) ----
   double uw = 0.0, uu = 0.0, ww = 0.0;
   int neq = 0;
-  for (int c = t; c < k * 2 * cpr; c += 256) {
-    const int slot = c / (2 * cpr), part = (c / cpr) & 1, d0 = (c % cpr) * EPC;
-    const int j = T[slot];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = t + 256 * i;
+    if (c >= nch) continue;
+    const int j = sT[c >> (cs + 1)];
     if (j < 0 || j >= S) continue;
     double u[EPC], w[EPC];
-    load_chunk_f64<E>(buf + (size_t)c * EPC, u);
-    load_chunk_f64<E>((part ? vc : kc) + (head_base + j) * D + d0, w);
+    chunk_f64<E>(ub[i], u);
+    chunk_f64<E>(uc[i], w);
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
       uw += u[e] * w[e];
@@ -111,7 +255,7 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
       neq |= (u[e] != w[e]);
     }
   }
-  const int valid_slot = (t < k) ? (T[t] >= 0 && T[t] < S) : 0;
+  const int valid_slot = (t < k) ? (told >= 0 && told < S) : 0;
   uw = wave_sum_f64(uw);
   uu = wave_sum_f64(uu);
   ww = wave_sum_f64(ww);
@@ -123,6 +267,7 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
     sflag[wave] = wflags;
   }
   __syncthreads();
+  float sig = 1.f;                               // thread 0: this head's sigma
   if (t == 0) {
     double UW = 0.0, UU = 0.0, WW = 0.0;
     int F = 0;
@@ -141,99 +286,29 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
     // Report in fp32 on the side of gamma the fp64 value lies on.
     float f = (float)sigma;
     if (sigma < (double)a.gamma && !(f < a.gamma)) f = nextafterf(a.gamma, -INFINITY);
-    a.sigma[(size_t)b * a.Hq + h] = f;
+    sig = f;
   }
-  if (!do_update) return;
-  __syncthreads();
+  if (!do_update) {
+    if (t == 0) a.sigma[(size_t)b * a.Hq + h] = sig;
+    return;
+  }
 
-  // ---- top-k of this step's mass: k-th largest value by 8-bit radix passes ----
-  const float* mass = a.mass + ((size_t)b * a.Hq + h) * S;
-  for (int j = t; j < S; j += 256) keys[j] = order_key(mass[j]);
-  const uint32_t want = (uint32_t)min(k, S);
-  uint32_t prefix = 0, pmask = 0, rem = want;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[t] = 0;
-    __syncthreads();
-    for (int j = t; j < S; j += 256) {
-      const uint32_t u = keys[j];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // Lane L owns digits 255-4L .. 252-4L (descending); inclusive scan over lanes.
-      uint32_t cnt[4], own = 0;
+  // ---- new set out, and the tracking buffer refilled with its K||V rows ----
+  // (all loads first, then the stores, which the compiler cannot prove do not alias them)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        cnt[e] = hist[255 - 4 * lane - e];
-        own += cnt[e];
-      }
-      uint32_t inc = own;
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = min(t + 256 * i, nch - 1);
+    const int slot = c >> (cs + 1), part = (c >> cs) & 1, d0 = (c & (cpr - 1)) * EPC;
+    const int j = sTn[slot];
+    ub[i] = *(const u32x4*)((part ? vc : kc) + (head_base + (j >= 0 ? j : 0)) * D + d0);
+    if (j < 0) ub[i] = u32x4{0u, 0u, 0u, 0u};    // empty slot (S < k): zero row
+  }
+  if (t == 0) a.sigma[(size_t)b * a.Hq + h] = sig;
+  for (int sl = t; sl < k; sl += 256) T[sl] = sTn[sl];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += o;
-      }
-      const uint32_t exc = inc - own;
-      if (exc < rem && rem <= inc) {
-        uint32_t above = exc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (above + cnt[e] >= rem) {
-            s_digit = 255u - 4u * lane - e;
-            s_rem = rem - above;
-            break;
-          }
-          above += cnt[e];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    pmask |= 0xffu << shift;
-    rem = s_rem;
-  }
-  // prefix is the k-th largest value; `rem` of the values equal to it are taken, lowest
-  // positions first.  Selection in ascending position order over contiguous ranges.
-  const int per = (S + 255) / 256;
-  const int j0 = min(S, t * per), j1 = min(S, j0 + per);
-  uint32_t ties = 0;
-  for (int j = j0; j < j1; ++j) ties += (keys[j] == prefix);
-  uint32_t tot;
-  uint32_t tie_base = block_exclusive_scan(ties, wsum, &tot);
-  uint32_t sel = 0;
-  {
-    uint32_t tb = tie_base;
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t u = keys[j];
-      if (u > prefix) ++sel;
-      else if (u == prefix) sel += (tb++ < rem);
-    }
-  }
-  uint32_t pos = block_exclusive_scan(sel, wsum, &tot);
-  {
-    uint32_t tb = tie_base;
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t u = keys[j];
-      const bool take = (u > prefix) || (u == prefix && tb++ < rem);
-      if (take) {
-        if (pos < (uint32_t)k) sT[pos] = j;
-        ++pos;
-      }
-    }
-  }
-  __syncthreads();
-  for (int sl = (int)want + t; sl < k; sl += 256) sT[sl] = -1;
-  __syncthreads();
-  for (int sl = t; sl < k; sl += 256) T[sl] = sT[sl];
-
-  // ---- refill the tracking buffer with the K||V rows at the new positions ----
-  for (int c = t; c < k * 2 * cpr; c += 256) {
-    const int slot = c / (2 * cpr), part = (c / cpr) & 1, d0 = (c % cpr) * EPC;
-    const int j = sT[slot];
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (j >= 0) val = *(const uint4*)((part ? vc : kc) + (head_base + j) * D + d0);
-    *(uint4*)(buf + (size_t)c * EPC) = val;
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = t + 256 * i;
+    if (c < nch) *(u32x4*)(buf + (size_t)c * EPC) = ub[i];
   }
 }
 
@@ -264,8 +339,25 @@ hipError_t launch_drift(const DriftArgs& a, hipStream_t s) {
   dim3 grid(a.Hq, a.B);
   const int upd = a.mass != nullptr;
   const size_t lds = upd ? (size_t)a.S * sizeof(uint32_t) : 0;
-  if (a.kind == kCacheF32) drift_track<float><<<grid, 256, lds, s>>>(a, upd);
-  else drift_track<bf16_t><<<grid, 256, lds, s>>>(a, upd);
+  const int esz = a.kind == kCacheF32 ? 4 : 2;
+  const int per = (a.k * 2 * a.D * esz / 16 + 255) / 256;  // chunks per thread, <= 16
+  const int ch = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
+  if (a.kind == kCacheF32) {
+    switch (ch) {
+      case 1: drift_track<float, 1><<<grid, 256, lds, s>>>(a, upd); break;
+      case 2: drift_track<float, 2><<<grid, 256, lds, s>>>(a, upd); break;
+      case 4: drift_track<float, 4><<<grid, 256, lds, s>>>(a, upd); break;
+      case 8: drift_track<float, 8><<<grid, 256, lds, s>>>(a, upd); break;
+      default: drift_track<float, 16><<<grid, 256, lds, s>>>(a, upd); break;
+    }
+  } else {
+    switch (ch) {
+      case 1: drift_track<bf16_t, 1><<<grid, 256, lds, s>>>(a, upd); break;
+      case 2: drift_track<bf16_t, 2><<<grid, 256, lds, s>>>(a, upd); break;
+      case 4: drift_track<bf16_t, 4><<<grid, 256, lds, s>>>(a, upd); break;
+      default: drift_track<bf16_t, 8><<<grid, 256, lds, s>>>(a, upd); break;
+    }
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   drift_decide<<<a.B, 64, 0, s>>>(a);

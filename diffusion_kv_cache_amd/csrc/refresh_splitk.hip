@@ -19,7 +19,7 @@
 namespace dllm {
 namespace {
 
-constexpr int kPrefetch = 6;   // k-steps of W in flight per wave
+constexpr int kPrefetch = 8;   // k-steps of W in flight per wave
 
 // Three workgroups per CU (6 waves per SIMD) keep all 768 workgroups of a 4096-hidden,
 // 12288-column step resident at once.
@@ -28,54 +28,64 @@ void refresh_partial(RefreshArgs a, float* part) {
   extern __shared__ u32x4 As[];                  // [32 rows][cpr chunks], swizzled
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
   const int N = (a.Hq + 2 * a.Hkv) * a.D;
-  const int p = blockIdx.y;
-  const int m0 = blockIdx.z * 32;
+  const int p = blockIdx.x;                      // partitions fastest: the eight workgroups
+  const int m0 = blockIdx.z * 32;                // of a column tile are dispatched together
   const int Lp = a.H / kKSplit, kb = p * Lp;
   const int cpr = Lp / 8;                        // 16-byte chunks per staged row
   const int mask = (cpr % 8 == 0) ? 7 : 3;
 
-  const bf16_t* hid = (const bf16_t*)a.hidden;
-  for (int q = t; q < 32 * cpr; q += 512) {
-    const int r = q / cpr, c = q % cpr, m = m0 + r;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (m < a.M) {
-      const int b = m / a.n;
-      v = *(const u32x4*)(hid + ((size_t)b * a.S + a.idx[m]) * a.H + kb + c * 8);
-    }
-    As[r * cpr + (c ^ (r & mask))] = v;
+  // Prologue: the 32 row positions, then the gathered A slice global -> LDS by DMA (each
+  // lane fetches the source chunk that lands, swizzled, at its LDS slot) together with the
+  // first W steps.  Rows past M gather the last valid row: their accumulators are never
+  // stored.
+  __shared__ int s_row[32];                      // hidden row offset (b * S + pos) per A row
+  if (t < 32) {
+    const int m = min(m0 + t, a.M - 1);
+    s_row[t] = (m / a.n) * a.S + a.idx[m];
   }
-
-  const int col = blockIdx.x * 128 + wave * 16 + l16;
+  lds_barrier();
+  const bf16_t* hid = (const bf16_t*)a.hidden;
+  const int nblk = 32 * cpr / 64;                // 1 KB DMA blocks of the A slice
+  for (int blk = wave; blk < nblk; blk += 8) {
+    const int P = blk * 64 + lane;               // chunk slot in As
+    const int r = P / cpr, j = P % cpr;
+    const bf16_t* src = hid + (size_t)s_row[r] * a.H + kb + (j ^ (r & mask)) * 8;
+    dma_16B(src, As + blk * 64);
+  }
+  const int col = blockIdx.y * 128 + wave * 16 + l16;
   const bool col_ok = col < N;
   const bf16_t* wr = (const bf16_t*)a.w + (size_t)(col_ok ? col : N - 1) * a.H + kb + lg * 8;
   const int steps = Lp / 32;
   u32x4 wv[kPrefetch];
 #pragma unroll
-  for (int u = 0; u < kPrefetch; ++u)
-    if (u < steps) wv[u] = *(const u32x4*)(wr + u * 32);
+  for (int u = 0; u < kPrefetch; ++u) wv[u] = *(const u32x4*)(wr + min(u, steps - 1) * 32);
+  DLLM_WAIT_VMCNT(0);
   __syncthreads();
 
+  // A ring of kPrefetch W steps in registers: slot u holds step s0 + u; right after it is
+  // consumed it is refilled with step s0 + u + kPrefetch, so kPrefetch - 1 loads stay in
+  // flight while each step's MFMAs run.  The last round issues no loads (no branch around a
+  // load anywhere, which keeps the compiler's count of loads in flight exact).
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  for (int s0 = 0; s0 < steps; s0 += kPrefetch) {
-    u32x4 wn[kPrefetch];
+  auto step = [&](int st, const u32x4& wq) {
+    const int c = st * 4 + lg;
 #pragma unroll
-    for (int u = 0; u < kPrefetch; ++u)
-      if (s0 + kPrefetch + u < steps) wn[u] = *(const u32x4*)(wr + (s0 + kPrefetch + u) * 32);
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r = rt * 16 + l16;
+      acc[rt] = mfma_bf16(as_bf16x8(As[r * cpr + (c ^ (r & mask))]), as_bf16x8(wq), acc[rt]);
+    }
+  };
+  int s0 = 0;
+  for (; s0 + kPrefetch < steps; s0 += kPrefetch) {
 #pragma unroll
     for (int u = 0; u < kPrefetch; ++u) {
-      if (s0 + u < steps) {
-        const int c = (s0 + u) * 4 + lg;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const int r = rt * 16 + l16;
-          const bf16x8 af = as_bf16x8(As[r * cpr + (c ^ (r & mask))]);
-          acc[rt] = mfma_bf16(af, as_bf16x8(wv[u]), acc[rt]);
-        }
-      }
+      step(s0 + u, wv[u]);
+      wv[u] = *(const u32x4*)(wr + min(s0 + u + kPrefetch, steps - 1) * 32);
     }
-#pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) wv[u] = wn[u];
   }
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u)
+    if (s0 + u < steps) step(s0 + u, wv[u]);
 
   if (!col_ok) return;
 #pragma unroll
@@ -160,7 +170,7 @@ size_t splitk_workspace_bytes(int M, int N) { return (size_t)kKSplit * M * N * s
 
 hipError_t launch_refresh_splitk(const RefreshArgs& a, float* part, hipStream_t s) {
   const int N = (a.Hq + 2 * a.Hkv) * a.D;
-  dim3 grid((N + 127) / 128, kKSplit, (a.M + 31) / 32);
+  dim3 grid(kKSplit, (N + 127) / 128, (a.M + 31) / 32);
   const size_t lds = (size_t)32 * (a.H / kKSplit) * sizeof(bf16_t);
   refresh_partial<<<grid, 512, lds, s>>>(a, part);
   hipError_t e = hipGetLastError();

@@ -189,6 +189,19 @@ ATT_CASES = {
                            prompt=450, cache="fp8", block_start=450, block_len=16, seed=37),
     "f32_d64": C(batch=2, hidden=256, q_heads=4, kv_heads=2, head_dim=64, seq=77, prompt=40,
                  act="f32", cache="f32", block_start=41, block_len=9, seed=38),
+    # one case per remaining (cache dtype, packed query tile, head dim) kernel instance
+    "bf16_g4_qt64_d128": C(batch=2, hidden=256, q_heads=8, kv_heads=2, head_dim=128, seq=410,
+                           prompt=200, block_start=203, block_len=40, seed=39),
+    "bf16_g8_qt128_d64": C(batch=1, hidden=256, q_heads=8, kv_heads=1, head_dim=64, seq=333,
+                           prompt=160, block_start=161, block_len=70, seed=40),
+    "fp8_g1_qt32": C(batch=2, hidden=512, q_heads=4, kv_heads=4, head_dim=128, seq=611,
+                     prompt=300, cache="fp8", block_start=301, block_len=20, seed=41),
+    "fp8_g8_qt128": C(batch=1, hidden=256, q_heads=8, kv_heads=1, head_dim=128, seq=290,
+                      prompt=150, cache="fp8", block_start=150, block_len=64, seed=42),
+    "fp8_d64_g4_qt64": C(batch=2, hidden=256, q_heads=8, kv_heads=2, head_dim=64, seq=520,
+                         prompt=260, cache="fp8", block_start=263, block_len=20, seed=43),
+    "fp8_d64_g8_qt128": C(batch=1, hidden=256, q_heads=8, kv_heads=1, head_dim=64, seq=300,
+                          prompt=150, cache="fp8", block_start=151, block_len=70, seed=44),
 }
 
 
