@@ -42,6 +42,105 @@ __device__ __forceinline__ size_t out_row_offset(const RefreshArgs& a, int m, in
   return (((size_t)b * a.Hkv + g) * a.S + pos) * (size_t)a.D;
 }
 
+// Epilogue of a finished (TM rows) x (one head) tile held as per-wave accumulators tot:
+// rotary embedding of Q and K heads in registers, the fp32 tile staged in LDS (smem, at least
+// TM * (D + 4) floats, free when called), then whole rows out: bf16 / fp32 rows, or per-row
+// FP8 codes with their scale.
+// WM waves along the rows (2 * WM waves, 128 * WM threads); wave w owns rows
+// (w / 2) * TM / WM + [0, TM / WM).
+template <typename T, int KIND, int TM, int D, int WM>
+__device__ __forceinline__ void tile_epilogue(const RefreshArgs& a,
+                                              f32x4 (&tot)[TM / (16 * WM)][D / 32], char* smem,
+                                              int j, int m0, const int (&colv)[D / 32]) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int RT = TM / (16 * WM), CT = D / 32, CH = CT / 2;
+  constexpr int NT = 128 * WM;
+  constexpr int EPI_STRIDE = D + 4;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  // Rotary embedding of Q and K heads, in registers.
+  if (j < a.Hq + a.Hkv) {
+    float hi[CH], lo[CH];
+#pragma unroll
+    for (int sb = 0; sb < CH; ++sb) rope_turns(wn * (D / 4) + sb * 16 + l16, D, a.rope_base, hi[sb], lo[sb]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + wm * (TM / WM) + rt * 16 + lg * 4 + v;
+        const int pos = (m < a.M) ? a.idx[m] : 0;
+#pragma unroll
+        for (int sb = 0; sb < CH; ++sb) {
+          float s, c;
+          rope_sincos(pos, hi[sb], lo[sb], s, c);
+          float x = tot[rt][sb][v], y = tot[rt][CH + sb][v];
+          rope_rotate(x, y, s, c);
+          tot[rt][sb][v] = x;
+          tot[rt][CH + sb][v] = y;
+        }
+      }
+  }
+
+  // Stage the fp32 tile in LDS (the loop's last barrier already retired the stage buffers).
+  float* tile = (float*)smem;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        tile[(wm * (TM / WM) + rt * 16 + lg * 4 + v) * EPI_STRIDE + colv[ct]] = tot[rt][ct][v];
+  __syncthreads();
+
+  // Whole rows out: D/8 threads per row, eight values each.
+  constexpr int TPR = D / 8;
+  const int cpos = (t % TPR) * 8;
+  for (int r = t / TPR; r < TM; r += NT / TPR) {
+    const int m = m0 + r;
+    if (m >= a.M) continue;  // uniform over the TPR threads of a row
+    float x[8];
+    const float4 x0 = *(const float4*)(tile + r * EPI_STRIDE + cpos);
+    const float4 x1 = *(const float4*)(tile + r * EPI_STRIDE + cpos + 4);
+    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    int which;
+    const size_t off = out_row_offset(a, m, j, which);
+    if (which == 0 || KIND != kCacheFP8) {
+      void* base = which == 0 ? a.q_out : which == 1 ? a.kc : a.vc;
+      if constexpr (BF) {
+        u32x4 o;
+        o.x = pack_bf16x2(x[0], x[1]);
+        o.y = pack_bf16x2(x[2], x[3]);
+        o.z = pack_bf16x2(x[4], x[5]);
+        o.w = pack_bf16x2(x[6], x[7]);
+        *(u32x4*)((bf16_t*)base + off + cpos) = o;
+      } else {
+        float* dst = (float*)base + off + cpos;
+        *(float4*)dst = x0;
+        *(float4*)(dst + 4) = x1;
+      }
+    } else {
+      // Per-row FP8: amax over the row (TPR consecutive lanes), scale = amax / 448.
+      float am = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
+#pragma unroll
+      for (int msk = 1; msk < TPR; msk <<= 1) am = fmaxf(am, __shfl_xor(am, msk, kWave));
+      const float scale = (am == 0.f) ? 1.f : am / 448.f;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo |= e4m3_encode(x[e] / scale) << (8 * e);
+        hi |= e4m3_encode(x[4 + e] / scale) << (8 * e);
+      }
+      uint8_t* dst = (uint8_t*)(which == 1 ? a.kc : a.vc) + off + cpos;
+      *(uint2*)dst = make_uint2(lo, hi);
+      if ((t % TPR) == 0) (which == 1 ? a.ks : a.vs)[off / D] = scale;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Tiled kernel: one workgroup per (TM rows) x (one head = D columns), four waves as 2 (rows)
 // x 2 (rotary-pair column groups).  A (gathered hidden rows) and W tiles go through LDS,
@@ -196,86 +295,127 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
     __syncthreads();
   }
 
-  // Rotary embedding of Q and K heads, in registers.
-  if (j < a.Hq + a.Hkv) {
-    float hi[CH], lo[CH];
-#pragma unroll
-    for (int sb = 0; sb < CH; ++sb) rope_turns(wn * (D / 4) + sb * 16 + l16, D, a.rope_base, hi[sb], lo[sb]);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * (TM / 2) + rt * 16 + lg * 4 + v;
-        const int pos = (m < a.M) ? a.idx[m] : 0;
-#pragma unroll
-        for (int sb = 0; sb < CH; ++sb) {
-          float s, c;
-          rope_sincos(pos, hi[sb], lo[sb], s, c);
-          float x = tot[rt][sb][v], y = tot[rt][CH + sb][v];
-          rope_rotate(x, y, s, c);
-          tot[rt][sb][v] = x;
-          tot[rt][CH + sb][v] = y;
-        }
-      }
-  }
+  tile_epilogue<T, KIND, TM, D, 2>(a, tot, smem, j, m0, colv);
+}
 
-  // Stage the fp32 tile in LDS (the loop's last barrier already retired the stage buffers).
-  float* tile = (float*)smem;
+// ------------------------------------------------------------------------------------------
+// Pipelined bf16 kernel (large M): the same tile, partitioning and epilogue as refresh_tiled,
+// with the A (gathered rows) and W tiles moved global -> LDS by DMA through an NST-stage
+// ring, so NST - 1 stages are in flight while one is multiplied.  Each lane fetches the
+// source chunk that lands, swizzled (chunk c of row r at slot c ^ (r % BKC)), at its LDS
+// slot.  A barrier per stage; each wave waits only for its own transfers of the stage it is
+// about to read.
+// ------------------------------------------------------------------------------------------
+template <int KIND, int TM, int D, int BKC, int NST, int WM>
+__global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
+  constexpr int NW = 2 * WM;                 // waves: WM along the rows x 2 column groups
+  constexpr int EPC = 8;                     // bf16 per 16-byte chunk
+  constexpr int BK = BKC * EPC;              // k per stage
+  constexpr int RT = TM / (16 * WM), CT = D / 32, CH = CT / 2;
+  constexpr int RPI = 64 / BKC;              // rows (or columns) per DMA instruction
+  constexpr int IA = TM / RPI, IW = D / RPI; // DMA instructions per stage for A and W
+  constexpr int NI = (IA + IW) / NW;         // per wave
+  static_assert((IA + IW) % NW == 0, "DMA instructions must split evenly over the waves");
+  constexpr int A_BYTES = TM * BKC * 16;
+  constexpr int STAGE = (TM + D) * BKC * 16;
+  constexpr int EPI = TM * (D + 4) * 4;
+  constexpr int SMEM = (NST * STAGE > EPI) ? NST * STAGE : EPI;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int j = blockIdx.x;
+  const int m0 = blockIdx.y * TM;
+
+  // Source of this lane's chunk for each of the wave's NI DMA instructions (k = 0).
+  const bf16_t* src[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int gi = wave * NI + i;
+    const int cp = lane % BKC;
+    if (gi < IA) {
+      const int r = gi * RPI + lane / BKC;
+      const int m = min(m0 + r, a.M - 1);        // rows past M: never stored
+      src[i] = (const bf16_t*)a.hidden + hidden_row_offset(a, m) + (cp ^ (r & (BKC - 1))) * EPC;
+    } else {
+      const int c = (gi - IA) * RPI + lane / BKC;
+      src[i] = (const bf16_t*)a.w + (size_t)(j * D + c) * a.H + (cp ^ (c & (BKC - 1))) * EPC;
+    }
+  }
+  auto issue = [&](int stage, int slot) {
+    char* base = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma_16B(src[i] + stage * BK, base + (wave * NI + i) * 1024);
+  };
+
+  int colv[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+    colv[ct] = (ct / CH) * (D / 2) + wn * (D / 4) + (ct % CH) * 16 + l16;
+
+  f32x4 acc[RT][CT], tot[RT][CT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        tile[(wm * (TM / 2) + rt * 16 + lg * 4 + v) * EPI_STRIDE + colv[ct]] = tot[rt][ct][v];
-  __syncthreads();
+    for (int ct = 0; ct < CT; ++ct) {
+      acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tot[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-  // Whole rows out: D/8 threads per row, eight values each.
-  constexpr int TPR = D / 8;
-  const int cpos = (t % TPR) * 8;
-  for (int r = t / TPR; r < TM; r += 256 / TPR) {
-    const int m = m0 + r;
-    if (m >= a.M) continue;  // uniform over the TPR threads of a row
-    float x[8];
-    const float4 x0 = *(const float4*)(tile + r * EPI_STRIDE + cpos);
-    const float4 x1 = *(const float4*)(tile + r * EPI_STRIDE + cpos + 4);
-    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-    int which;
-    const size_t off = out_row_offset(a, m, j, which);
-    if (which == 0 || KIND != kCacheFP8) {
-      void* base = which == 0 ? a.q_out : which == 1 ? a.kc : a.vc;
-      if constexpr (BF) {
-        u32x4 o;
-        o.x = pack_bf16x2(x[0], x[1]);
-        o.y = pack_bf16x2(x[2], x[3]);
-        o.z = pack_bf16x2(x[4], x[5]);
-        o.w = pack_bf16x2(x[6], x[7]);
-        *(u32x4*)((bf16_t*)base + off + cpos) = o;
-      } else {
-        float* dst = (float*)base + off + cpos;
-        *(float4*)dst = x0;
-        *(float4*)(dst + 4) = x1;
+  const int stages = a.H / BK;
+  const int per_part = stages / kKSplit;
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st)
+    if (st < stages) issue(st, st);
+  for (int s = 0; s < stages; ++s) {
+    // this wave's transfers for stage s are done once at most those of the later stages
+    // already issued (min(NST - 2, stages - 1 - s) of them) are outstanding
+    if (s + NST - 2 < stages) DLLM_WAIT_VMCNT(NI * (NST - 2));
+    else DLLM_WAIT_VMCNT(0);
+    lds_barrier();
+    if (s + NST - 1 < stages) issue(s + NST - 1, (s + NST - 1) % NST);
+    const char* A = smem + (s % NST) * STAGE;
+    const char* W = A + A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < BKC / 4; ++ks) {
+      const int c = ks * 4 + lg;
+      bf16x8 af[RT], bfr[CT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int r = wm * (TM / WM) + rt * 16 + l16;
+        af[rt] = as_bf16x8(*(const u32x4*)(A + (r * BKC + (c ^ (r & (BKC - 1)))) * 16));
       }
-    } else {
-      // Per-row FP8: amax over the row (TPR consecutive lanes), scale = amax / 448.
-      float am = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
-#pragma unroll
-      for (int msk = 1; msk < TPR; msk <<= 1) am = fmaxf(am, __shfl_xor(am, msk, kWave));
-      const float scale = (am == 0.f) ? 1.f : am / 448.f;
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo |= e4m3_encode(x[e] / scale) << (8 * e);
-        hi |= e4m3_encode(x[4 + e] / scale) << (8 * e);
+      for (int ct = 0; ct < CT; ++ct) {
+        const int col = colv[ct];
+        bfr[ct] = as_bf16x8(*(const u32x4*)(W + (col * BKC + (c ^ (col & (BKC - 1)))) * 16));
       }
-      uint8_t* dst = (uint8_t*)(which == 1 ? a.kc : a.vc) + off + cpos;
-      *(uint2*)dst = make_uint2(lo, hi);
-      if ((t % TPR) == 0) (which == 1 ? a.ks : a.vs)[off / D] = scale;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mfma_bf16(af[rt], bfr[ct], acc[rt][ct]);
+    }
+    if ((s + 1) % per_part == 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          tot[rt][ct] = tot[rt][ct] + acc[rt][ct];
+          acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
   }
+  lds_barrier();  // every wave is done reading the ring before the epilogue reuses it
+  tile_epilogue<bf16_t, KIND, TM, D, WM>(a, tot, smem, j, m0, colv);
+}
+
+template <int KIND, int TM, int D, int BKC, int NST, int WM>
+hipError_t launch_gemm(const RefreshArgs& a, hipStream_t s) {
+  const int heads = a.Hq + 2 * a.Hkv;
+  dim3 grid(heads, (a.M + TM - 1) / TM);
+  refresh_gemm<KIND, TM, D, BKC, NST, WM><<<grid, 128 * WM, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T, int KIND, int D, int BKC>
@@ -301,11 +441,18 @@ hipError_t launch_tiled_bk(const RefreshArgs& a, int tm, hipStream_t s) {
 
 template <int D>
 hipError_t launch_d(const RefreshArgs& a, hipStream_t s) {
-  const int heads = a.Hq + 2 * a.Hkv;
   if (a.act == DLLM_F32) return launch_tiled_bk<float, kCacheF32, D>(a, 64, s);
-  const int tm = ((a.M + 127) / 128) * heads >= 512 ? 128 : 64;
-  if (a.kind == kCacheFP8) return launch_tiled_bk<bf16_t, kCacheFP8, D>(a, tm, s);
-  return launch_tiled_bk<bf16_t, kCacheBF16, D>(a, tm, s);
+  // 128 rows x one head per workgroup, eight waves of 32 rows x half the head's column pairs.
+  // Small M streams W at the HBM rate and wants a third stage in flight; large M wants the
+  // occupancy of two stages.
+  const bool bk8 = (a.H / kKSplit) % 64 == 0;
+  const bool deep = a.M <= 512;
+  if (a.kind == kCacheFP8) {
+    if (!bk8) return launch_gemm<kCacheFP8, 128, D, 4, 2, (D == 64 ? 2 : 4)>(a, s);
+    return deep ? launch_gemm<kCacheFP8, 128, D, 8, 3, 4>(a, s) : launch_gemm<kCacheFP8, 128, D, 8, 2, 4>(a, s);
+  }
+  if (!bk8) return launch_gemm<kCacheBF16, 128, D, 4, 2, (D == 64 ? 2 : 4)>(a, s);
+  return deep ? launch_gemm<kCacheBF16, 128, D, 8, 3, 4>(a, s) : launch_gemm<kCacheBF16, 128, D, 8, 2, 4>(a, s);
 }
 
 }  // namespace
