@@ -21,6 +21,10 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# Per-source additions.  The attention forward pass keeps its MFMA accumulators in ordinary
+# VGPRs: with accumulation registers the compiler copied all 64 output accumulators out and
+# back on every key tile (the lazily rescaled softmax state is loop-carried through a branch).
+EXTRA = {"attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -30,7 +34,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = ["hipcc", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ["hipcc", *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

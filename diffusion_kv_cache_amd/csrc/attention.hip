@@ -91,10 +91,15 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
   constexpr int DS = D / 32;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
+  // All key chunks of one (b, KV head) run on one XCD: the group's queries are fetched into
+  // that L2 once.
+  const int nkc = (a.S + 127) / 128;
+  int bg, kchunk;
+  xcd_group_unit(blockIdx.x, a.B * a.Hkv, nkc, bg, kchunk);
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int rows = a.n * G;
-  const int key0 = blockIdx.x * 128 + wave * 32;
+  const int key0 = kchunk * 128 + wave * 32;
   const size_t head_base = ((size_t)b * a.Hkv + g) * a.S;
   constexpr int ELT = (KIND == kCacheFP8) ? 1 : 2;
   const char* kc = (const char*)a.kc;
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
       merged_ml(ml, nrows_all, (size_t)bg * rows + r, splits, mm, L);
       const float l2 = mm + log2f(L);
       lse2_s[r] = l2;
-      if (blockIdx.x == 0) {
+      if (kchunk == 0) {
         const int i = r / G, h = g * G + r % G;
         a.lse[((size_t)b * a.Hq + h) * a.n + i] = l2 * kLn2;
       }
@@ -197,9 +202,9 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
   }
 
   if constexpr (MERGE) {
-    // outputs of the rows r = blockIdx.x + gridDim.x * (4 it + wave), one wave per row
+    // outputs of the rows r = kchunk + nkc * (4 it + wave), one wave per row
     constexpr int PER = D / 64;
-    for (int r = blockIdx.x + gridDim.x * wave; r < rows; r += 4 * gridDim.x) {
+    for (int r = kchunk + nkc * wave; r < rows; r += 4 * nkc) {
       const size_t pr0 = (size_t)bg * rows + r;
       float mm, L;
       merged_ml(ml, nrows_all, pr0, splits, mm, L);
@@ -289,7 +294,7 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (a.mass) {
-    dim3 grid2((a.S + 127) / 128, a.B * a.Hkv);
+    const int grid2 = ((a.S + 127) / 128) * a.B * a.Hkv;
     if (fuse)
       attn_mass_mfma<KIND, D, true><<<grid2, 256, (size_t)rows * sizeof(float), s>>>(a, p.splits);
     else

@@ -63,6 +63,9 @@ struct Cfg {
   static constexpr int DMA_T = TILE / 1024;      // 1 KB DMA blocks per tensor tile
   static constexpr int DMA_W = DMA_T / QW;       // ... per wave
   static constexpr int MERGE = (KW - 1) * QW * (DT * 4 * 64 + 2 * 64) * 4;  // one column tile
+  // ring depth: one key group (QW = 4) keeps three tiles in flight; four groups fit two
+  // stages each in LDS
+  static constexpr int NST = (KIND == kCacheFP8) ? 2 : (QW == 4 ? 4 : QW == 2 ? 3 : 2);
 };
 
 // bf16: this wave's share of the DMA blocks of one tile (K and V) into stage memory `st`.
@@ -159,12 +162,12 @@ __device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2
       for (int ct = 0; ct < 2; ++ct) sacc[ct][kt] = mfma_bf16(kf, as_bf16x8(qf[ct][ds]), sacc[ct][kt]);
     }
   }
+  // Only the last tile of a split can hold keys past the end; the others skip the masking.
+  const bool full = key0 + kKeys <= kend;
   float ksc[8], vsc[8];
-  bool kval[8];
+  if constexpr (KIND == kCacheFP8) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    kval[e] = key0 + lg * 8 + e < kend;
-    if constexpr (KIND == kCacheFP8) {
+    for (int e = 0; e < 8; ++e) {
       ksc[e] = SC[lg * 8 + e];
       vsc[e] = SC[kKeys + lg * 8 + e];
     }
@@ -172,16 +175,22 @@ __device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2
   bf16x8 pb[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    float y[8], mt = -INFINITY;
+    float sv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float sv = sacc[ct][e >> 2][e & 3];
-      if constexpr (KIND == kCacheFP8) sv *= ksc[e];
-      y[e] = kval[e] ? sv * c : -INFINITY;
-      mt = fmaxf(mt, y[e]);
+      sv[e] = sacc[ct][e >> 2][e & 3];
+      if constexpr (KIND == kCacheFP8) sv[e] *= ksc[e];
     }
-    mt = wave_max_xor(mt, 16);
-    mt = wave_max_xor(mt, 32);
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key0 + lg * 8 + e >= kend) sv[e] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float mt = mx * c;                     // this tile's column max, log2 domain
     // Lazy rescale: move the running max only when a score would exceed it by 2^kLazy.
     if (__any(mt > m[ct] + kLazy)) {
       const float mn = fmaxf(m[ct], mt);
@@ -191,11 +200,13 @@ __device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2
       for (int dt = 0; dt < C::DT; ++dt) oacc[ct][dt] = oacc[ct][dt] * alpha;
       m[ct] = mn;
     }
-    const bool none = (m[ct] == -INFINITY);
+    // Every tile holds a valid key, so m[ct] is finite here; masked keys give exp2(-inf) = 0.
+    // The exponent is at most kLazy, so the raw hardware exp2 needs no range handling.
+    const float mneg = -m[ct];
     float p[8], ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = none ? 0.f : exp2f(y[e] - m[ct]);
+      p[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c, mneg));
       ps += p[e];
     }
     lsum[ct] += ps;
@@ -235,21 +246,21 @@ template <int KIND, int QW, int D>
 __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int splits, int kps) {
   using C = Cfg<KIND, QW, D>;
   constexpr int KW = C::KW, QT = 32 * QW;
-  // Two stage arrays per key group: distinct allocations, so a DMA into one stage is known
-  // not to alias the reads of the other.
-  __shared__ __attribute__((aligned(16))) char stage0[KW * C::STAGE];
-  __shared__ __attribute__((aligned(16))) char stage1[KW * C::STAGE];
+  // NST-stage ring per key group (bf16: NST - 1 tiles in flight; FP8 uses two stages).
+  constexpr int NST = C::NST;
+  __shared__ __attribute__((aligned(16))) char ring[KW * NST * C::STAGE];
 
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, lg = lane >> 4;
   const int qw = wave % QW, kw = wave / QW;
   const int gt = qw * 64 + lane;
 
-  int id = blockIdx.x;
-  const int split = id % splits;
-  id /= splits;
-  const int qt = id % qtiles;
-  const int bg = id / qtiles;
+  // All query tiles and key splits of one (b, KV head) run on one XCD: its K/V rows are
+  // fetched into that L2 once.
+  int bg, unit;
+  xcd_group_unit(blockIdx.x, a.B * a.Hkv, qtiles * splits, bg, unit);
+  const int split = unit % splits;
+  const int qt = unit / splits;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int rows = a.n * G;
@@ -277,8 +288,9 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
   const size_t head_base = ((size_t)b * a.Hkv + g) * a.S;
   const char* kc = (const char*)a.kc;
   const char* vc = (const char*)a.vc;
-  char* st0 = stage0 + kw * C::STAGE;
-  char* st1 = stage1 + kw * C::STAGE;
+  char* ring_kw = ring + kw * NST * C::STAGE;
+  char* st0 = ring_kw;
+  char* st1 = ring_kw + C::STAGE;
 
   f32x4 oacc[2][C::DT];
   float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
@@ -301,37 +313,27 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     }
   } else {
     constexpr int PEND = 2 * C::DMA_W;           // DMA ops of one tile per wave
-
-    dma_tile<KIND, QW, D>(st0, kc, vc, head_base, kbeg + kw * kKeys, kbeg, kend, qw, lane);
-    for (int it = 0; it < iters; it += 2) {
-      // even iteration: compute stage 0 while stage 1 fills
-      {
-        const int tile = it * KW + kw;
-        if (it + 1 < iters) {
-          dma_tile<KIND, QW, D>(st1, kc, vc, head_base, kbeg + (tile + KW) * kKeys, kbeg, kend, qw, lane);
-          DLLM_WAIT_VMCNT(PEND);
-        } else {
-          DLLM_WAIT_VMCNT(0);
-        }
-        lds_barrier();
-        if (tile < ntiles) tile_compute<KIND, QW, D>(st0, qf, oacc, m, lsum, kbeg + tile * kKeys, kend, c, l16, lg);
-        lds_barrier();
-      }
-      if (it + 1 >= iters) break;
-      // odd iteration: compute stage 1 while stage 0 fills
-      {
-        const int tile = (it + 1) * KW + kw;
-        if (it + 2 < iters) {
-          dma_tile<KIND, QW, D>(st0, kc, vc, head_base, kbeg + (tile + KW) * kKeys, kbeg, kend, qw, lane);
-          DLLM_WAIT_VMCNT(PEND);
-        } else {
-          DLLM_WAIT_VMCNT(0);
-        }
-        lds_barrier();
-        if (tile < ntiles) tile_compute<KIND, QW, D>(st1, qf, oacc, m, lsum, kbeg + tile * kKeys, kend, c, l16, lg);
-        lds_barrier();
-      }
+    // prologue: the first NST - 1 tiles of this key group
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+      if (st < iters)
+        dma_tile<KIND, QW, D>(ring_kw + st * C::STAGE, kc, vc, head_base, kbeg + (st * KW + kw) * kKeys,
+                              kbeg, kend, qw, lane);
+    for (int it = 0; it < iters; ++it) {
+      // this wave's transfers for tile `it` are done once at most those of the later tiles
+      // already issued are outstanding
+      if (it + NST - 2 < iters) DLLM_WAIT_VMCNT(PEND * (NST - 2));
+      else DLLM_WAIT_VMCNT(0);
+      lds_barrier();                             // tile `it` visible; slot of it - 1 free
+      if (it + NST - 1 < iters)
+        dma_tile<KIND, QW, D>(ring_kw + ((it + NST - 1) % NST) * C::STAGE, kc, vc, head_base,
+                              kbeg + ((it + NST - 1) * KW + kw) * kKeys, kbeg, kend, qw, lane);
+      const int tile = it * KW + kw;
+      if (tile < ntiles)
+        tile_compute<KIND, QW, D>(ring_kw + (it % NST) * C::STAGE, qf, oacc, m, lsum, kbeg + tile * kKeys,
+                                  kend, c, l16, lg);
     }
+    lds_barrier();                               // ring reads done before the merge reuses it
   }
 
   // Normaliser: each lane group held its own keys' share.
@@ -345,8 +347,8 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
   // time through the (now idle) stage memory.
   if constexpr (KW > 1) {
     constexpr int BLK = C::DT * 4 * 64 + 2 * 64;
-    static_assert(C::MERGE <= KW * C::STAGE, "merge buffer does not fit");
-    float* mb = (float*)stage0;
+    static_assert(C::MERGE <= KW * NST * C::STAGE, "merge buffer does not fit");
+    float* mb = (float*)ring;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       __syncthreads();

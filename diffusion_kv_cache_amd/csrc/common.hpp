@@ -26,18 +26,18 @@ enum CacheKind : int { kCacheF32 = DLLM_F32, kCacheBF16 = DLLM_BF16, kCacheFP8 =
 
 // ------------------------------------------------------------------------ conversions ---
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+// fp32 -> bf16 bits, round to nearest even (NaN stays a NaN): the hardware conversion
+// (v_cvt_pk_bf16_f32), branch-free.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Two fp32 values -> packed bf16 pair (lo in bits 0..15), one conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // fp32 -> OCP E4M3 ("fn") code: round to nearest even, saturate to +-448, NaN -> 0x7f|sign.
@@ -119,6 +119,24 @@ __device__ __forceinline__ void dma_16B(const void* g, const void* lds_block) {
                :
                : "v"(g), "s"(base)
                : "memory");
+}
+
+// ------------------------------------------------------------------ XCD placement -----
+
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2): workgroup id goes to
+// XCD id % 8.  For a grid of `groups` x `per` units in which the `per` units of a group share
+// their inputs (one KV head's cache rows, one head's queries), this maps the id to (group,
+// unit) so that every unit of a group runs on the same XCD, consecutively, and the shared
+// data is fetched into one L2 once.  Needs groups % 8 == 0 (else the plain row-major order).
+__device__ __forceinline__ void xcd_group_unit(int id, int groups, int per, int& group, int& unit) {
+  if ((groups & 7) == 0) {
+    const int local = id >> 3;
+    group = (id & 7) + 8 * (local / per);
+    unit = local % per;
+  } else {
+    group = id / per;
+    unit = id % per;
+  }
 }
 
 // ------------------------------------------------------------------------ reductions ----
