@@ -24,7 +24,9 @@ FLAGS = [
 # Per-source additions.  The attention forward pass keeps its MFMA accumulators in ordinary
 # VGPRs: with accumulation registers the compiler copied all 64 output accumulators out and
 # back on every key tile (the lazily rescaled softmax state is loop-carried through a branch).
-EXTRA = {"attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# NaNs are not honoured there either (no canonicalising max before every fmaxf of a score):
+# scores of finite inputs are finite, and masked keys are -inf, which stays honoured.
+EXTRA = {"attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
 
 
 def build(verbose: bool = False) -> str:

@@ -55,10 +55,6 @@ __global__ __launch_bounds__(64) void attn_merge(AttnArgs a, int splits) {
   if (threadIdx.x == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = (mm + log2f(L)) * kLn2;
 }
 
-// Largest packed-row count (n * G) whose log-sum-exp the fused merge + mass kernel stages in
-// LDS (32 KB); larger problems merge in attn_merge first.
-constexpr int kFusedMergeRows = 8192;
-
 // Merged state of packed row pr0 from the split partials, in split order (the same arithmetic
 // as attn_merge): running max mm and normaliser L.
 __device__ __forceinline__ void merged_ml(const float* ml, size_t nrows_all, size_t pr0, int splits,
@@ -76,19 +72,40 @@ __device__ __forceinline__ void merged_ml(const float* ml, size_t nrows_all, siz
 // Column attention mass, second pass after the log-sum-exp is known:
 //   mass[b, h, j] = sum_i exp(<q_i, k_j> * scale - lse_i).
 // One workgroup per (b, KV head g) and 128 keys, so each K row is read once for all G query
-// heads of its group: each wave keeps 32 keys' K rows as MFMA A operands (S^T = K Q^T), then
-// for each query head streams its n queries in tiles of 16 (the next tile's loads in flight
-// during the current one's MFMAs and exponentials).  Lane (l16, lg) sums query column l16 over
-// the tiles in order; the 16 lanes of a key are added at the end in a fixed butterfly order.
+// heads of its group: each wave keeps 32 keys' K rows as MFMA A operands (S^T = K Q^T).  The
+// group's queries stream through an LDS ring in tiles of 32 rows of one head (DMA, three
+// stages, shared by the four waves), and every row's log-sum-exp sits in LDS.  Lane (l16, lg)
+// sums query column l16 over the tiles in order; the 16 lanes of a key are added at the end
+// of each head in a fixed butterfly order.
 //
 // MERGE (the attention was split over keys): the kernel first forms every packed row's
-// log-sum-exp from the split partials (staged in LDS), the workgroups of key chunk 0 write
-// it, and the rows' outputs are merged here too (rows dealt round-robin over the key chunks),
-// so no separate merge launch is needed.
-template <int KIND, int D, bool MERGE>
+// log-sum-exp from the split partials, the workgroups of key chunk 0 write it, and the rows'
+// outputs are merged here too (rows dealt round-robin over the key chunks), so no separate
+// merge launch is needed.
+constexpr int kMassQRows = 32;                   // query rows per ring tile
+constexpr int kMassNst = 3;                      // ring stages
+// Largest packed-row count (n * G) whose log-sum-exp the mass pass stages in LDS (32 KB);
+// beyond it the rows' log-sum-exp is read from memory (and split attention merges first).
+constexpr int kMassLdsRows = 8192;
+
+template <int D>
+__device__ __forceinline__ int swz_q(int r) {   // chunk swizzle of a staged query row
+  return D == 128 ? ((r & 3) | (((r >> 2) & 3) << 2)) : ((r & 3) | (((r >> 2) & 1) << 2));
+}
+
+template <int KIND, int D, bool MERGE, bool LDS_LSE>
 __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
-  extern __shared__ float lse2_s[];              // MERGE: [n * G] log2-domain LSE
+  static_assert(LDS_LSE || !MERGE, "the fused merge stages the log-sum-exp in LDS");
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
   constexpr int DS = D / 32;
+  constexpr int RB = D * 2;                      // bytes per query row
+  constexpr int QTILE = kMassQRows * RB;         // bytes per ring tile
+  constexpr int RPI = 1024 / RB;                 // rows per DMA block
+  constexpr int NBLK = QTILE / 1024;             // DMA blocks per tile
+  constexpr int BPW = (NBLK + 3) / 4;            // per wave (the last wave may have fewer)
+  constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  char* ring = dyn;                              // [kMassNst][QTILE]
+  float* lse2_s = (float*)(dyn + kMassNst * QTILE);  // [n * G] log2-domain LSE
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, lg = lane >> 4;
   // All key chunks of one (b, KV head) run on one XCD: the group's queries are fetched into
@@ -103,6 +120,28 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
   const size_t head_base = ((size_t)b * a.Hkv + g) * a.S;
   constexpr int ELT = (KIND == kCacheFP8) ? 1 : 2;
   const char* kc = (const char*)a.kc;
+
+  // Query tiles: it = hh * ntq + (i0 / 32), rows i0 .. i0 + 31 of head g * G + hh (rows past
+  // n read row n - 1 and are masked out of the sums).
+  const int ntq = (a.n + kMassQRows - 1) / kMassQRows;
+  const int iters = G * ntq;
+  const bf16_t* q = (const bf16_t*)a.q;
+  auto issue = [&](int it, int slot) {
+    const int hh = it / ntq, i0 = (it % ntq) * kMassQRows;
+#pragma unroll
+    for (int u = 0; u < BPW; ++u) {
+      const int blk = wave * BPW + u;
+      if (blk < NBLK) {
+        const int r = blk * RPI + lane / CPR, sc = lane % CPR;
+        const int i = min(i0 + r, a.n - 1);
+        const bf16_t* src = q + (((size_t)b * a.n + i) * a.Hq + g * G + hh) * D + (sc ^ swz_q<D>(r)) * 8;
+        dma_16B(src, ring + slot * QTILE + blk * 1024);
+      }
+    }
+  };
+#pragma unroll
+  for (int st = 0; st < kMassNst - 1; ++st)
+    if (st < iters) issue(st, st);
 
   bf16x8 kf[2][DS];
   float ksc[2][4];
@@ -130,55 +169,58 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
     }
   }
 
+  // log-sum-exp of every packed row r = i * G + hh, log2 domain
   const size_t nrows_all = (size_t)a.B * a.Hkv * rows;
   const float* ml = a.part + (size_t)splits * nrows_all * D;
-  if constexpr (MERGE) {
-    for (int r = t; r < rows; r += 256) {
+  for (int r = t; LDS_LSE && r < rows; r += 256) {
+    const int i = r / G, h = g * G + r % G;
+    if constexpr (MERGE) {
       float mm, L;
       merged_ml(ml, nrows_all, (size_t)bg * rows + r, splits, mm, L);
       const float l2 = mm + log2f(L);
       lse2_s[r] = l2;
-      if (kchunk == 0) {
-        const int i = r / G, h = g * G + r % G;
-        a.lse[((size_t)b * a.Hq + h) * a.n + i] = l2 * kLn2;
-      }
+      if (kchunk == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = l2 * kLn2;
+    } else {
+      lse2_s[r] = a.lse[((size_t)b * a.Hq + h) * a.n + i] * kLog2e;
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   const float c = a.scale * kLog2e;
-  const bf16_t* q = (const bf16_t*)a.q;
-  const int ntq = (a.n + 15) / 16;
-  const int iters = G * ntq;
-  // Q^T fragments of tile `it` = (query head g*G + it / ntq, queries 16 (it % ntq) ...).
-  // Rows past n read row 0 (finite data) and are masked out of the sums.
-  // Without MERGE the row's log-sum-exp comes from global memory and is fetched with Q.
-  auto load_q = [&](int it, u32x4 (&qf)[DS], float& l) {
-    const int hh = it / ntq, i = (it % ntq) * 16 + l16;
-    const int ic = i < a.n ? i : 0;
-    const bf16_t* src = q + (((size_t)b * a.n + ic) * a.Hq + g * G + hh) * D + lg * 8;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[ds] = *(const u32x4*)(src + ds * 32);
-    if constexpr (!MERGE) l = a.lse[((size_t)b * a.Hq + g * G + hh) * a.n + ic];
-  };
-  u32x4 qcur[DS], qnext[DS];
-  float lcur = 0.f, lnext = 0.f;
-  if (iters > 0) load_q(0, qcur, lcur);
   float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  constexpr int PEND = BPW;                      // this wave's DMA ops per tile (at most)
   for (int it = 0; it < iters; ++it) {
-    if (it + 1 < iters) load_q(it + 1, qnext, lnext);
-    const int hh = it / ntq, i = (it % ntq) * 16 + l16;
-    const bool ok = i < a.n;
-    float lse2;
-    if constexpr (MERGE) lse2 = ok ? lse2_s[i * G + hh] : 0.f;
-    else lse2 = ok ? lcur * kLog2e : 0.f;
+    if (it + kMassNst - 2 < iters) DLLM_WAIT_VMCNT(PEND * (kMassNst - 2));
+    else DLLM_WAIT_VMCNT(0);
+    lds_barrier();
+    if (it + kMassNst - 1 < iters) issue(it + kMassNst - 1, (it + kMassNst - 1) % kMassNst);
+    const char* Q = ring + (it % kMassNst) * QTILE;
+    const int hh = it / ntq, i0 = (it % ntq) * kMassQRows;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < kMassQRows / 16; ++ct) {
+      const int r = ct * 16 + l16;
+      const int i = i0 + r;
+      const bool ok = i < a.n;
+      const int ic = min(i, a.n - 1);
+      const float lse2 = LDS_LSE ? lse2_s[ic * G + hh]
+                                 : a.lse[((size_t)b * a.Hq + g * G + hh) * a.n + ic] * kLog2e;
+      bf16x8 qf[DS];
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) sv = mfma_bf16(kf[kt][ds], as_bf16x8(qcur[ds]), sv);
+      for (int ds = 0; ds < DS; ++ds) {
+        const int ch = ds * 4 + lg;
+        qf[ds] = as_bf16x8(*(const u32x4*)(Q + r * RB + ((ch ^ swz_q<D>(r)) << 4)));
+      }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[kt][v] += ok ? exp2f(sv[v] * ksc[kt][v] * c - lse2) : 0.f;
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) sv = mfma_bf16(kf[kt][ds], qf[ds], sv);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sv[v] * ksc[kt][v], c, -lse2));
+          acc[kt][v] += ok ? e : 0.f;
+        }
+      }
     }
     if ((it + 1) % ntq == 0) {                   // last tile of this head: reduce and store
       const int h = g * G + hh;
@@ -196,9 +238,6 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
           acc[kt][v] = 0.f;
         }
     }
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qcur[ds] = qnext[ds];
-    lcur = lnext;
   }
 
   if constexpr (MERGE) {
@@ -287,7 +326,8 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   const int qtiles = (rows + p.qt - 1) / p.qt;
   hipError_t e = launch_attn_fwd<KIND, D>(a, p, qtiles, s);
   if (e != hipSuccess) return e;
-  const bool fuse = a.mass && p.splits > 1 && rows <= kFusedMergeRows;
+  const bool lds_lse = rows <= kMassLdsRows;
+  const bool fuse = a.mass && p.splits > 1 && lds_lse;
   if (p.splits > 1 && !fuse) {
     attn_merge<bf16_t, D><<<a.B * a.Hkv * rows, 64, 0, s>>>(a, p.splits);
     e = hipGetLastError();
@@ -295,10 +335,13 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   }
   if (a.mass) {
     const int grid2 = ((a.S + 127) / 128) * a.B * a.Hkv;
+    const size_t lds = (size_t)kMassNst * kMassQRows * D * 2 + (lds_lse ? (size_t)rows * sizeof(float) : 0);
     if (fuse)
-      attn_mass_mfma<KIND, D, true><<<grid2, 256, (size_t)rows * sizeof(float), s>>>(a, p.splits);
+      attn_mass_mfma<KIND, D, true, true><<<grid2, 256, lds, s>>>(a, p.splits);
+    else if (lds_lse)
+      attn_mass_mfma<KIND, D, false, true><<<grid2, 256, lds, s>>>(a, p.splits);
     else
-      attn_mass_mfma<KIND, D, false><<<grid2, 256, 0, s>>>(a, p.splits);
+      attn_mass_mfma<KIND, D, false, false><<<grid2, 256, lds, s>>>(a, p.splits);
     e = hipGetLastError();
   }
   return e;

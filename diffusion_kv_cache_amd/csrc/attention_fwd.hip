@@ -69,21 +69,34 @@ struct Cfg {
 };
 
 // bf16: this wave's share of the DMA blocks of one tile (K and V) into stage memory `st`.
+// koff / voff: this lane's byte offsets within a tile (row r of block blk, swizzled chunk),
+// fixed for the whole loop; a full tile then costs one address add per block.  The partial
+// last tile clamps rows past the end to the split's first row (their scores are masked).
 template <int KIND, int QW, int D>
-__device__ __forceinline__ void dma_tile(char* st, const char* kc, const char* vc, size_t head_base,
-                                         int key0, int kbeg, int kend, int qw, int lane) {
+__device__ __forceinline__ void dma_tile(char* st, const char* kh, const char* vh, int key0, int kbeg,
+                                         int kend, int qw, int lane, const uint32_t* koff,
+                                         const uint32_t* voff) {
   using C = Cfg<KIND, QW, D>;
   constexpr int RPI = 1024 / C::RB;              // rows per DMA block
+  if (key0 + kKeys <= kend) {
+    const char* kt = kh + (size_t)key0 * C::RB;
+    const char* vt = vh + (size_t)key0 * C::RB;
 #pragma unroll
-  for (int u = 0; u < C::DMA_W; ++u) {
-    const int blk = qw + QW * u;
-    const int r = blk * RPI + lane / C::CPR, s = lane % C::CPR;
-    const int key = key0 + r;
-    const size_t row = head_base + (key < kend ? key : kbeg);
-    const char* ks = kc + (row * D + (size_t)((s ^ swz_k<D>(r)) * 8)) * 2;
-    const char* vs = vc + (row * D + (size_t)((s ^ swz_v(r)) * 8)) * 2;
-    dma_16B(ks, st + blk * 1024);
-    dma_16B(vs, st + C::TILE + blk * 1024);
+    for (int u = 0; u < C::DMA_W; ++u) {
+      const int blk = qw + QW * u;
+      dma_16B(kt + koff[u], st + blk * 1024);
+      dma_16B(vt + voff[u], st + C::TILE + blk * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < C::DMA_W; ++u) {
+      const int blk = qw + QW * u;
+      const int r = blk * RPI + lane / C::CPR;
+      const int key = key0 + r;
+      const size_t rowb = (size_t)((key < kend ? key : kbeg) - r) * C::RB;
+      dma_16B(kh + rowb + koff[u], st + blk * 1024);
+      dma_16B(vh + rowb + voff[u], st + C::TILE + blk * 1024);
+    }
   }
 }
 
@@ -188,8 +201,7 @@ __device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2
     }
     float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
+    mx = max_across_rows(mx);
     const float mt = mx * c;                     // this tile's column max, log2 domain
     // Lazy rescale: move the running max only when a score would exceed it by 2^kLazy.
     if (__any(mt > m[ct] + kLazy)) {
@@ -313,12 +325,22 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     }
   } else {
     constexpr int PEND = 2 * C::DMA_W;           // DMA ops of one tile per wave
+    constexpr int RPI = 1024 / C::RB;
+    uint32_t koff[C::DMA_W], voff[C::DMA_W];
+#pragma unroll
+    for (int u = 0; u < C::DMA_W; ++u) {
+      const int r = (qw + QW * u) * RPI + lane / C::CPR, sc = lane % C::CPR;
+      koff[u] = (uint32_t)(r * C::RB + ((sc ^ swz_k<D>(r)) << 4));
+      voff[u] = (uint32_t)(r * C::RB + ((sc ^ swz_v(r)) << 4));
+    }
+    const char* kh = kc + head_base * C::RB;
+    const char* vh = vc + head_base * C::RB;
     // prologue: the first NST - 1 tiles of this key group
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
       if (st < iters)
-        dma_tile<KIND, QW, D>(ring_kw + st * C::STAGE, kc, vc, head_base, kbeg + (st * KW + kw) * kKeys,
-                              kbeg, kend, qw, lane);
+        dma_tile<KIND, QW, D>(ring_kw + st * C::STAGE, kh, vh, kbeg + (st * KW + kw) * kKeys, kbeg,
+                              kend, qw, lane, koff, voff);
     for (int it = 0; it < iters; ++it) {
       // this wave's transfers for tile `it` are done once at most those of the later tiles
       // already issued are outstanding
@@ -326,8 +348,8 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
       else DLLM_WAIT_VMCNT(0);
       lds_barrier();                             // tile `it` visible; slot of it - 1 free
       if (it + NST - 1 < iters)
-        dma_tile<KIND, QW, D>(ring_kw + ((it + NST - 1) % NST) * C::STAGE, kc, vc, head_base,
-                              kbeg + ((it + NST - 1) * KW + kw) * kKeys, kbeg, kend, qw, lane);
+        dma_tile<KIND, QW, D>(ring_kw + ((it + NST - 1) % NST) * C::STAGE, kh, vh,
+                              kbeg + ((it + NST - 1) * KW + kw) * kKeys, kbeg, kend, qw, lane, koff, voff);
       const int tile = it * KW + kw;
       if (tile < ntiles)
         tile_compute<KIND, QW, D>(ring_kw + (it % NST) * C::STAGE, qf, oacc, m, lsum, kbeg + tile * kKeys,
@@ -338,10 +360,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
 
   // Normaliser: each lane group held its own keys' share.
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    lsum[ct] += __shfl_xor(lsum[ct], 16, kWave);
-    lsum[ct] += __shfl_xor(lsum[ct], 32, kWave);
-  }
+  for (int ct = 0; ct < 2; ++ct) lsum[ct] = sum_across_rows(lsum[ct]);
 
   // Merge the KW key groups in order (their key ranges are disjoint), one column tile at a
   // time through the (now idle) stage memory.

@@ -145,6 +145,24 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, kWave));
 }
 
+// Max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48), with the
+// gfx950 row swaps instead of LDS permutes: v_permlane32_swap exchanges the upper half of
+// its first operand with the lower half of its second, v_permlane16_swap the odd rows of the
+// first with the even rows of the second; with both operands = x, the two results hold x of
+// lane l and of its partner, in some order, so max / sum of the pair is the same on both.
+__device__ __forceinline__ float max_across_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_across_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ------------------------------------------------------------------------ rotary --------
 
 // Turns of rotary pair i: t_i = base^(-2i/D) / (2 pi), split into two floats (hi + lo).

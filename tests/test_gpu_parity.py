@@ -202,6 +202,9 @@ ATT_CASES = {
                          prompt=260, cache="fp8", block_start=263, block_len=20, seed=43),
     "fp8_d64_g8_qt128": C(batch=1, hidden=256, q_heads=8, kv_heads=1, head_dim=64, seq=300,
                           prompt=150, cache="fp8", block_start=151, block_len=70, seed=44),
+    # n * G = 8800 packed rows: more log-sum-exp values than the mass pass stages in LDS
+    "bf16_mass_rows_over_lds": C(batch=1, hidden=256, q_heads=8, kv_heads=1, head_dim=64,
+                                 seq=1100, prompt=0, block_start=0, block_len=1100, seed=45),
 }
 
 
