@@ -177,8 +177,11 @@ def run(args):
     torch.cuda.synchronize()
 
     names = ["refresh", "attention"] + (["drift"] if track else [])
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(args.steps)]
+    # Per-call events go into every `event_every`-th timed step only: each recorded event adds a
+    # bubble of a few microseconds to the GPU timeline, which would otherwise inflate the step
+    # time it is meant to split up.
+    sampled = [s for s in range(args.steps) if s % args.event_every == args.event_every - 1]
+    ev = {s: [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for s in sampled}
 
     def step(ly, evs=None):
         if evs:
@@ -201,11 +204,11 @@ def run(args):
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for s in range(args.steps):
-        step(layers[(args.warmup + s) % L], ev[s])
+        step(layers[(args.warmup + s) % L], ev.get(s))
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    per = {nm: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)])) * 1e3
+    per = {nm: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in sampled])) * 1e3
            for i, nm in enumerate(names)}
     ms_per_step = total_ms / args.steps
     value = M / (ms_per_step * 1e-3)
@@ -232,6 +235,7 @@ def run(args):
                    "kv_heads": wl.kv_heads, "head_dim": D, "cache_dtype": wl.cache,
                    "tracking": track, "layer_instances": L, "parallelism": "none (1 GPU)"},
         "per_call_us": {k_: round(v, 2) for k_, v in per.items()},
+        "per_call_sampled_steps": len(sampled),
         "rooflines": entries,
         "roofline": roof,
     }
@@ -299,11 +303,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="layer instances to rotate (0: auto)")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="record per-call events in every N-th timed step (at least one step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="after timing, run a plain device copy of this size (counter scaling)")
     args = ap.parse_args()
+    args.event_every = max(1, min(args.event_every, args.steps))
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
               f"requested).", file=sys.stderr)
