@@ -223,7 +223,7 @@ dllm_status dllm_block_attention(const dllm_cache* c, const void* q, int32_t act
                 d.num_kv_heads);
   if (act_dtype == DLLM_F32) {
     if (d.kv_dtype != DLLM_F32) return fail(DLLM_EUNSUPPORTED, "fp32 queries need an fp32 cache");
-    if (d.max_seq > 16384) return fail(DLLM_EUNSUPPORTED, "fp32 attention supports S <= 16384");
+    if (d.max_seq > 8192) return fail(DLLM_EUNSUPPORTED, "fp32 attention supports S <= 8192");
   } else if (act_dtype == DLLM_BF16) {
     if (d.kv_dtype == DLLM_F32) return fail(DLLM_EUNSUPPORTED, "bf16 queries need a bf16 or FP8 cache");
   } else {

@@ -267,56 +267,100 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
 }
 
 // ---------------------------------------------------------------- fp32 (small shapes) ---
-// One wave per (b, h, i): scores into LDS, exact softmax, output; fp32 FMA in key order.
-__global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
-  extern __shared__ float z[];
-  const int lane = threadIdx.x;
+// One workgroup per (b, h, i): q staged in LDS, one thread per key for the scores (fp32 FMA
+// in d order), block max / sum, then the output with 256 / D key groups per column, their
+// partial sums added in group order.
+template <int D>
+__global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
+  extern __shared__ float z[];                   // [S] scores, then [D] q, then reductions
+  constexpr int NG = 256 / D;                    // key groups of the output pass
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int i = blockIdx.x % a.n, bh = blockIdx.x / a.n;
   const int b = bh / a.Hq, h = bh % a.Hq, g = h / (a.Hq / a.Hkv);
-  const int D = a.D;
+  float* qs = z + a.S;
+  float* red = qs + D;                           // [4] wave results, then [NG][D] partials
   const float* q = (const float*)a.q + (((size_t)b * a.n + i) * a.Hq + h) * D;
   const float* K = (const float*)a.kc + ((size_t)b * a.Hkv + g) * a.S * D;
   const float* V = (const float*)a.vc + ((size_t)b * a.Hkv + g) * a.S * D;
+  if (t < D) qs[t] = q[t];
+  __syncthreads();
   float mx = -INFINITY;
-  for (int j = lane; j < a.S; j += 64) {
+  for (int j = t; j < a.S; j += 256) {
+    const float4* kr = (const float4*)(K + (size_t)j * D);
     float s = 0.f;
-    for (int d = 0; d < D; ++d) s = fmaf(q[d], K[(size_t)j * D + d], s);
+#pragma unroll 8
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+      const float4 k4 = kr[d4];
+      s = fmaf(qs[4 * d4], k4.x, s);
+      s = fmaf(qs[4 * d4 + 1], k4.y, s);
+      s = fmaf(qs[4 * d4 + 2], k4.z, s);
+      s = fmaf(qs[4 * d4 + 3], k4.w, s);
+    }
     s *= a.scale;
     z[j] = s;
     mx = fmaxf(mx, s);
   }
   for (int msk = 1; msk < 64; msk <<= 1) mx = fmaxf(mx, __shfl_xor(mx, msk, kWave));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
   float l = 0.f;
-  for (int j = lane; j < a.S; j += 64) {
+  for (int j = t; j < a.S; j += 256) {
     const float p = expf(z[j] - mx);
     z[j] = p;
     l += p;
   }
   for (int msk = 1; msk < 64; msk <<= 1) l += __shfl_xor(l, msk, kWave);
+  if (lane == 0) red[wave] = l;
   __syncthreads();
-  float* o = (float*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-    for (int j = 0; j < a.S; ++j) acc = fmaf(z[j], V[(size_t)j * D + d], acc);
-    o[d] = acc / l;
+  l = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();
+  const int d = t % D, grp = t / D;
+  float acc = 0.f;
+  for (int j = grp; j < a.S; j += NG) acc = fmaf(z[j], V[(size_t)j * D + d], acc);
+  red[4 + grp * D + d] = acc;
+  __syncthreads();
+  if (t < D) {
+    float o = 0.f;
+    for (int q2 = 0; q2 < NG; ++q2) o += red[4 + q2 * D + t];
+    ((float*)a.out)[(((size_t)b * a.n + i) * a.Hq + h) * D + t] = o / l;
   }
-  if (lane == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = mx + logf(l);
+  if (t == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = mx + logf(l);
 }
 
+// One thread per key (64 keys per workgroup) with its K row in registers; the head's queries
+// and their log-sum-exp are staged in LDS 64 at a time and summed in query order.
+template <int D>
 __global__ __launch_bounds__(64) void attn_mass_f32(AttnArgs a) {
-  const int j = blockIdx.x * 64 + threadIdx.x;
+  __shared__ float qs[64][D + 1];
+  __shared__ float ls[64];
+  const int t = threadIdx.x;
+  const int j = blockIdx.x * 64 + t;
   const int bh = blockIdx.y, b = bh / a.Hq, h = bh % a.Hq, g = h / (a.Hq / a.Hkv);
-  if (j >= a.S) return;
-  const int D = a.D;
-  const float* K = (const float*)a.kc + (((size_t)b * a.Hkv + g) * a.S + j) * D;
-  float acc = 0.f;
-  for (int i = 0; i < a.n; ++i) {
-    const float* q = (const float*)a.q + (((size_t)b * a.n + i) * a.Hq + h) * D;
-    float s = 0.f;
-    for (int d = 0; d < D; ++d) s = fmaf(q[d], K[d], s);
-    acc += expf(s * a.scale - a.lse[((size_t)b * a.Hq + h) * a.n + i]);
+  const float* K = (const float*)a.kc + (((size_t)b * a.Hkv + g) * a.S + (j < a.S ? j : 0)) * D;
+  float kr[D];
+#pragma unroll
+  for (int d4 = 0; d4 < D / 4; ++d4) {
+    const float4 k4 = ((const float4*)K)[d4];
+    kr[4 * d4] = k4.x; kr[4 * d4 + 1] = k4.y; kr[4 * d4 + 2] = k4.z; kr[4 * d4 + 3] = k4.w;
   }
-  a.mass[((size_t)b * a.Hq + h) * a.S + j] = acc;
+  float acc = 0.f;
+  for (int i0 = 0; i0 < a.n; i0 += 64) {
+    const int cnt = min(64, a.n - i0);
+    __syncthreads();
+    for (int r = 0; r < cnt; ++r)
+      for (int d = t; d < D; d += 64) qs[r][d] = ((const float*)a.q)[(((size_t)b * a.n + i0 + r) * a.Hq + h) * D + d];
+    if (t < cnt) ls[t] = a.lse[((size_t)b * a.Hq + h) * a.n + i0 + t];
+    __syncthreads();
+    for (int r = 0; r < cnt; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) s = fmaf(qs[r][d], kr[d], s);
+      acc += expf(s * a.scale - ls[r]);
+    }
+  }
+  if (j < a.S) a.mass[((size_t)b * a.Hq + h) * a.S + j] = acc;
 }
 
 template <int KIND, int D>
@@ -377,11 +421,14 @@ AttnPlan plan_attention(int B, int n, int Hq, int Hkv, int S, int D, int act, in
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   if (a.act == DLLM_F32) {
-    attn_f32<<<a.B * a.Hq * a.n, 64, (size_t)a.S * sizeof(float), s>>>(a);
+    const size_t lds = ((size_t)a.S + a.D + 4 + 256) * sizeof(float);
+    if (a.D == 128) attn_f32<128><<<a.B * a.Hq * a.n, 256, lds, s>>>(a);
+    else attn_f32<64><<<a.B * a.Hq * a.n, 256, lds, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.mass) return e;
     dim3 grid((a.S + 63) / 64, a.B * a.Hq);
-    attn_mass_f32<<<grid, 64, 0, s>>>(a);
+    if (a.D == 128) attn_mass_f32<128><<<grid, 64, 0, s>>>(a);
+    else attn_mass_f32<64><<<grid, 64, 0, s>>>(a);
     return hipGetLastError();
   }
   if (a.kind == kCacheFP8) return a.D == 128 ? launch_mfma<kCacheFP8, 128>(a, p, s) : launch_mfma<kCacheFP8, 64>(a, p, s);

@@ -62,7 +62,6 @@ struct Cfg {
   static constexpr int GT = 64 * QW;             // threads per group
   static constexpr int DMA_T = TILE / 1024;      // 1 KB DMA blocks per tensor tile
   static constexpr int DMA_W = DMA_T / QW;       // ... per wave
-  static constexpr int MERGE = (KW - 1) * QW * (DT * 4 * 64 + 2 * 64) * 4;  // one column tile
   // ring depth: one key group (QW = 4) keeps three tiles in flight; four groups fit two
   // stages each in LDS
   static constexpr int NST = (KIND == kCacheFP8) ? 2 : (QW == 4 ? 4 : QW == 2 ? 3 : 2);
@@ -260,7 +259,10 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
   constexpr int KW = C::KW, QT = 32 * QW;
   // NST-stage ring per key group (bf16: NST - 1 tiles in flight; FP8 uses two stages).
   constexpr int NST = C::NST;
-  __shared__ __attribute__((aligned(16))) char ring[KW * NST * C::STAGE];
+  // (also the key-group merge buffer: KW x QW waves x two column tiles of D x 16 + 2 values)
+  constexpr int MERGE_BYTES = (KW > 1) ? KW * QW * 2 * (C::DT * 4 * 64 + 2 * 64) * 4 : 0;
+  constexpr int RING_BYTES = KW * NST * C::STAGE > MERGE_BYTES ? KW * NST * C::STAGE : MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char ring[RING_BYTES];
 
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -362,47 +364,63 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) lsum[ct] = sum_across_rows(lsum[ct]);
 
-  // Merge the KW key groups in order (their key ranges are disjoint), one column tile at a
-  // time through the (now idle) stage memory.
+  // Merge the KW key groups (disjoint key ranges) through the idle ring: every wave writes its
+  // state, then each wave combines a 1/KW slice of the output columns d for all groups, in
+  // group order, and writes that slice.
+  constexpr int DTW = C::DT / KW;                // output 16-column tiles per wave
+  int dt0 = 0;
+  f32x4 ofin[2][DTW];
   if constexpr (KW > 1) {
-    constexpr int BLK = C::DT * 4 * 64 + 2 * 64;
-    static_assert(C::MERGE <= KW * NST * C::STAGE, "merge buffer does not fit");
+    constexpr int BLK = 2 * (C::DT * 4 * 64 + 2 * 64);
+    static_assert(KW * QW * BLK * 4 <= RING_BYTES, "merge buffer does not fit");
     float* mb = (float*)ring;
+    __syncthreads();                             // every wave is done with the ring
+    {
+      float* dst = mb + (kw * QW + qw) * BLK;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      __syncthreads();
-      if (kw > 0) {
-        float* dst = mb + ((kw - 1) * QW + qw) * BLK;
+      for (int ct = 0; ct < 2; ++ct) {
+        float* dc = dst + ct * (C::DT * 4 * 64 + 2 * 64);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) dst[(dt * 4 + v) * 64 + lane] = oacc[ct][dt][v];
-        dst[C::DT * 4 * 64 + lane] = m[ct];
-        dst[C::DT * 4 * 64 + 64 + lane] = lsum[ct];
-      }
-      __syncthreads();
-      if (kw == 0) {
-        for (int w2 = 1; w2 < KW; ++w2) {
-          const float* src = mb + ((w2 - 1) * QW + qw) * BLK;
-          const float m2 = src[C::DT * 4 * 64 + lane];
-          const float l2 = src[C::DT * 4 * 64 + 64 + lane];
-          const float mm = fmaxf(m[ct], m2);
-          const float a0 = (m[ct] == -INFINITY) ? 0.f : exp2f(m[ct] - mm);
-          const float a1 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mm);
-          lsum[ct] = lsum[ct] * a0 + l2 * a1;
-#pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              oacc[ct][dt][v] = oacc[ct][dt][v] * a0 + src[(dt * 4 + v) * 64 + lane] * a1;
-          m[ct] = mm;
-        }
+          for (int v = 0; v < 4; ++v) dc[(dt * 4 + v) * 64 + lane] = oacc[ct][dt][v];
+        dc[C::DT * 4 * 64 + lane] = m[ct];
+        dc[C::DT * 4 * 64 + 64 + lane] = lsum[ct];
       }
     }
-    if (kw > 0) return;
+    __syncthreads();
+    dt0 = kw * DTW;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w2 = 0; w2 < KW; ++w2)
+        mm = fmaxf(mm, mb[(w2 * QW + qw) * BLK + ct * (C::DT * 4 * 64 + 2 * 64) + C::DT * 4 * 64 + lane]);
+      float L = 0.f;
+#pragma unroll
+      for (int u = 0; u < DTW; ++u) ofin[ct][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w2 = 0; w2 < KW; ++w2) {
+        const float* src = mb + (w2 * QW + qw) * BLK + ct * (C::DT * 4 * 64 + 2 * 64);
+        const float mw = src[C::DT * 4 * 64 + lane];
+        const float aw = (mw == -INFINITY) ? 0.f : exp2f(mw - mm);
+        L += src[C::DT * 4 * 64 + 64 + lane] * aw;
+#pragma unroll
+        for (int u = 0; u < DTW; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) ofin[ct][u][v] += src[((dt0 + u) * 4 + v) * 64 + lane] * aw;
+      }
+      m[ct] = mm;
+      lsum[ct] = L;
+    }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int u = 0; u < DTW; ++u) ofin[ct][u] = oacc[ct][u];
   }
 
-  // Final output when unsplit, else this split's partial state.
+  // This wave's slice of the final output when unsplit, else of this split's partial state.
   const size_t nrows_all = (size_t)a.B * a.Hkv * rows;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
@@ -413,23 +431,23 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
       const float inv = 1.f / lsum[ct];
       bf16_t* o = (bf16_t*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const int d = dt * 16 + lg * 4;
+      for (int u = 0; u < DTW; ++u) {
+        const int d = (dt0 + u) * 16 + lg * 4;
         uint2 w2;
-        w2.x = pack_bf16x2(oacc[ct][dt][0] * inv, oacc[ct][dt][1] * inv);
-        w2.y = pack_bf16x2(oacc[ct][dt][2] * inv, oacc[ct][dt][3] * inv);
+        w2.x = pack_bf16x2(ofin[ct][u][0] * inv, ofin[ct][u][1] * inv);
+        w2.y = pack_bf16x2(ofin[ct][u][2] * inv, ofin[ct][u][3] * inv);
         *(uint2*)(o + d) = w2;
       }
-      if (lg == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = (m[ct] + log2f(lsum[ct])) * kLn2;
+      if (lg == 0 && kw == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = (m[ct] + log2f(lsum[ct])) * kLn2;
     } else {
       const size_t pr = (size_t)split * nrows_all + (size_t)bg * rows + r;
       float* po = a.part + pr * D;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const int d = dt * 16 + lg * 4;
-        *(float4*)(po + d) = make_float4(oacc[ct][dt][0], oacc[ct][dt][1], oacc[ct][dt][2], oacc[ct][dt][3]);
+      for (int u = 0; u < DTW; ++u) {
+        const int d = (dt0 + u) * 16 + lg * 4;
+        *(float4*)(po + d) = make_float4(ofin[ct][u][0], ofin[ct][u][1], ofin[ct][u][2], ofin[ct][u][3]);
       }
-      if (lg == 0) {
+      if (lg == 0 && kw == 0) {
         float* ml = a.part + (size_t)splits * nrows_all * D + pr * 2;
         ml[0] = m[ct];
         ml[1] = lsum[ct];

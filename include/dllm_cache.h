@@ -164,7 +164,9 @@ DLLM_API size_t dllm_attention_workspace_bytes(const dllm_cache_desc *d, int32_t
  *                after the log-sum-exp is known)
  *   workspace    device scratch of ws_bytes >= dllm_attention_workspace_bytes(...)
  * FP8 cache: K and V are dequantised with their row scales inside the kernel.
- * Results are deterministic: every reduction runs in a fixed order. */
+ * Results are deterministic: every reduction runs in a fixed order.
+ * Errors: DLLM_EINVAL, DLLM_ESIZE (workspace too small), DLLM_EUNSUPPORTED (fp32 with
+ * S > 8192), DLLM_ELAUNCH. */
 DLLM_API dllm_status dllm_block_attention(const dllm_cache *c, const void *q, int32_t act_dtype,
                                  int32_t num_q_heads, int32_t n, float softmax_scale,
                                  void *out, float *lse, float *attn_mass, void *workspace,
