@@ -34,10 +34,17 @@ void refresh_partial(RefreshArgs a, float* part) {
   const int cpr = Lp / 8;                        // 16-byte chunks per staged row
   const int mask = (cpr % 8 == 0) ? 7 : 3;
 
-  // Prologue: the 32 row positions, then the gathered A slice global -> LDS by DMA (each
-  // lane fetches the source chunk that lands, swizzled, at its LDS slot) together with the
-  // first W steps.  Rows past M gather the last valid row: their accumulators are never
-  // stored.
+  // Prologue: the first W steps go out before anything else (they depend on nothing); then
+  // the 32 row positions, then the gathered A slice global -> LDS by DMA (each lane fetches
+  // the source chunk that lands, swizzled, at its LDS slot).  Rows past M gather the last
+  // valid row: their accumulators are never stored.
+  const int col = blockIdx.y * 128 + wave * 16 + l16;
+  const bool col_ok = col < N;
+  const bf16_t* wr = (const bf16_t*)a.w + (size_t)(col_ok ? col : N - 1) * a.H + kb + lg * 8;
+  const int steps = Lp / 32;
+  u32x4 wv[kPrefetch];
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u) wv[u] = *(const u32x4*)(wr + min(u, steps - 1) * 32);
   __shared__ int s_row[32];                      // hidden row offset (b * S + pos) per A row
   if (t < 32) {
     const int m = min(m0 + t, a.M - 1);
@@ -52,13 +59,6 @@ void refresh_partial(RefreshArgs a, float* part) {
     const bf16_t* src = hid + (size_t)s_row[r] * a.H + kb + (j ^ (r & mask)) * 8;
     dma_16B(src, As + blk * 64);
   }
-  const int col = blockIdx.y * 128 + wave * 16 + l16;
-  const bool col_ok = col < N;
-  const bf16_t* wr = (const bf16_t*)a.w + (size_t)(col_ok ? col : N - 1) * a.H + kb + lg * 8;
-  const int steps = Lp / 32;
-  u32x4 wv[kPrefetch];
-#pragma unroll
-  for (int u = 0; u < kPrefetch; ++u) wv[u] = *(const u32x4*)(wr + min(u, steps - 1) * 32);
   DLLM_WAIT_VMCNT(0);
   __syncthreads();
 
@@ -97,70 +97,94 @@ void refresh_partial(RefreshArgs a, float* part) {
     }
 }
 
-// One wave per (row, head): lane i < D/2 owns the rotary pair (i, i + D/2); for D = 64 the
-// two half-waves take two rows.
+// One 16-lane group per (row, head): lane L of the group owns the rotary pairs
+// (i, i + D/2) for i in [L * PPL, L * PPL + PPL), read as PPL-float vectors from each
+// partition.  A wave takes four consecutive (row, head) items.
 template <int D, int KIND>
-__global__ __launch_bounds__(256) void refresh_reduce(RefreshArgs a, const float* part) {
+__global__ __launch_bounds__(64) void refresh_reduce(RefreshArgs a, const float* part) {
   constexpr int HALF = D / 2;
-  constexpr int RPW = 64 / HALF;                 // rows per wave
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = lane % HALF;
-  const int j = blockIdx.x;
-  const int N = (a.Hq + 2 * a.Hkv) * D;
-  const int m = (blockIdx.y * 4 + wave) * RPW + lane / HALF;
-  const bool ok = m < a.M;
-  const int mm = ok ? m : 0;
-  float x = 0.f, y = 0.f;
+  constexpr int PPL = HALF / 16;                 // pairs per lane: 4 (D = 128) or 2 (D = 64)
+  typedef __attribute__((ext_vector_type(PPL))) float fvec;
+  const int lane = threadIdx.x, L = lane & 15;
+  const int heads = a.Hq + 2 * a.Hkv, N = heads * D;
+  const int item = blockIdx.x * 4 + (lane >> 4);
+  const bool ok = item < a.M * heads;
+  const int it = ok ? item : 0;
+  const int m = it / heads, j = it % heads;
+  // every lane forms the rotation frequency of pair (lane mod D/2); the group's lanes
+  // fetch theirs by shuffle
+  float hi_own, lo_own;
+  rope_turns(lane % HALF, D, a.rope_base, hi_own, lo_own);
+  fvec x = {}, y = {};
 #pragma unroll
   for (int p = 0; p < kKSplit; ++p) {
-    const float* row = part + ((size_t)p * a.M + mm) * N + j * D;
-    x = x + row[i];
-    y = y + row[i + HALF];
+    const float* row = part + ((size_t)p * a.M + m) * N + j * D + L * PPL;
+    x = x + *(const fvec*)row;
+    y = y + *(const fvec*)(row + HALF);
   }
-  if (j < a.Hq + a.Hkv) {
-    float hi, lo, s, c;
-    rope_turns(i, D, a.rope_base, hi, lo);
-    rope_sincos(a.idx[mm], hi, lo, s, c);
-    rope_rotate(x, y, s, c);
+  const int pos = a.idx[m];
+  const bool rot = j < a.Hq + a.Hkv;
+#pragma unroll
+  for (int e = 0; e < PPL; ++e) {
+    const float hi = __shfl(hi_own, L * PPL + e, kWave), lo = __shfl(lo_own, L * PPL + e, kWave);
+    if (rot) {
+      float sn, cs, xe = x[e], ye = y[e];
+      rope_sincos(pos, hi, lo, sn, cs);
+      rope_rotate(xe, ye, sn, cs);
+      x[e] = xe;
+      y[e] = ye;
+    }
   }
-  const int b = mm / a.n;
+  const int b = m / a.n;
+  const int i0 = L * PPL;
   if (j < a.Hq) {
     if (ok) {
-      bf16_t* q = (bf16_t*)a.q_out + ((size_t)mm * a.Hq + j) * D;
-      q[i] = f32_to_bf16(x);
-      q[i + HALF] = f32_to_bf16(y);
+      bf16_t* q = (bf16_t*)a.q_out + ((size_t)m * a.Hq + j) * D;
+#pragma unroll
+      for (int e = 0; e < PPL; ++e) {
+        q[i0 + e] = f32_to_bf16(x[e]);
+        q[i0 + e + HALF] = f32_to_bf16(y[e]);
+      }
     }
     return;
   }
   const bool is_k = j < a.Hq + a.Hkv;
   const int g = is_k ? j - a.Hq : j - a.Hq - a.Hkv;
-  const size_t row = ((size_t)b * a.Hkv + g) * a.S + a.idx[mm];
+  const size_t row = ((size_t)b * a.Hkv + g) * a.S + pos;
   if constexpr (KIND == kCacheFP8) {
-    float am = fmaxf(fabsf(x), fabsf(y));
+    float am = 0.f;
 #pragma unroll
-    for (int msk = 1; msk < HALF; msk <<= 1) am = fmaxf(am, __shfl_xor(am, msk, kWave));
+    for (int e = 0; e < PPL; ++e) am = fmaxf(am, fmaxf(fabsf(x[e]), fabsf(y[e])));
+#pragma unroll
+    for (int msk = 1; msk < 16; msk <<= 1) am = fmaxf(am, __shfl_xor(am, msk, kWave));
     const float scale = (am == 0.f) ? 1.f : am / 448.f;
     if (ok) {
       uint8_t* dst = (uint8_t*)(is_k ? a.kc : a.vc) + row * D;
-      dst[i] = (uint8_t)e4m3_encode(x / scale);
-      dst[i + HALF] = (uint8_t)e4m3_encode(y / scale);
-      if (i == 0) (is_k ? a.ks : a.vs)[row] = scale;
+#pragma unroll
+      for (int e = 0; e < PPL; ++e) {
+        dst[i0 + e] = (uint8_t)e4m3_encode(x[e] / scale);
+        dst[i0 + e + HALF] = (uint8_t)e4m3_encode(y[e] / scale);
+      }
+      if (L == 0) (is_k ? a.ks : a.vs)[row] = scale;
     }
   } else {
     if (ok) {
       bf16_t* dst = (bf16_t*)(is_k ? a.kc : a.vc) + row * D;
-      dst[i] = f32_to_bf16(x);
-      dst[i + HALF] = f32_to_bf16(y);
+#pragma unroll
+      for (int e = 0; e < PPL; ++e) {
+        dst[i0 + e] = f32_to_bf16(x[e]);
+        dst[i0 + e + HALF] = f32_to_bf16(y[e]);
+      }
     }
   }
 }
 
 template <int D>
 hipError_t launch_reduce(const RefreshArgs& a, const float* part, hipStream_t s) {
-  constexpr int RPB = 4 * (128 / D);             // rows per workgroup
-  dim3 grid(a.Hq + 2 * a.Hkv, (a.M + RPB - 1) / RPB);
-  if (a.kind == kCacheFP8) refresh_reduce<D, kCacheFP8><<<grid, 256, 0, s>>>(a, part);
-  else refresh_reduce<D, kCacheBF16><<<grid, 256, 0, s>>>(a, part);
+  const long long items = (long long)a.M * (a.Hq + 2 * a.Hkv);
+  const unsigned grid = (unsigned)((items + 3) / 4);
+  if (a.kind == kCacheFP8) refresh_reduce<D, kCacheFP8><<<grid, 64, 0, s>>>(a, part);
+  else refresh_reduce<D, kCacheBF16><<<grid, 64, 0, s>>>(a, part);
   return hipGetLastError();
 }
 

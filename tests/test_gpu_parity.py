@@ -46,6 +46,14 @@ REFRESH_CASES = {
                               prompt=40, block_start=45, block_len=45, seed=22),
     "f32_d128_gqa": C(batch=1, hidden=512, q_heads=4, kv_heads=2, head_dim=128, seq=40,
                       prompt=20, act="f32", cache="f32", block_start=3, block_len=30, seed=18),
+    # more split-K shapes: GQA with D = 64 over a scattered set, 129 query heads of 64, and
+    # 33 + 33 + 33 heads of 128
+    "splitk_gqa_d64": C(batch=2, hidden=512, q_heads=6, kv_heads=2, head_dim=64, seq=80,
+                        prompt=40, refresh="window+subset", window=5, subset=8, seed=23),
+    "splitk_d64_129_heads": C(batch=1, hidden=256, q_heads=129, kv_heads=1, head_dim=64,
+                              seq=40, prompt=20, block_start=21, block_len=7, seed=24),
+    "splitk_d128_33_heads": C(batch=2, hidden=256, q_heads=33, kv_heads=33, head_dim=128,
+                              seq=48, prompt=24, block_start=24, block_len=16, seed=25),
 }
 
 
@@ -104,7 +112,9 @@ def test_refresh_parity_and_untouched_rows(name):
 
 @pytest.mark.parametrize("name", ["skinny_bf16_d128", "skinny_gqa_d64_scattered",
                                   "tiled64_bf16_ragged", "fp8_tiled_d128", "f32_d64",
-                                  "f32_d128_gqa", "splitk_fp8_h768_m64", "splitk_bf16_h768_d64"])
+                                  "f32_d128_gqa", "splitk_fp8_h768_m64", "splitk_bf16_h768_d64",
+                                  "splitk_gqa_d64", "splitk_d64_129_heads",
+                                  "splitk_d128_33_heads"])
 def test_step_reproduces_full_refresh_bitwise(name):
     """Cached step (prefill on H_prev, refresh of R on H_cur) stores exactly what a full
     refresh on H_cur stores -- on the GPU too, whichever kernel each call picks."""
