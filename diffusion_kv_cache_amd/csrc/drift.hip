@@ -9,9 +9,10 @@
 // drift_track: one workgroup per (b, h).  The K||V rows of the tracked slots are compared in
 // fp64 (16-byte loads, wave butterflies, then the four waves in order).  Then, when this
 // step's mass is given, a radix select over the order-preserving bits of the mass (staged in
-// LDS) finds the k-th largest value in four 8-bit passes; values above it are taken, and of
-// the values equal to it the lowest positions, using two block scans so the set comes out in
-// ascending position order; the tracking buffer is refilled from the current cache.
+// LDS) finds the k-th largest value in up to four 8-bit passes (it stops as soon as every key
+// of the boundary digit is taken); values above it are taken, and of the values equal to it
+// the lowest positions, using a block scan so the set comes out in ascending position order;
+// the tracking buffer is refilled from the current cache.  Scans within a wave are DPP moves.
 // drift_decide: one wave per sequence, any head below gamma.
 #include <math.h>
 
@@ -27,15 +28,24 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts of 1, 2, 4 and 8
+// lanes inside each row of 16, then the running totals of rows 0 and 2 (lanes 15, 47) into
+// rows 1 and 3, then that of rows 0-1 (lane 31) into rows 2 and 3.  Lanes without a source
+// add 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // Block-wide exclusive scan of one value per thread (256 threads), through LDS only.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += o;
-  }
+  const uint32_t inc = wave_inclusive_scan(v);
   if (lane == 63) wsum[wave] = inc;
   lds_barrier();
   uint32_t base = inc - v;
@@ -181,48 +191,49 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
         cnt[e] = hp[255 - 4 * lane - e];
         own += cnt[e];
       }
-      uint32_t inc = own;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(inc, off, kWave);
-        if (lane >= off) inc += o;
-      }
+      const uint32_t inc = wave_inclusive_scan(own);
       const uint32_t exc = inc - own;
-      // the digit holding the rem-th largest candidate, and how many of it are taken
-      uint32_t digit = 0, left = 0, above = exc;
+      // the digit holding the rem-th largest candidate, how many of it are taken, and how
+      // many keys it holds
+      uint32_t digit = 0, left = 0, size = 0, above = exc;
       bool found = false;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (!found && above + cnt[e] >= rem) {
           digit = 255u - 4u * lane - e;
           left = rem - above;
+          size = cnt[e];
           found = true;
         }
         above += cnt[e];
       }
       const int src = __ffsll((unsigned long long)__ballot(exc < rem && rem <= inc)) - 1;
-      digit = __shfl(digit, src, kWave);
-      left = __shfl(left, src, kWave);
+      digit = __builtin_amdgcn_readlane(digit, src);
+      left = __builtin_amdgcn_readlane(left, src);
+      size = __builtin_amdgcn_readlane(size, src);
       prefix |= digit << shift;
       pmask |= 0xffu << shift;
       rem = left;
+      if (left == size) break;                   // the whole digit is taken: the set is known
     }
 
-    // prefix is the k-th largest key; `rem` of the keys equal to it are taken, lowest
-    // positions first.  One scan of (greater, equal) counts over contiguous position ranges
-    // gives every taken key its slot in ascending position order.
+    // prefix holds the leading bytes of the k-th largest key (all four unless the passes
+    // stopped early because every key of the last digit is taken); `rem` of the keys whose
+    // leading bytes equal it are taken, lowest positions first.  One scan of (greater, equal)
+    // counts over contiguous position ranges gives every taken key its slot in ascending
+    // position order.
     const int per = (S + 255) / 256;
     const int j0 = min(S, t * per), j1 = min(S, j0 + per);
     uint32_t gt = 0, eq = 0;
     for (int j = j0; j < j1; ++j) {
-      const uint32_t u = keys[j];
+      const uint32_t u = keys[j] & pmask;
       gt += (u > prefix);
       eq += (u == prefix);
     }
     const uint32_t base = block_exclusive_scan(gt | (eq << 16), wsum);  // S <= 16384
     uint32_t gb = base & 0xffffu, eb = base >> 16;
     for (int j = j0; j < j1; ++j) {
-      const uint32_t u = keys[j];
+      const uint32_t u = keys[j] & pmask;
       if (u > prefix) {
         const uint32_t slot = gb + min(eb, rem);
         if (slot < (uint32_t)k) sTn[slot] = j;
