@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdllm_cache.so")
-SOURCES = ["api.hip", "refresh.hip", "refresh_splitk.hip", "attention.hip", "attention_fwd.hip", "drift.hip"]
+SOURCES = ["api.hip", "refresh.hip", "refresh_splitk.hip", "attention.hip", "attention_fwd.hip",
+           "attention_fused.hip", "drift.hip"]
 ARCH = os.environ.get("DLLM_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -21,12 +22,13 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-# Per-source additions.  The attention forward pass keeps its MFMA accumulators in ordinary
+# Per-source additions.  The attention kernels keep their MFMA accumulators in ordinary
 # VGPRs: with accumulation registers the compiler copied all 64 output accumulators out and
 # back on every key tile (the lazily rescaled softmax state is loop-carried through a branch).
 # NaNs are not honoured there either (no canonicalising max before every fmaxf of a score):
 # scores of finite inputs are finite, and masked keys are -inf, which stays honoured.
-EXTRA = {"attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
+EXTRA = {"attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+         "attention_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
 
 
 def build(verbose: bool = False) -> str:

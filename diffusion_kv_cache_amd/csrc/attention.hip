@@ -432,6 +432,7 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s)
     return hipGetLastError();
   }
   if (a.kind == kCacheFP8) return a.D == 128 ? launch_mfma<kCacheFP8, 128>(a, p, s) : launch_mfma<kCacheFP8, 64>(a, p, s);
+  if (attn_fused_fits(a, p)) return launch_attn_fused(a, s);
   return a.D == 128 ? launch_mfma<kCacheBF16, 128>(a, p, s) : launch_mfma<kCacheBF16, 64>(a, p, s);
 }
 

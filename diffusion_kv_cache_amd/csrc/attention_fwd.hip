@@ -37,18 +37,13 @@ constexpr float kLazy = 8.0f;      // log2 headroom before the running max is mo
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// Per-row chunk swizzles (chunk index XOR f(row)).  K: the 16 rows one MFMA operand read
-// touches hit 16 (D = 128) or 8 (D = 64) distinct chunk slots.  V: the four rows of one
-// transposing read hit distinct 32-byte slot pairs.
+// Per-row chunk swizzle of K tiles (chunk index XOR f(row)): the 16 rows one MFMA operand
+// read touches hit 16 (D = 128) or 8 (D = 64) distinct chunk slots.  V tiles use
+// attn_swz_v, and the key order of the score MFMAs is attn_perm_key (common.hpp).
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
   return D == 128 ? ((r & 3) | (((r >> 3) & 3) << 2)) : ((r & 3) | (((r >> 3) & 1) << 2));
 }
-__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
-
-// Key r of a 32-key tile that MFMA row rho of key-subtile kt reads: the eight score slots of
-// lane group lg are then keys 8 lg .. 8 lg + 7.
-__device__ __forceinline__ int perm_key(int kt, int rho) { return ((rho >> 2) << 3) + (kt << 2) + (rho & 3); }
 
 template <int KIND, int QW, int D>
 struct Cfg {
@@ -143,8 +138,8 @@ __device__ __forceinline__ void fp8_store(const Fp8Stage<KIND, QW, D>& f, char* 
     const u32x4 v0 = e4m3x8_to_bf16x8(f.v[u].x, f.v[u].y), v1 = e4m3x8_to_bf16x8(f.v[u].z, f.v[u].w);
     *(u32x4*)(st + r * C::RB + ((c0 ^ swz_k<D>(r)) << 4)) = k0;
     *(u32x4*)(st + r * C::RB + (((c0 + 1) ^ swz_k<D>(r)) << 4)) = k1;
-    *(u32x4*)(st + C::TILE + r * C::RB + ((c0 ^ swz_v(r)) << 4)) = v0;
-    *(u32x4*)(st + C::TILE + r * C::RB + (((c0 + 1) ^ swz_v(r)) << 4)) = v1;
+    *(u32x4*)(st + C::TILE + r * C::RB + ((c0 ^ attn_swz_v(r)) << 4)) = v0;
+    *(u32x4*)(st + C::TILE + r * C::RB + (((c0 + 1) ^ attn_swz_v(r)) << 4)) = v1;
   }
   if (gt < 2 * kKeys) ((float*)(st + 2 * C::TILE))[gt] = f.sc;
 }
@@ -168,7 +163,7 @@ __device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2
   for (int ds = 0; ds < C::DS; ++ds) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int R = perm_key(kt, l16), ch = ds * 4 + lg;
+      const int R = attn_perm_key(kt, l16), ch = ds * 4 + lg;
       const bf16x8 kf = as_bf16x8(*(const u32x4*)(K + R * C::RB + ((ch ^ swz_k<D>(R)) << 4)));
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) sacc[ct][kt] = mfma_bf16(kf, as_bf16x8(qf[ct][ds]), sacc[ct][kt]);
@@ -240,7 +235,7 @@ __device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2
       const int R = 8 * lg + 4 * hh + (l16 >> 2);
       const int d0 = 16 * dt + 4 * (l16 & 3);
       const int ch = d0 >> 3;
-      const char* addr = V + R * C::RB + ((ch ^ swz_v(R)) << 4) + ((d0 & 4) ? 8 : 0);
+      const char* addr = V + R * C::RB + ((ch ^ attn_swz_v(R)) << 4) + ((d0 & 4) ? 8 : 0);
       h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)addr);
     }
     const u32x4 vw = {(uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16),
@@ -333,7 +328,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     for (int u = 0; u < C::DMA_W; ++u) {
       const int r = (qw + QW * u) * RPI + lane / C::CPR, sc = lane % C::CPR;
       koff[u] = (uint32_t)(r * C::RB + ((sc ^ swz_k<D>(r)) << 4));
-      voff[u] = (uint32_t)(r * C::RB + ((sc ^ swz_v(r)) << 4));
+      voff[u] = (uint32_t)(r * C::RB + ((sc ^ attn_swz_v(r)) << 4));
     }
     const char* kh = kc + head_base * C::RB;
     const char* vh = vc + head_base * C::RB;

@@ -121,6 +121,20 @@ __device__ __forceinline__ void dma_16B(const void* g, const void* lds_block) {
                : "memory");
 }
 
+// ------------------------------------------------------------ attention tile layout ----
+
+// Score tiles are computed transposed, S^T = K Q^T, over 32-key tiles made of two 16-row
+// MFMA subtiles kt.  Key of the tile that MFMA row rho of subtile kt reads: the eight score
+// slots of lane group lg (rows 4 lg .. 4 lg + 3 of both subtiles) are then the consecutive
+// keys 8 lg .. 8 lg + 7.
+__device__ __forceinline__ int attn_perm_key(int kt, int rho) {
+  return ((rho >> 2) << 3) + (kt << 2) + (rho & 3);
+}
+
+// Chunk swizzle (16-byte chunk index XOR f(row)) of a V tile in LDS: the four rows of one
+// transposing read (ds_read_b64_tr_b16) hit distinct 32-byte slot pairs.
+__device__ __forceinline__ int attn_swz_v(int r) { return (r & 3) << 1; }
+
 // ------------------------------------------------------------------ XCD placement -----
 
 // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2): workgroup id goes to

@@ -7,12 +7,13 @@
 // of the 32 most-attended tokens.
 //
 // drift_track: one workgroup per (b, h).  The K||V rows of the tracked slots are compared in
-// fp64 (16-byte loads, wave butterflies, then the four waves in order).  Then, when this
-// step's mass is given, a radix select over the order-preserving bits of the mass (staged in
-// LDS) finds the k-th largest value in up to four 8-bit passes (it stops as soon as every key
-// of the boundary digit is taken); values above it are taken, and of the values equal to it
-// the lowest positions, using a block scan so the set comes out in ascending position order;
-// the tracking buffer is refilled from the current cache.  Scans within a wave are DPP moves.
+// fp64 (16-byte loads, DPP sums over rows of 16 lanes, then the 16 row sums in order).  Then,
+// when this step's mass is given, a radix select over the order-preserving bits of the mass
+// (staged in LDS) finds the k-th largest value in up to four 8-bit passes (it stops as soon as
+// every key of the boundary digit is taken); values above it are taken, and of the values
+// equal to it the lowest positions, placed by ballot counts so the set comes out in ascending
+// position order; the tracking buffer is refilled from the current cache.  Scans within a
+// wave are DPP moves.
 // drift_decide: one wave per sequence, any head below gamma.
 #include <math.h>
 
@@ -22,9 +23,23 @@
 namespace dllm {
 namespace {
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) v += __shfl_xor(v, msk, kWave);
+// One DPP move of both halves of a double (all lanes have a source for the patterns used).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over each row of 16 lanes, left in every lane of the row: partners at lane distance
+// 1 and 2 (quad permutes), then the mirrored half-row and the mirrored row.  Every step adds
+// two operands that are swapped between the partners, so all 16 lanes hold the same bits.
+__device__ __forceinline__ double row_sum_f64(double v) {
+  v += dpp_f64<0xb1>(v);                         // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4e>(v);                         // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);                        // row_half_mirror
+  v += dpp_f64<0x140>(v);                        // row_mirror
   return v;
 }
 
@@ -40,17 +55,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
-}
-
-// Block-wide exclusive scan of one value per thread (256 threads), through LDS only.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t inc = wave_inclusive_scan(v);
-  if (lane == 63) wsum[wave] = inc;
-  lds_barrier();
-  uint32_t base = inc - v;
-  for (int q = 0; q < wave; ++q) base += wsum[q];
-  return base;
 }
 
 // Order-preserving map of fp32 bits to uint32 (larger float -> larger key).
@@ -82,7 +86,8 @@ constexpr int kMassAhead = 4;
 // top-k set and the tracking-buffer refill.  The old set and the buffer are read before any
 // write.  Global loads that do not depend on each other are issued together (old positions,
 // buffer rows, this step's mass), the cache rows of the cosine stay in flight while the
-// top-k runs on LDS, and the refill costs one more round trip.
+// top-k runs on LDS, and the rows of the new set are requested as soon as it is known, so
+// they arrive while the cosine is formed.
 // CH: 16-byte chunks of the tracked K||V rows per thread (k * 2 * D / elements per chunk /
 // 256, rounded up to a power of two).  Chunk indices past the end are clamped to the last
 // chunk, so every load is issued unconditionally, back to back.
@@ -104,11 +109,11 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   const int cs = __builtin_ctz(cpr);
   const int nch = k * 2 * cpr;                   // chunks of the tracked rows
 
-  __shared__ double red[3][4];
+  __shared__ double red[3][16];                  // row sums: [quantity][wave * 4 + row]
   __shared__ int sflag[4];
   __shared__ int32_t sT[64], sTn[64];            // old and new tracked positions
   __shared__ uint32_t hist[4][256];              // one digit histogram per radix pass
-  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t wcnt[2][4];                // per wave: keys above, keys equal
 
   // ---- loads issued together: old positions, buffer rows, the first round of mass ----
   const int told = (t < k) ? T[t] : -1;
@@ -219,31 +224,72 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
 
     // prefix holds the leading bytes of the k-th largest key (all four unless the passes
     // stopped early because every key of the last digit is taken); `rem` of the keys whose
-    // leading bytes equal it are taken, lowest positions first.  One scan of (greater, equal)
-    // counts over contiguous position ranges gives every taken key its slot in ascending
-    // position order.
-    const int per = (S + 255) / 256;
-    const int j0 = min(S, t * per), j1 = min(S, j0 + per);
-    uint32_t gt = 0, eq = 0;
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t u = keys[j] & pmask;
-      gt += (u > prefix);
-      eq += (u == prefix);
+    // leading bytes equal it are taken, lowest positions first.  Wave w walks the positions
+    // [w Q, w Q + Q) 64 at a time: ballots count the keys above and equal, the four waves'
+    // counts are exchanged once, and a second walk places every taken key at its slot in
+    // ascending position order (keys above: #above before it + min(#equal before it, rem);
+    // equal keys: #above before + #equal before, if that is below rem).  Q is a multiple of
+    // 256 so each round reads four keys per lane before any ballot.
+    const int Q = (S + 1023) / 1024 * 256;       // positions per wave, 256 per round
+    const int jb = wave * Q;
+    uint32_t ngt = 0, neq = 0;
+    for (int c = 0; c < Q; c += 256) {
+      uint32_t u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = keys[min(jb + c + 64 * e + lane, S - 1)] & pmask;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = jb + c + 64 * e + lane < S;
+        ngt += (uint32_t)__builtin_popcountll(__ballot(in && u[e] > prefix));
+        neq += (uint32_t)__builtin_popcountll(__ballot(in && u[e] == prefix));
+      }
     }
-    const uint32_t base = block_exclusive_scan(gt | (eq << 16), wsum);  // S <= 16384
-    uint32_t gb = base & 0xffffu, eb = base >> 16;
-    for (int j = j0; j < j1; ++j) {
-      const uint32_t u = keys[j] & pmask;
-      if (u > prefix) {
-        const uint32_t slot = gb + min(eb, rem);
-        if (slot < (uint32_t)k) sTn[slot] = j;
-        ++gb;
-      } else if (u == prefix) {
-        if (eb < rem && gb + eb < (uint32_t)k) sTn[gb + eb] = j;
-        ++eb;
+    if (lane == 0) {
+      wcnt[0][wave] = ngt;
+      wcnt[1][wave] = neq;
+    }
+    lds_barrier();
+    uint32_t gb = 0, eb = 0;
+    for (int q = 0; q < wave; ++q) {
+      gb += wcnt[0][q];
+      eb += wcnt[1][q];
+    }
+    for (int c = 0; c < Q; c += 256) {
+      uint32_t u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = keys[min(jb + c + 64 * e + lane, S - 1)] & pmask;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = jb + c + 64 * e + lane;
+        const bool in = j < S, above = in && u[e] > prefix, equal = in && u[e] == prefix;
+        const unsigned long long ba = __ballot(above), be = __ballot(equal);
+        const uint32_t ga = gb + __builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(ba >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ba, 0u));
+        const uint32_t ge = eb + __builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+        if (above) {
+          const uint32_t slot = ga + min(ge, rem);
+          if (slot < (uint32_t)k) sTn[slot] = j;
+        } else if (equal && ge < rem && ga + ge < (uint32_t)k) {
+          sTn[ga + ge] = j;
+        }
+        gb += (uint32_t)__builtin_popcountll(ba);
+        eb += (uint32_t)__builtin_popcountll(be);
       }
     }
     for (int sl = (int)want + t; sl < k; sl += 256) sTn[sl] = -1;
+    lds_barrier();
+  }
+
+  // ---- rows of the new set: in flight during the cosine (row 0 without an update, so the
+  // loads need no branch) ----
+  u32x4 un[kMaxChunks];
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = min(t + 256 * i, nch - 1);
+    const int slot = c >> (cs + 1), part = (c >> cs) & 1, d0 = (c & (cpr - 1)) * EPC;
+    const int j = do_update ? sTn[slot] : 0;
+    un[i] = *(const u32x4*)((part ? vc : kc) + (head_base + (j >= 0 ? j : 0)) * D + d0);
   }
 
   // ---- sigma over the previous tracked set (fp64) ----
@@ -267,27 +313,27 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
     }
   }
   const int valid_slot = (t < k) ? (told >= 0 && told < S) : 0;
-  uw = wave_sum_f64(uw);
-  uu = wave_sum_f64(uu);
-  ww = wave_sum_f64(ww);
+  uw = row_sum_f64(uw);
+  uu = row_sum_f64(uu);
+  ww = row_sum_f64(ww);
   const int wflags = (__any(neq) ? 1 : 0) | (__any(valid_slot) ? 2 : 0);
-  if (lane == 0) {
-    red[0][wave] = uw;
-    red[1][wave] = uu;
-    red[2][wave] = ww;
-    sflag[wave] = wflags;
+  if ((lane & 15) == 0) {
+    red[0][wave * 4 + (lane >> 4)] = uw;
+    red[1][wave * 4 + (lane >> 4)] = uu;
+    red[2][wave * 4 + (lane >> 4)] = ww;
   }
-  __syncthreads();
+  if (lane == 0) sflag[wave] = wflags;
+  lds_barrier();
   float sig = 1.f;                               // thread 0: this head's sigma
   if (t == 0) {
     double UW = 0.0, UU = 0.0, WW = 0.0;
     int F = 0;
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 16; ++q) {
       UW += red[0][q];
       UU += red[1][q];
       WW += red[2][q];
-      F |= sflag[q];
     }
+    for (int q = 0; q < 4; ++q) F |= sflag[q];
     double sigma;
     if (!(F & 2)) sigma = 1.0;
     else {
@@ -305,21 +351,15 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   }
 
   // ---- new set out, and the tracking buffer refilled with its K||V rows ----
-  // (all loads first, then the stores, which the compiler cannot prove do not alias them)
-#pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = min(t + 256 * i, nch - 1);
-    const int slot = c >> (cs + 1), part = (c >> cs) & 1, d0 = (c & (cpr - 1)) * EPC;
-    const int j = sTn[slot];
-    ub[i] = *(const u32x4*)((part ? vc : kc) + (head_base + (j >= 0 ? j : 0)) * D + d0);
-    if (j < 0) ub[i] = u32x4{0u, 0u, 0u, 0u};    // empty slot (S < k): zero row
-  }
   if (t == 0) a.sigma[(size_t)b * a.Hq + h] = sig;
   for (int sl = t; sl < k; sl += 256) T[sl] = sTn[sl];
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = t + 256 * i;
-    if (c < nch) *(u32x4*)(buf + (size_t)c * EPC) = ub[i];
+    if (c < nch) {
+      const bool empty = sTn[c >> (cs + 1)] < 0;   // empty slot (S < k): zero row
+      *(u32x4*)(buf + (size_t)c * EPC) = empty ? u32x4{0u, 0u, 0u, 0u} : un[i];
+    }
   }
 }
 

@@ -62,6 +62,11 @@ struct AttnPlan {
 AttnPlan plan_attention(int B, int n, int Hq, int Hkv, int S, int D, int act, int kind);
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
+// Attention and column mass in one launch (one workgroup per (b, KV head)): taken when the
+// mass is requested for a bf16 cache, one query head per KV head, n <= 32, and the batch's
+// heads alone fill the GPU (the plan does not split keys).
+bool attn_fused_fits(const AttnArgs& a, const AttnPlan& p);
+hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t s);
 // Forward pass of the MFMA attention (bf16 queries; bf16 or FP8 cache), one launch.
 template <int KIND, int D>
 hipError_t launch_attn_fwd(const AttnArgs& a, const AttnPlan& p, int qtiles, hipStream_t s);

@@ -212,6 +212,15 @@ ATT_CASES = {
                          prompt=260, cache="fp8", block_start=263, block_len=20, seed=43),
     "fp8_d64_g8_qt128": C(batch=1, hidden=256, q_heads=8, kv_heads=1, head_dim=64, seq=300,
                           prompt=150, cache="fp8", block_start=151, block_len=70, seed=44),
+    # one query head per KV head, n <= 32, heads enough not to split keys (B * Hkv >= 512):
+    # attention and mass in one launch -- ragged last key tile, a wave without tiles (3 tiles
+    # for 4 waves), a single key
+    "fused_d128_ragged": C(batch=16, hidden=256, q_heads=32, kv_heads=32, head_dim=128, seq=300,
+                           prompt=150, block_start=151, block_len=20, seed=46),
+    "fused_d64_three_tiles": C(batch=16, hidden=256, q_heads=32, kv_heads=32, head_dim=64,
+                               seq=70, prompt=30, block_start=32, block_len=32, seed=47),
+    "fused_s1": C(batch=16, hidden=256, q_heads=32, kv_heads=32, head_dim=64, seq=1, prompt=0,
+                  block_start=0, block_len=1, seed=48),
     # n * G = 8800 packed rows: more log-sum-exp values than the mass pass stages in LDS
     "bf16_mass_rows_over_lds": C(batch=1, hidden=256, q_heads=8, kv_heads=1, head_dim=64,
                                  seq=1100, prompt=0, block_start=0, block_len=1100, seed=45),
@@ -279,6 +288,10 @@ def _drift_inputs(p, seed):
         buf = synth.round_to_bf16(buf)
     mass = synth.uniform_mass(rng, (B, Hq, S), ties=S // 5)
     mass[0, 1, :] = 0.25                                   # all tied: lowest positions win
+    if S > k:                                              # exactly k values in [4, 8): the
+        big = rng.choice(S, size=k, replace=False)         # leading byte alone decides
+        mass[1, 0, :] = rng.uniform(0.0, 1.0, S).astype(np.float32)
+        mass[1, 0, big] = rng.uniform(4.0, 8.0, k).astype(np.float32)
     return kc, vc, T, buf, mass
 
 
