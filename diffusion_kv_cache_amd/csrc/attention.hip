@@ -18,6 +18,86 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kKeys = 32;          // keys per tile
 
+// Merged state of packed row pr0 from the split partials, in split order (the same arithmetic
+// as attn_merge): running max mm and normaliser L.  Up to eight splits are loaded together
+// (clamped, unconditional loads) before any arithmetic, so the row costs one round trip.
+constexpr int kMergeBatch = 8;
+
+__device__ __forceinline__ void merged_ml(const float* ml, size_t nrows_all, size_t pr0, int splits,
+                                          float& mm, float& L) {
+  if (splits <= kMergeBatch) {
+    float ms[kMergeBatch], ls[kMergeBatch];
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e) {
+      const float2 v = *(const float2*)(ml + ((size_t)min(e, splits - 1) * nrows_all + pr0) * 2);
+      ms[e] = v.x;
+      ls[e] = v.y;
+    }
+    mm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e)
+      if (e < splits) mm = fmaxf(mm, ms[e]);
+    L = 0.f;
+#pragma unroll
+    for (int e = 0; e < kMergeBatch; ++e)
+      if (e < splits) L += ls[e] * ((ms[e] == -INFINITY) ? 0.f : exp2f(ms[e] - mm));
+    return;
+  }
+  mm = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp) mm = fmaxf(mm, ml[((size_t)sp * nrows_all + pr0) * 2]);
+  L = 0.f;
+  for (int sp = 0; sp < splits; ++sp) {
+    const size_t pr = (size_t)sp * nrows_all + pr0;
+    const float ms = ml[pr * 2], ls = ml[pr * 2 + 1];
+    L += ls * ((ms == -INFINITY) ? 0.f : exp2f(ms - mm));
+  }
+}
+
+// Merged state and unnormalised output (lane's columns lane + 64 e) of packed row pr0, in
+// split order; up to eight splits' loads are issued together before the arithmetic.
+template <int D>
+__device__ __forceinline__ void merge_row(const float* part, const float* ml, size_t nrows_all, size_t pr0,
+                                          int splits, int lane, float (&o)[D / 64], float& mm, float& L) {
+  constexpr int PER = D / 64;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = 0.f;
+  mm = -INFINITY;
+  L = 0.f;
+  if (splits <= kMergeBatch) {
+    float ms[kMergeBatch], ls[kMergeBatch], po[kMergeBatch][PER];
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q) {
+      const size_t pr = (size_t)min(q, splits - 1) * nrows_all + pr0;
+      const float2 v = *(const float2*)(ml + pr * 2);
+      ms[q] = v.x;
+      ls[q] = v.y;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) po[q][e] = part[pr * D + lane + 64 * e];
+    }
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q)
+      if (q < splits) mm = fmaxf(mm, ms[q]);
+#pragma unroll
+    for (int q = 0; q < kMergeBatch; ++q) {
+      if (q >= splits) continue;
+      const float wgt = (ms[q] == -INFINITY) ? 0.f : exp2f(ms[q] - mm);
+      L += ls[q] * wgt;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] += po[q][e] * wgt;
+    }
+    return;
+  }
+  for (int sp = 0; sp < splits; ++sp) mm = fmaxf(mm, ml[((size_t)sp * nrows_all + pr0) * 2]);
+  for (int sp = 0; sp < splits; ++sp) {
+    const size_t pr = (size_t)sp * nrows_all + pr0;
+    const float ms = ml[pr * 2], ls = ml[pr * 2 + 1];
+    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - mm);
+    L += ls * wgt;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] += part[pr * D + lane + 64 * e] * wgt;
+  }
+}
+
 // Combine split partial states in split order: one wave per packed query row.
 template <typename OutT, int D>
 __global__ __launch_bounds__(64) void attn_merge(AttnArgs a, int splits) {
@@ -28,21 +108,9 @@ __global__ __launch_bounds__(64) void attn_merge(AttnArgs a, int splits) {
   const int bg = (int)(pr0 / rows), r = (int)(pr0 % rows);
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const float* ml = a.part + (size_t)splits * nrows_all * D;
-  float mm = -INFINITY;
-  for (int sp = 0; sp < splits; ++sp) mm = fmaxf(mm, ml[((size_t)sp * nrows_all + pr0) * 2]);
-  float L = 0.f;
   constexpr int PER = D / 64;
-  float o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const size_t pr = (size_t)sp * nrows_all + pr0;
-    const float ms = ml[pr * 2], ls = ml[pr * 2 + 1];
-    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - mm);
-    L += ls * wgt;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] += a.part[pr * D + threadIdx.x + 64 * e] * wgt;
-  }
+  float mm, L, o[PER];
+  merge_row<D>(a.part, ml, nrows_all, pr0, splits, threadIdx.x, o, mm, L);
   const int i = r / G, h = g * G + r % G;
   OutT* out = (OutT*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
   const float inv = 1.f / L;
@@ -55,20 +123,6 @@ __global__ __launch_bounds__(64) void attn_merge(AttnArgs a, int splits) {
   if (threadIdx.x == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = (mm + log2f(L)) * kLn2;
 }
 
-// Merged state of packed row pr0 from the split partials, in split order (the same arithmetic
-// as attn_merge): running max mm and normaliser L.
-__device__ __forceinline__ void merged_ml(const float* ml, size_t nrows_all, size_t pr0, int splits,
-                                          float& mm, float& L) {
-  mm = -INFINITY;
-  for (int sp = 0; sp < splits; ++sp) mm = fmaxf(mm, ml[((size_t)sp * nrows_all + pr0) * 2]);
-  L = 0.f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const size_t pr = (size_t)sp * nrows_all + pr0;
-    const float ms = ml[pr * 2], ls = ml[pr * 2 + 1];
-    L += ls * ((ms == -INFINITY) ? 0.f : exp2f(ms - mm));
-  }
-}
-
 // Column attention mass, second pass after the log-sum-exp is known:
 //   mass[b, h, j] = sum_i exp(<q_i, k_j> * scale - lse_i).
 // One workgroup per (b, KV head g) and 128 keys, so each K row is read once for all G query
@@ -76,12 +130,12 @@ __device__ __forceinline__ void merged_ml(const float* ml, size_t nrows_all, siz
 // group's queries stream through an LDS ring in tiles of 32 rows of one head (DMA, three
 // stages, shared by the four waves), and every row's log-sum-exp sits in LDS.  Lane (l16, lg)
 // sums query column l16 over the tiles in order; the 16 lanes of a key are added at the end
-// of each head in a fixed butterfly order.
+// of each head in a fixed DPP order (row16_sum).
 //
-// MERGE (the attention was split over keys): the kernel first forms every packed row's
-// log-sum-exp from the split partials, the workgroups of key chunk 0 write it, and the rows'
-// outputs are merged here too (rows dealt round-robin over the key chunks), so no separate
-// merge launch is needed.
+// MERGE (the attention was split over keys): the rows' outputs are merged here (rows dealt
+// round-robin over the key chunks), first thing after the prologue's loads are issued, so no
+// separate merge launch is needed; then every packed row's log-sum-exp is formed from the
+// split partials and the workgroups of key chunk 0 write it.
 constexpr int kMassQRows = 32;                   // query rows per ring tile
 constexpr int kMassNst = 3;                      // ring stages
 // Largest packed-row count (n * G) whose log-sum-exp the mass pass stages in LDS (32 KB);
@@ -169,9 +223,25 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
     }
   }
 
-  // log-sum-exp of every packed row r = i * G + hh, log2 domain
   const size_t nrows_all = (size_t)a.B * a.Hkv * rows;
   const float* ml = a.part + (size_t)splits * nrows_all * D;
+  // The rows' outputs are merged first: their loads then travel with the prologue's.
+  if constexpr (MERGE) {
+    // outputs of the rows r = kchunk + nkc * (4 it + wave), one wave per row
+    constexpr int PER = D / 64;
+    for (int r = kchunk + nkc * wave; r < rows; r += 4 * nkc) {
+      const size_t pr0 = (size_t)bg * rows + r;
+      float mm, L, o[PER];
+      merge_row<D>(a.part, ml, nrows_all, pr0, splits, lane, o, mm, L);
+      const int i = r / G, h = g * G + r % G;
+      bf16_t* out = (bf16_t*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) out[lane + 64 * e] = f32_to_bf16(o[e] * inv);
+    }
+  }
+
+  // log-sum-exp of every packed row r = i * G + hh, log2 domain
   for (int r = t; LDS_LSE && r < rows; r += 256) {
     const int i = r / G, h = g * G + r % G;
     if constexpr (MERGE) {
@@ -228,11 +298,7 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float x = acc[kt][v];
-          x += __shfl_xor(x, 1, kWave);
-          x += __shfl_xor(x, 2, kWave);
-          x += __shfl_xor(x, 4, kWave);
-          x += __shfl_xor(x, 8, kWave);
+          const float x = row16_sum(acc[kt][v]);
           const int key = key0 + kt * 16 + lg * 4 + v;
           if (l16 == 0 && key < a.S) a.mass[((size_t)b * a.Hq + h) * a.S + key] = x;
           acc[kt][v] = 0.f;
@@ -240,30 +306,6 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
     }
   }
 
-  if constexpr (MERGE) {
-    // outputs of the rows r = kchunk + nkc * (4 it + wave), one wave per row
-    constexpr int PER = D / 64;
-    for (int r = kchunk + nkc * wave; r < rows; r += 4 * nkc) {
-      const size_t pr0 = (size_t)bg * rows + r;
-      float mm, L;
-      merged_ml(ml, nrows_all, pr0, splits, mm, L);
-      float o[PER];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) o[e] = 0.f;
-      for (int sp = 0; sp < splits; ++sp) {
-        const size_t pr = (size_t)sp * nrows_all + pr0;
-        const float ms = ml[pr * 2];
-        const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - mm);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] += a.part[pr * D + lane + 64 * e] * wgt;
-      }
-      const int i = r / G, h = g * G + r % G;
-      bf16_t* out = (bf16_t*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
-      const float inv = 1.f / L;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) out[lane + 64 * e] = f32_to_bf16(o[e] * inv);
-    }
-  }
 }
 
 // ---------------------------------------------------------------- fp32 (small shapes) ---

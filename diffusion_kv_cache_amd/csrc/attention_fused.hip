@@ -129,16 +129,6 @@ __device__ __forceinline__ void tile_stats(const Tile<D>& k, char* kst, const u3
   }
 }
 
-// Sum over the 16 lanes of a row, left in every lane of the row (DPP: partners at distance 1
-// and 2, then the mirrored half-row and the mirrored row).
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
-  return x;
-}
-
 // Pass 2 on one tile: exact probabilities, the tile's 32 column masses, and O^T += V^T P^T.
 template <int D, bool FULL>
 __device__ __forceinline__ void tile_out(const Tile<D>& k, const Tile<D>& v, char* kst, char* vst,

@@ -177,6 +177,18 @@ __device__ __forceinline__ float sum_across_rows(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Sum over the 16 lanes of a row (lanes 16 r .. 16 r + 15), left in every lane of the row:
+// DPP partners at distance 1 and 2 (quad permutes), then the mirrored half-row and the
+// mirrored row.  Each step adds two operands that are swapped between the partners, so all
+// 16 lanes end with the same bits.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xf, 0xf, false));
+  return x;
+}
+
 // ------------------------------------------------------------------------ rotary --------
 
 // Turns of rotary pair i: t_i = base^(-2i/D) / (2 pi), split into two floats (hi + lo).
