@@ -5,7 +5,7 @@
 //     of the gathered hidden rows is staged once in LDS with coalesced 16-byte loads; each of
 //     the eight waves streams 16 W rows of that partition from global memory with a deep
 //     register prefetch and chains 16x16x32 MFMAs over the partition in ascending k.  The
-//     partition's fp32 result goes to the workspace.
+//     partition's fp32 tile goes to the workspace as whole rows (staged in LDS).
 //   refresh_reduce: adds the eight partitions in order ((0 + P0) + P1) + ... + P7 -- exactly the
 //     arithmetic of the tiled kernel -- rotates the Q and K pairs (i, i + D/2), and writes Q,
 //     K and V rows (bf16, or per-row FP8 with its fp32 scale).
@@ -13,6 +13,8 @@
 // What it computes: Flash-dLLM news summary (skillfed.io), memory paragraph -- projection,
 // RoPE and cache write of the refreshed rows; LaCache (gist.science), Technical Summary,
 // Methodology 1 (RoPECache: post-projection, post-RoPE states) and 2 (1 x 128 FP8 groups).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,6 +22,7 @@ namespace dllm {
 namespace {
 
 constexpr int kPrefetch = 8;   // k-steps of W in flight per wave
+constexpr int kPartLd = 132;   // floats per staged partial row (128 + 4: no bank conflicts)
 
 // Three workgroups per CU (6 waves per SIMD) keep all 768 workgroups of a 4096-hidden,
 // 12288-column step resident at once.
@@ -38,9 +41,8 @@ void refresh_partial(RefreshArgs a, float* part) {
   // the 32 row positions, then the gathered A slice global -> LDS by DMA (each lane fetches
   // the source chunk that lands, swizzled, at its LDS slot).  Rows past M gather the last
   // valid row: their accumulators are never stored.
-  const int col = blockIdx.y * 128 + wave * 16 + l16;
-  const bool col_ok = col < N;
-  const bf16_t* wr = (const bf16_t*)a.w + (size_t)(col_ok ? col : N - 1) * a.H + kb + lg * 8;
+  const int col = blockIdx.y * 128 + wave * 16 + l16;  // columns past N compute, not stored
+  const bf16_t* wr = (const bf16_t*)a.w + (size_t)min(col, N - 1) * a.H + kb + lg * 8;
   const int steps = Lp / 32;
   u32x4 wv[kPrefetch];
 #pragma unroll
@@ -87,14 +89,22 @@ void refresh_partial(RefreshArgs a, float* part) {
   for (int u = 0; u < kPrefetch; ++u)
     if (s0 + u < steps) step(s0 + u, wv[u]);
 
-  if (!col_ok) return;
+  // The 32 x 128 partial tile goes out as whole rows: staged in LDS (over the A slice, which
+  // every wave is done reading), then 16-byte stores of 512-byte row segments.
+  __syncthreads();
+  float* T = (float*)As;                         // [32][kPartLd]
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = m0 + rt * 16 + lg * 4 + v;
-      if (m < a.M) part[((size_t)p * a.M + m) * N + col] = acc[rt][v];
-    }
+    for (int v = 0; v < 4; ++v) T[(rt * 16 + lg * 4 + v) * kPartLd + wave * 16 + l16] = acc[rt][v];
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int id = u * 512 + t, r = id >> 5, c4 = (id & 31) * 4;
+    const int m = m0 + r, cc = blockIdx.y * 128 + c4;
+    if (m < a.M && cc < N)
+      *(float4*)(part + ((size_t)p * a.M + m) * N + cc) = *(const float4*)(T + r * kPartLd + c4);
+  }
 }
 
 // One 16-lane group per (row, head): lane L of the group owns the rotary pairs
@@ -195,7 +205,8 @@ size_t splitk_workspace_bytes(int M, int N) { return (size_t)kKSplit * M * N * s
 hipError_t launch_refresh_splitk(const RefreshArgs& a, float* part, hipStream_t s) {
   const int N = (a.Hq + 2 * a.Hkv) * a.D;
   dim3 grid(kKSplit, (N + 127) / 128, (a.M + 31) / 32);
-  const size_t lds = (size_t)32 * (a.H / kKSplit) * sizeof(bf16_t);
+  const size_t lds = std::max((size_t)32 * (a.H / kKSplit) * sizeof(bf16_t),
+                              (size_t)32 * kPartLd * sizeof(float));
   refresh_partial<<<grid, 512, lds, s>>>(a, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
