@@ -338,6 +338,10 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
       if (st < iters)
         dma_tile<KIND, QW, D>(ring_kw + st * C::STAGE, kh, vh, kbeg + (st * KW + kw) * kKeys, kbeg,
                               kend, qw, lane, koff, voff);
+    // The query operands (ordinary loads, issued first) are complete here as far as the
+    // compiler can tell: otherwise it keeps waiting for them inside the loop, on a counter
+    // that also counts the tile transfers in flight, and drains the ring on every tile.
+    DLLM_WAIT_VMCNT(0);
     for (int it = 0; it < iters; ++it) {
       // this wave's transfers for tile `it` are done once at most those of the later tiles
       // already issued are outstanding

@@ -24,19 +24,14 @@
 namespace dllm {
 namespace {
 
-__device__ __forceinline__ size_t hidden_row_offset(const RefreshArgs& a, int m) {
-  const int b = m / a.n;
-  return ((size_t)b * a.S + (size_t)a.idx[m]) * (size_t)a.H;
-}
-
-// Destination of output row m (= b * n + i) of head slot j; element type chosen by caller.
-__device__ __forceinline__ size_t out_row_offset(const RefreshArgs& a, int m, int j, int& which) {
+// Destination of output row m (= b * n + i, position pos) of head slot j; element type chosen
+// by caller.
+__device__ __forceinline__ size_t out_row_offset(const RefreshArgs& a, int m, int j, int pos, int& which) {
   const int b = m / a.n;
   if (j < a.Hq) {
     which = 0;
     return ((size_t)m * a.Hq + j) * (size_t)a.D;
   }
-  const int pos = a.idx[m];
   const int g = (j < a.Hq + a.Hkv) ? j - a.Hq : j - a.Hq - a.Hkv;
   which = (j < a.Hq + a.Hkv) ? 1 : 2;
   return (((size_t)b * a.Hkv + g) * a.S + pos) * (size_t)a.D;
@@ -59,6 +54,18 @@ __device__ __forceinline__ void tile_epilogue(const RefreshArgs& a,
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, lg = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
+  // Positions of the rows this lane rotates, and of the rows this thread stores: all loaded
+  // together (clamped, unconditional), one round trip instead of one per row.
+  constexpr int TPR = D / 8;                     // threads per stored row
+  constexpr int SPT = TM / (NT / TPR);           // stored rows per thread
+  int rpos[RT][4], spos[SPT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) rpos[rt][v] = a.idx[min(m0 + wm * (TM / WM) + rt * 16 + lg * 4 + v, a.M - 1)];
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) spos[k] = a.idx[min(m0 + t / TPR + k * (NT / TPR), a.M - 1)];
+
   // Rotary embedding of Q and K heads, in registers.
   if (j < a.Hq + a.Hkv) {
     float hi[CH], lo[CH];
@@ -68,8 +75,7 @@ __device__ __forceinline__ void tile_epilogue(const RefreshArgs& a,
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = m0 + wm * (TM / WM) + rt * 16 + lg * 4 + v;
-        const int pos = (m < a.M) ? a.idx[m] : 0;
+        const int pos = rpos[rt][v];
 #pragma unroll
         for (int sb = 0; sb < CH; ++sb) {
           float s, c;
@@ -94,9 +100,10 @@ __device__ __forceinline__ void tile_epilogue(const RefreshArgs& a,
   __syncthreads();
 
   // Whole rows out: D/8 threads per row, eight values each.
-  constexpr int TPR = D / 8;
   const int cpos = (t % TPR) * 8;
-  for (int r = t / TPR; r < TM; r += NT / TPR) {
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const int r = t / TPR + k * (NT / TPR);
     const int m = m0 + r;
     if (m >= a.M) continue;  // uniform over the TPR threads of a row
     float x[8];
@@ -105,7 +112,7 @@ __device__ __forceinline__ void tile_epilogue(const RefreshArgs& a,
     x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
     x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
     int which;
-    const size_t off = out_row_offset(a, m, j, which);
+    const size_t off = out_row_offset(a, m, j, spos[k], which);
     if (which == 0 || KIND != kCacheFP8) {
       void* base = which == 0 ? a.q_out : which == 1 ? a.kc : a.vc;
       if constexpr (BF) {
@@ -178,12 +185,15 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
   // Global sources of this thread's chunks (fixed rows; k advances).
   const T* asrc[A_PER_T];
   bool aval[A_PER_T];
+  int prow[A_PER_T];
+#pragma unroll
+  for (int u = 0; u < A_PER_T; ++u) prow[u] = a.idx[min(m0 + t / BKC + u * (256 / BKC), a.M - 1)];
 #pragma unroll
   for (int u = 0; u < A_PER_T; ++u) {
     const int r = t / BKC + u * (256 / BKC);
-    const int m = m0 + r;
-    aval[u] = m < a.M;
-    asrc[u] = hid + hidden_row_offset(a, aval[u] ? m : 0) + cchunk * EPC;
+    const int m = min(m0 + r, a.M - 1);
+    aval[u] = m0 + r < a.M;
+    asrc[u] = hid + ((size_t)(m / a.n) * a.S + prow[u]) * a.H + cchunk * EPC;
   }
   const T* wsrc[W_PER_T];
 #pragma unroll
@@ -328,16 +338,25 @@ __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
   const int j = blockIdx.x;
   const int m0 = blockIdx.y * TM;
 
-  // Source of this lane's chunk for each of the wave's NI DMA instructions (k = 0).
+  // Source of this lane's chunk for each of the wave's NI DMA instructions (k = 0).  The row
+  // positions are loaded for every instruction (clamped, unconditional) before any address is
+  // formed, so they cost one round trip.
   const bf16_t* src[NI];
+  int mrow[NI], prow[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = min((wave * NI + i) * RPI + lane / BKC, TM - 1);
+    mrow[i] = min(m0 + r, a.M - 1);              // rows past M: never stored
+    prow[i] = a.idx[mrow[i]];
+  }
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int gi = wave * NI + i;
     const int cp = lane % BKC;
     if (gi < IA) {
       const int r = gi * RPI + lane / BKC;
-      const int m = min(m0 + r, a.M - 1);        // rows past M: never stored
-      src[i] = (const bf16_t*)a.hidden + hidden_row_offset(a, m) + (cp ^ (r & (BKC - 1))) * EPC;
+      const size_t hrow = (size_t)(mrow[i] / a.n) * a.S + prow[i];
+      src[i] = (const bf16_t*)a.hidden + hrow * a.H + (cp ^ (r & (BKC - 1))) * EPC;
     } else {
       const int c = (gi - IA) * RPI + lane / BKC;
       src[i] = (const bf16_t*)a.w + (size_t)(j * D + c) * a.H + (cp ^ (c & (BKC - 1))) * EPC;
