@@ -303,7 +303,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="layer instances to rotate (0: auto)")
-    ap.add_argument("--event-every", type=int, default=5,
+    ap.add_argument("--event-every", type=int, default=10,
                     help="record per-call events in every N-th timed step (at least one step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
