@@ -62,12 +62,13 @@ struct Cfg {
   static constexpr int NST = (KIND == kCacheFP8) ? 2 : (QW == 4 ? 4 : QW == 2 ? 3 : 2);
 };
 
-// bf16: this wave's share of the DMA blocks of one tile (K and V) into stage memory `st`.
-// koff / voff: this lane's byte offsets within a tile (row r of block blk, swizzled chunk),
-// fixed for the whole loop; a full tile then costs one address add per block.  The partial
-// last tile clamps rows past the end to the split's first row (their scores are masked).
+// bf16: this wave's share of the DMA blocks of one tile (K and V) into the stage at LDS
+// address st (wave-uniform).  koff / voff: this lane's byte offsets within a tile (row r of
+// block blk, swizzled chunk), fixed for the whole loop; a full tile's base address is
+// wave-uniform (scalar registers), so a transfer costs no vector arithmetic.  The partial last
+// tile clamps rows past the end to the split's first row (their scores are masked).
 template <int KIND, int QW, int D>
-__device__ __forceinline__ void dma_tile(char* st, const char* kh, const char* vh, int key0, int kbeg,
+__device__ __forceinline__ void dma_tile(uint32_t st, const char* kh, const char* vh, int key0, int kbeg,
                                          int kend, int qw, int lane, const uint32_t* koff,
                                          const uint32_t* voff) {
   using C = Cfg<KIND, QW, D>;
@@ -77,9 +78,9 @@ __device__ __forceinline__ void dma_tile(char* st, const char* kh, const char* v
     const char* vt = vh + (size_t)key0 * C::RB;
 #pragma unroll
     for (int u = 0; u < C::DMA_W; ++u) {
-      const int blk = qw + QW * u;
-      dma_16B(kt + koff[u], st + blk * 1024);
-      dma_16B(vt + voff[u], st + C::TILE + blk * 1024);
+      const uint32_t blk = (uint32_t)(qw + QW * u) * 1024u;
+      dma_16B_sbase(koff[u], kt, st + blk);
+      dma_16B_sbase(voff[u], vt, st + C::TILE + blk);
     }
   } else {
 #pragma unroll
@@ -87,9 +88,9 @@ __device__ __forceinline__ void dma_tile(char* st, const char* kh, const char* v
       const int blk = qw + QW * u;
       const int r = blk * RPI + lane / C::CPR;
       const int key = key0 + r;
-      const size_t rowb = (size_t)((key < kend ? key : kbeg) - r) * C::RB;
-      dma_16B(kh + rowb + koff[u], st + blk * 1024);
-      dma_16B(vh + rowb + voff[u], st + C::TILE + blk * 1024);
+      const uint32_t rowb = (uint32_t)((key < kend ? key : kbeg) - r) * C::RB;
+      dma_16B_sbase(rowb + koff[u], kh, st + blk * 1024);
+      dma_16B_sbase(rowb + voff[u], vh, st + C::TILE + blk * 1024);
     }
   }
 }
@@ -261,7 +262,8 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
 
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int qw = wave % QW, kw = wave / QW;
+  // wave-uniform indices (scalar registers: the DMA stage addresses derive from them)
+  const int qw = __builtin_amdgcn_readfirstlane(wave % QW), kw = __builtin_amdgcn_readfirstlane(wave / QW);
   const int gt = qw * 64 + lane;
 
   // All query tiles and key splits of one (b, KV head) run on one XCD: its K/V rows are
@@ -332,11 +334,12 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     }
     const char* kh = kc + head_base * C::RB;
     const char* vh = vc + head_base * C::RB;
+    const uint32_t ring_st = lds_addr(ring) + (uint32_t)(kw * NST * C::STAGE);   // this group's ring
     // prologue: the first NST - 1 tiles of this key group
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
       if (st < iters)
-        dma_tile<KIND, QW, D>(ring_kw + st * C::STAGE, kh, vh, kbeg + (st * KW + kw) * kKeys, kbeg,
+        dma_tile<KIND, QW, D>(ring_st + st * C::STAGE, kh, vh, kbeg + (st * KW + kw) * kKeys, kbeg,
                               kend, qw, lane, koff, voff);
     // The query operands (ordinary loads, issued first) are complete here as far as the
     // compiler can tell: otherwise it keeps waiting for them inside the loop, on a counter
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
       else DLLM_WAIT_VMCNT(0);
       lds_barrier();                             // tile `it` visible; slot of it - 1 free
       if (it + NST - 1 < iters)
-        dma_tile<KIND, QW, D>(ring_kw + ((it + NST - 1) % NST) * C::STAGE, kh, vh,
+        dma_tile<KIND, QW, D>(ring_st + ((it + NST - 1) % NST) * C::STAGE, kh, vh,
                               kbeg + ((it + NST - 1) * KW + kw) * kKeys, kbeg, kend, qw, lane, koff, voff);
       const int tile = it * KW + kw;
       if (tile < ntiles)

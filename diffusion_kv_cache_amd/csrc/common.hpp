@@ -121,6 +121,22 @@ __device__ __forceinline__ void dma_16B(const void* g, const void* lds_block) {
                : "memory");
 }
 
+// LDS byte address of a __shared__ object (a constant for a named array; no null check).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One LDS-DMA instruction with a wave-uniform 64-bit base in scalar registers and a 32-bit
+// per-lane byte offset: lane l copies 16 bytes from sbase + voff to lds + 16 l.  sbase and lds
+// must be wave-uniform (scalar registers); waiting is the caller's, as for dma_16B.
+__device__ __forceinline__ void dma_16B_sbase(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
+}
+
 // ------------------------------------------------------------ attention tile layout ----
 
 // Score tiles are computed transposed, S^T = K Q^T, over 32-key tiles made of two 16-row
