@@ -180,16 +180,19 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
   const int ntq = (a.n + kMassQRows - 1) / kMassQRows;
   const int iters = G * ntq;
   const bf16_t* q = (const bf16_t*)a.q;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform: scalar DMA bases
+  const uint32_t ring_lds = lds_addr(dyn);
   auto issue = [&](int it, int slot) {
     const int hh = it / ntq, i0 = (it % ntq) * kMassQRows;
+    const bf16_t* qb = q + ((size_t)b * a.n * a.Hq + g * G + hh) * D;   // row 0 of this head
 #pragma unroll
     for (int u = 0; u < BPW; ++u) {
-      const int blk = wave * BPW + u;
+      const int blk = wave_u * BPW + u;
       if (blk < NBLK) {
         const int r = blk * RPI + lane / CPR, sc = lane % CPR;
         const int i = min(i0 + r, a.n - 1);
-        const bf16_t* src = q + (((size_t)b * a.n + i) * a.Hq + g * G + hh) * D + (sc ^ swz_q<D>(r)) * 8;
-        dma_16B(src, ring + slot * QTILE + blk * 1024);
+        const uint32_t voff = (uint32_t)(((size_t)i * a.Hq * D + (sc ^ swz_q<D>(r)) * 8) * sizeof(bf16_t));
+        dma_16B_sbase(voff, qb, ring_lds + (uint32_t)(slot * QTILE + blk * 1024));
       }
     }
   };
