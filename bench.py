@@ -177,25 +177,18 @@ def run(args):
     torch.cuda.synchronize()
 
     names = ["refresh", "attention"] + (["drift"] if track else [])
-    # Per-call events go into every `event_every`-th timed step only: each recorded event adds a
-    # bubble of a few microseconds to the GPU timeline, which would otherwise inflate the step
-    # time it is meant to split up.
-    sampled = [s for s in range(args.steps) if s % args.event_every == args.event_every - 1]
-    ev = {s: [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for s in sampled}
+    calls = {
+        "refresh": lambda ly: dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_cur, idx_t, ly.w, Hq,
+                                                                wl.rope_base, q, rws),
+        "attention": lambda ly: dkv.dllm_block_attention(ly.cache, q, Hq, scale, out, lse,
+                                                         mass if track else None, ws),
+        "drift": lambda ly: dkv.dllm_drift_check(ly.cache, Hq, k, wl.gamma, ly.T, ly.buf, mass,
+                                                 sigma, refresh),
+    }
 
-    def step(ly, evs=None):
-        if evs:
-            evs[0].record()
-        dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_cur, idx_t, ly.w, Hq, wl.rope_base, q, rws)
-        if evs:
-            evs[1].record()
-        dkv.dllm_block_attention(ly.cache, q, Hq, scale, out, lse, mass if track else None, ws)
-        if evs:
-            evs[2].record()
-        if track:
-            dkv.dllm_drift_check(ly.cache, Hq, k, wl.gamma, ly.T, ly.buf, mass, sigma, refresh)
-            if evs:
-                evs[3].record()
+    def step(ly):
+        for nm in names:
+            calls[nm](ly)
 
     for s in range(args.warmup):
         step(layers[s % L])
@@ -204,16 +197,43 @@ def run(args):
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for s in range(args.steps):
-        step(layers[(args.warmup + s) % L], ev.get(s))
+        step(layers[(args.warmup + s) % L])
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    per = {nm: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in sampled])) * 1e3
-           for i, nm in enumerate(names)}
     ms_per_step = total_ms / args.steps
     value = M / (ms_per_step * 1e-3)
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; per call (us): "
-        + ", ".join(f"{k_}={v:.1f}" for k_, v in per.items()))
+
+    # Average duration of each call: the call alone, `burst` times back to back on the launch
+    # stream (layers rotating as in the steps), between two events.  Events between the calls
+    # of a step would each add a bubble of a few microseconds to the timeline they measure.
+    # A spin kernel ahead of the first event keeps the GPU busy while the host enqueues the
+    # burst, so host-side launch cost does not show in the interval (short calls would
+    # otherwise be timed at the rate the host issues them).
+    burst = max(10, args.steps)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(1 << 20)
+    e1.record()
+    torch.cuda.synchronize()
+    spin_per_ms = (1 << 20) / e0.elapsed_time(e1)
+    per = {}
+    for nm in names:
+        t0 = time.perf_counter()
+        for r in range(burst):
+            calls[nm](layers[r % L])
+        host_ms = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(spin_per_ms * (2.0 * host_ms + 0.2)))
+        e0.record()
+        for r in range(burst):
+            calls[nm](layers[r % L])
+        e1.record()
+        torch.cuda.synchronize()
+        per[nm] = e0.elapsed_time(e1) / burst * 1e3
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; per call (us, {burst} back to "
+        f"back): " + ", ".join(f"{k_}={v:.1f}" for k_, v in per.items()))
 
     works = work_model(wl)
     dtype = "f32" if wl.act == "f32" else "bf16"
@@ -235,7 +255,7 @@ def run(args):
                    "kv_heads": wl.kv_heads, "head_dim": D, "cache_dtype": wl.cache,
                    "tracking": track, "layer_instances": L, "parallelism": "none (1 GPU)"},
         "per_call_us": {k_: round(v, 2) for k_, v in per.items()},
-        "per_call_sampled_steps": len(sampled),
+        "per_call_back_to_back": burst,
         "rooflines": entries,
         "roofline": roof,
     }
@@ -303,14 +323,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="layer instances to rotate (0: auto)")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="record per-call events in every N-th timed step (at least one step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="after timing, run a plain device copy of this size (counter scaling)")
     args = ap.parse_args()
-    args.event_every = max(1, min(args.event_every, args.steps))
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
               f"requested).", file=sys.stderr)
