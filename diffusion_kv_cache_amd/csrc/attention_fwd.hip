@@ -145,8 +145,10 @@ __device__ __forceinline__ void fp8_store(const Fp8Stage<KIND, QW, D>& f, char* 
   if (gt < 2 * kKeys) ((float*)(st + 2 * C::TILE))[gt] = f.sc;
 }
 
-// One 32-key tile for one wave: scores, lazy online softmax, O^T update.
-template <int KIND, int QW, int D>
+// One 32-key tile for one wave: scores, lazy online softmax, O^T update.  MASKED: the tile
+// may hold keys past the split's end (only a split's last tile, which the key loop leaves for
+// after the loop, so the loop carries no masking work).
+template <int KIND, int QW, int D, bool MASKED>
 __device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2][D / 32],
                                              f32x4 (&oacc)[2][D / 16], float (&m)[2],
                                              float (&lsum)[2], int key0, int kend, float c,
@@ -170,8 +172,6 @@ __device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2
       for (int ct = 0; ct < 2; ++ct) sacc[ct][kt] = mfma_bf16(kf, as_bf16x8(qf[ct][ds]), sacc[ct][kt]);
     }
   }
-  // Only the last tile of a split can hold keys past the end; the others skip the masking.
-  const bool full = key0 + kKeys <= kend;
   float ksc[8], vsc[8];
   if constexpr (KIND == kCacheFP8) {
 #pragma unroll
@@ -189,7 +189,7 @@ __device__ __forceinline__ void tile_compute(const char* st, const u32x4 (&qf)[2
       sv[e] = sacc[ct][e >> 2][e & 3];
       if constexpr (KIND == kCacheFP8) sv[e] *= ksc[e];
     }
-    if (!full) {
+    if constexpr (MASKED) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (key0 + lg * 8 + e >= kend) sv[e] = -INFINITY;
@@ -318,10 +318,16 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
       const int tile = it * KW + kw;
       __syncthreads();
       if (it + 1 < iters) fp8_load<KIND, QW, D>(f, a, kc, vc, head_base, kbeg + (tile + KW) * kKeys, kbeg, kend, gt);
-      if (tile < ntiles)
-        tile_compute<KIND, QW, D>((it & 1) ? st1 : st0, qf, oacc, m, lsum, kbeg + tile * kKeys, kend, c, l16, lg);
+      if (tile < ntiles && kbeg + (tile + 1) * kKeys <= kend)
+        tile_compute<KIND, QW, D, false>((it & 1) ? st1 : st0, qf, oacc, m, lsum, kbeg + tile * kKeys,
+                                         kend, c, l16, lg);
       if (it + 1 < iters) fp8_store<KIND, QW, D>(f, (it & 1) ? st0 : st1, gt);
     }
+    // The split's partial last tile (if this group owns it) is still in its stage.
+    const int last = ntiles - 1;
+    if (last >= 0 && last % KW == kw && kbeg + (last + 1) * kKeys > kend)
+      tile_compute<KIND, QW, D, true>(((last / KW) & 1) ? st1 : st0, qf, oacc, m, lsum,
+                                      kbeg + last * kKeys, kend, c, l16, lg);
   } else {
     constexpr int PEND = 2 * C::DMA_W;           // DMA ops of one tile per wave
     constexpr int RPI = 1024 / C::RB;
@@ -355,10 +361,16 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
         dma_tile<KIND, QW, D>(ring_st + ((it + NST - 1) % NST) * C::STAGE, kh, vh,
                               kbeg + ((it + NST - 1) * KW + kw) * kKeys, kbeg, kend, qw, lane, koff, voff);
       const int tile = it * KW + kw;
-      if (tile < ntiles)
-        tile_compute<KIND, QW, D>(ring_kw + (it % NST) * C::STAGE, qf, oacc, m, lsum, kbeg + tile * kKeys,
-                                  kend, c, l16, lg);
+      if (tile < ntiles && kbeg + (tile + 1) * kKeys <= kend)
+        tile_compute<KIND, QW, D, false>(ring_kw + (it % NST) * C::STAGE, qf, oacc, m, lsum,
+                                         kbeg + tile * kKeys, kend, c, l16, lg);
     }
+    // The split's partial last tile, if this group owns it: its stage was filled at the
+    // group's last iteration and no transfer was issued after that.
+    const int last = ntiles - 1;
+    if (last >= 0 && last % KW == kw && kbeg + (last + 1) * kKeys > kend)
+      tile_compute<KIND, QW, D, true>(ring_kw + ((last / KW) % NST) * C::STAGE, qf, oacc, m, lsum,
+                                      kbeg + last * kKeys, kend, c, l16, lg);
     lds_barrier();                               // ring reads done before the merge reuses it
   }
 
