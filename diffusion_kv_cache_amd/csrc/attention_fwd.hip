@@ -351,19 +351,27 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     // compiler can tell: otherwise it keeps waiting for them inside the loop, on a counter
     // that also counts the tile transfers in flight, and drains the ring on every tile.
     DLLM_WAIT_VMCNT(0);
-    for (int it = 0; it < iters; ++it) {
-      // this wave's transfers for tile `it` are done once at most those of the later tiles
-      // already issued are outstanding
-      if (it + NST - 2 < iters) DLLM_WAIT_VMCNT(PEND * (NST - 2));
-      else DLLM_WAIT_VMCNT(0);
-      lds_barrier();                             // tile `it` visible; slot of it - 1 free
-      if (it + NST - 1 < iters)
-        dma_tile<KIND, QW, D>(ring_st + ((it + NST - 1) % NST) * C::STAGE, kh, vh,
-                              kbeg + ((it + NST - 1) * KW + kw) * kKeys, kbeg, kend, qw, lane, koff, voff);
-      const int tile = it * KW + kw;
-      if (tile < ntiles && kbeg + (tile + 1) * kKeys <= kend)
-        tile_compute<KIND, QW, D, false>(ring_kw + (it % NST) * C::STAGE, qf, oacc, m, lsum,
-                                         kbeg + tile * kKeys, kend, c, l16, lg);
+    // Unrolled by the ring depth, so the LDS addresses of every slot are constant offsets
+    // from one per-lane base (no address arithmetic per tile).
+    for (int it0 = 0; it0 < iters; it0 += NST) {
+#pragma unroll
+      for (int u = 0; u < NST; ++u) {
+        const int it = it0 + u;                  // it % NST == u
+        if (it >= iters) break;
+        // this wave's transfers for tile `it` are done once at most those of the later tiles
+        // already issued are outstanding
+        if (it + NST - 2 < iters) DLLM_WAIT_VMCNT(PEND * (NST - 2));
+        else DLLM_WAIT_VMCNT(0);
+        lds_barrier();                           // tile `it` visible; slot of it - 1 free
+        if (it + NST - 1 < iters)
+          dma_tile<KIND, QW, D>(ring_st + ((u + NST - 1) % NST) * C::STAGE, kh, vh,
+                                kbeg + ((it + NST - 1) * KW + kw) * kKeys, kbeg, kend, qw, lane, koff,
+                                voff);
+        const int tile = it * KW + kw;
+        if (tile < ntiles && kbeg + (tile + 1) * kKeys <= kend)
+          tile_compute<KIND, QW, D, false>(ring_kw + u * C::STAGE, qf, oacc, m, lsum, kbeg + tile * kKeys,
+                                           kend, c, l16, lg);
+      }
     }
     // The split's partial last tile, if this group owns it: its stage was filled at the
     // group's last iteration and no transfer was issued after that.
