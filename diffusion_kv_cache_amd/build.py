@@ -24,11 +24,13 @@ FLAGS = [
 ]
 # Per-source additions.  The attention kernels keep their MFMA accumulators in ordinary
 # VGPRs: with accumulation registers the compiler copied all 64 output accumulators out and
-# back on every key tile (the lazily rescaled softmax state is loop-carried through a branch).
+# back on every key tile (the lazily rescaled softmax state is loop-carried through a branch),
+# and the mass pass read every score out of them with one extra instruction each.
 # NaNs are not honoured there either (no canonicalising max before every fmaxf of a score):
 # scores of finite inputs are finite, and masked keys are -inf, which stays honoured.
 EXTRA = {"attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-         "attention_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
+         "attention_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+         "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def build(verbose: bool = False) -> str:

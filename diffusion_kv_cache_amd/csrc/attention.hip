@@ -273,10 +273,11 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
     for (int ct = 0; ct < kMassQRows / 16; ++ct) {
       const int r = ct * 16 + l16;
       const int i = i0 + r;
-      const bool ok = i < a.n;
       const int ic = min(i, a.n - 1);
-      const float lse2 = LDS_LSE ? lse2_s[ic * G + hh]
-                                 : a.lse[((size_t)b * a.Hq + g * G + hh) * a.n + ic] * kLog2e;
+      // rows past n (they read row n - 1) take lse = +inf, so their terms are exp2(-inf) = 0
+      const float lse2 = (i < a.n) ? (LDS_LSE ? lse2_s[ic * G + hh]
+                                              : a.lse[((size_t)b * a.Hq + g * G + hh) * a.n + ic] * kLog2e)
+                                   : INFINITY;
       bf16x8 qf[DS];
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
@@ -290,8 +291,7 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
         for (int ds = 0; ds < DS; ++ds) sv = mfma_bf16(kf[kt][ds], qf[ds], sv);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sv[v] * ksc[kt][v], c, -lse2));
-          acc[kt][v] += ok ? e : 0.f;
+          acc[kt][v] += __builtin_amdgcn_exp2f(fmaf(sv[v] * ksc[kt][v], c, -lse2));
         }
       }
     }
