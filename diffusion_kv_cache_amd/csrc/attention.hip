@@ -136,7 +136,6 @@ __global__ __launch_bounds__(64) void attn_merge(AttnArgs a, int splits) {
 // round-robin over the key chunks), first thing after the prologue's loads are issued, so no
 // separate merge launch is needed; then every packed row's log-sum-exp is formed from the
 // split partials and the workgroups of key chunk 0 write it.
-constexpr int kMassQRows = 32;                   // query rows per ring tile
 constexpr int kMassNst = 3;                      // ring stages
 // Largest packed-row count (n * G) whose log-sum-exp the mass pass stages in LDS (32 KB);
 // beyond it the rows' log-sum-exp is read from memory (and split attention merges first).
@@ -147,13 +146,14 @@ __device__ __forceinline__ int swz_q(int r) {   // chunk swizzle of a staged que
   return D == 128 ? ((r & 3) | (((r >> 2) & 3) << 2)) : ((r & 3) | (((r >> 2) & 1) << 2));
 }
 
-template <int KIND, int D, bool MERGE, bool LDS_LSE>
+// QR: query rows per ring tile (64, or 32 when the block has at most 32 rows).
+template <int KIND, int D, bool MERGE, bool LDS_LSE, int QR>
 __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
   static_assert(LDS_LSE || !MERGE, "the fused merge stages the log-sum-exp in LDS");
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   constexpr int DS = D / 32;
   constexpr int RB = D * 2;                      // bytes per query row
-  constexpr int QTILE = kMassQRows * RB;         // bytes per ring tile
+  constexpr int QTILE = QR * RB;         // bytes per ring tile
   constexpr int RPI = 1024 / RB;                 // rows per DMA block
   constexpr int NBLK = QTILE / 1024;             // DMA blocks per tile
   constexpr int BPW = (NBLK + 3) / 4;            // per wave (the last wave may have fewer)
@@ -177,13 +177,13 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
 
   // Query tiles: it = hh * ntq + (i0 / 32), rows i0 .. i0 + 31 of head g * G + hh (rows past
   // n read row n - 1 and are masked out of the sums).
-  const int ntq = (a.n + kMassQRows - 1) / kMassQRows;
+  const int ntq = (a.n + QR - 1) / QR;
   const int iters = G * ntq;
   const bf16_t* q = (const bf16_t*)a.q;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform: scalar DMA bases
   const uint32_t ring_lds = lds_addr(dyn);
   auto issue = [&](int it, int slot) {
-    const int hh = it / ntq, i0 = (it % ntq) * kMassQRows;
+    const int hh = it / ntq, i0 = (it % ntq) * QR;
     const bf16_t* qb = q + ((size_t)b * a.n * a.Hq + g * G + hh) * D;   // row 0 of this head
 #pragma unroll
     for (int u = 0; u < BPW; ++u) {
@@ -268,9 +268,9 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
     lds_barrier();
     if (it + kMassNst - 1 < iters) issue(it + kMassNst - 1, (it + kMassNst - 1) % kMassNst);
     const char* Q = ring + (it % kMassNst) * QTILE;
-    const int hh = it / ntq, i0 = (it % ntq) * kMassQRows;
+    const int hh = it / ntq, i0 = (it % ntq) * QR;
 #pragma unroll
-    for (int ct = 0; ct < kMassQRows / 16; ++ct) {
+    for (int ct = 0; ct < QR / 16; ++ct) {
       const int r = ct * 16 + l16;
       const int i = i0 + r;
       const int ic = min(i, a.n - 1);
@@ -424,13 +424,18 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   }
   if (a.mass) {
     const int grid2 = ((a.S + 127) / 128) * a.B * a.Hkv;
-    const size_t lds = (size_t)kMassNst * kMassQRows * D * 2 + (lds_lse ? (size_t)rows * sizeof(float) : 0);
+    const bool wide = a.n > 32;
+    const size_t lds = (size_t)kMassNst * (wide ? 64 : 32) * D * 2 + (lds_lse ? (size_t)rows * sizeof(float) : 0);
+#define DLLM_MASS(M_, L_)                                                                  \
+    (wide ? (attn_mass_mfma<KIND, D, M_, L_, 64><<<grid2, 256, lds, s>>>(a, p.splits), 0) \
+          : (attn_mass_mfma<KIND, D, M_, L_, 32><<<grid2, 256, lds, s>>>(a, p.splits), 0))
     if (fuse)
-      attn_mass_mfma<KIND, D, true, true><<<grid2, 256, lds, s>>>(a, p.splits);
+      DLLM_MASS(true, true);
     else if (lds_lse)
-      attn_mass_mfma<KIND, D, false, true><<<grid2, 256, lds, s>>>(a, p.splits);
+      DLLM_MASS(false, true);
     else
-      attn_mass_mfma<KIND, D, false, false><<<grid2, 256, lds, s>>>(a, p.splits);
+      DLLM_MASS(false, false);
+#undef DLLM_MASS
     e = hipGetLastError();
   }
   return e;
