@@ -314,9 +314,12 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
 // ring, so NST - 1 stages are in flight while one is multiplied.  Each lane fetches the
 // source chunk that lands, swizzled (chunk c of row r at slot c ^ (r % BKC)), at its LDS
 // slot.  A barrier per stage; each wave waits only for its own transfers of the stage it is
-// about to read.
+// about to read.  SB: the hidden states and W both span less than 4 GB, so each transfer
+// takes a wave-uniform base (advanced per stage in scalar registers) and a fixed 32-bit
+// per-lane offset, and costs no vector address arithmetic.  The stage loop is unrolled by the
+// ring depth, so every LDS slot address is a constant offset.
 // ------------------------------------------------------------------------------------------
-template <int KIND, int TM, int D, int BKC, int NST, int WM>
+template <int KIND, int TM, int D, int BKC, int NST, int WM, bool SB>
 __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
   constexpr int NW = 2 * WM;                 // waves: WM along the rows x 2 column groups
   constexpr int EPC = 8;                     // bf16 per 16-byte chunk
@@ -342,6 +345,7 @@ __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
   // positions are loaded for every instruction (clamped, unconditional) before any address is
   // formed, so they cost one round trip.
   const bf16_t* src[NI];
+  uint32_t voff[NI];                             // SB: byte offset from hidden (A) or w (W)
   int mrow[NI], prow[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -353,19 +357,33 @@ __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
   for (int i = 0; i < NI; ++i) {
     const int gi = wave * NI + i;
     const int cp = lane % BKC;
+    size_t e;                                    // element offset of the chunk
     if (gi < IA) {
       const int r = gi * RPI + lane / BKC;
       const size_t hrow = (size_t)(mrow[i] / a.n) * a.S + prow[i];
-      src[i] = (const bf16_t*)a.hidden + hrow * a.H + (cp ^ (r & (BKC - 1))) * EPC;
+      e = hrow * a.H + (cp ^ (r & (BKC - 1))) * EPC;
+      src[i] = (const bf16_t*)a.hidden + e;
     } else {
       const int c = (gi - IA) * RPI + lane / BKC;
-      src[i] = (const bf16_t*)a.w + (size_t)(j * D + c) * a.H + (cp ^ (c & (BKC - 1))) * EPC;
+      e = (size_t)(j * D + c) * a.H + (cp ^ (c & (BKC - 1))) * EPC;
+      src[i] = (const bf16_t*)a.w + e;
     }
+    voff[i] = (uint32_t)(e * sizeof(bf16_t));
   }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds_w = lds_addr(smem) + (uint32_t)(wave_u * NI * 1024);   // this wave's blocks
   auto issue = [&](int stage, int slot) {
-    char* base = smem + slot * STAGE;
+    if constexpr (SB) {
+      const char* hb = (const char*)a.hidden + (size_t)stage * BK * sizeof(bf16_t);
+      const char* wb = (const char*)a.w + (size_t)stage * BK * sizeof(bf16_t);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma_16B(src[i] + stage * BK, base + (wave * NI + i) * 1024);
+      for (int i = 0; i < NI; ++i)
+        dma_16B_sbase(voff[i], (wave_u * NI + i < IA) ? hb : wb, lds_w + (uint32_t)(slot * STAGE + i * 1024));
+    } else {
+      char* base = smem + slot * STAGE;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma_16B(src[i] + stage * BK, base + (wave * NI + i) * 1024);
+    }
   };
 
   int colv[CT];
@@ -387,14 +405,18 @@ __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
     if (st < stages) issue(st, st);
-  for (int s = 0; s < stages; ++s) {
+  for (int s0 = 0; s0 < stages; s0 += NST) {
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    const int s = s0 + u;                        // s % NST == u
+    if (s >= stages) break;
     // this wave's transfers for stage s are done once at most those of the later stages
     // already issued (min(NST - 2, stages - 1 - s) of them) are outstanding
     if (s + NST - 2 < stages) DLLM_WAIT_VMCNT(NI * (NST - 2));
     else DLLM_WAIT_VMCNT(0);
     lds_barrier();
-    if (s + NST - 1 < stages) issue(s + NST - 1, (s + NST - 1) % NST);
-    const char* A = smem + (s % NST) * STAGE;
+    if (s + NST - 1 < stages) issue(s + NST - 1, (u + NST - 1) % NST);
+    const char* A = smem + u * STAGE;
     const char* W = A + A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < BKC / 4; ++ks) {
@@ -425,6 +447,7 @@ __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
         }
     }
   }
+  }
   lds_barrier();  // every wave is done reading the ring before the epilogue reuses it
   tile_epilogue<bf16_t, KIND, TM, D, WM>(a, tot, smem, j, m0, colv);
 }
@@ -433,7 +456,13 @@ template <int KIND, int TM, int D, int BKC, int NST, int WM>
 hipError_t launch_gemm(const RefreshArgs& a, hipStream_t s) {
   const int heads = a.Hq + 2 * a.Hkv;
   dim3 grid(heads, (a.M + TM - 1) / TM);
-  refresh_gemm<KIND, TM, D, BKC, NST, WM><<<grid, 128 * WM, 0, s>>>(a);
+  // 32-bit per-lane offsets reach every chunk when both operands span less than 4 GB
+  const uint64_t hid_bytes = (uint64_t)a.B * a.S * a.H * sizeof(bf16_t);
+  const uint64_t w_bytes = (uint64_t)heads * D * a.H * sizeof(bf16_t);
+  if (hid_bytes < (1ull << 32) && w_bytes < (1ull << 32))
+    refresh_gemm<KIND, TM, D, BKC, NST, WM, true><<<grid, 128 * WM, 0, s>>>(a);
+  else
+    refresh_gemm<KIND, TM, D, BKC, NST, WM, false><<<grid, 128 * WM, 0, s>>>(a);
   return hipGetLastError();
 }
 
