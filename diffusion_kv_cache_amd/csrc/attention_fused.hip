@@ -97,13 +97,9 @@ __device__ __forceinline__ void scores(const char* kst, const u32x4 (&qf)[2][D /
 
 // Pass 1 on one tile: lazily rescaled running max m (log2 domain) and normaliser l per query
 // column; lane group lg holds keys 8 lg .. 8 lg + 7 of the tile.  FULL: no key past the end.
-template <int D, bool FULL>
-__device__ __forceinline__ void tile_stats(const Tile<D>& k, char* kst, const u32x4 (&qf)[2][D / 32],
-                                           float (&m)[2], float (&l)[2], int key0, int S, float c,
-                                           int lane, int l16, int lg) {
-  stage_tile<D, true>(k, kst, lane);
-  f32x4 s[2][2];
-  scores<D>(kst, qf, s, l16, lg);
+template <bool FULL>
+__device__ __forceinline__ void stats_from(const f32x4 (&s)[2][2], float (&m)[2], float (&l)[2], int key0,
+                                           int S, float c, int lg) {
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     float sv[8];
@@ -129,18 +125,25 @@ __device__ __forceinline__ void tile_stats(const Tile<D>& k, char* kst, const u3
   }
 }
 
-// Pass 2 on one tile: exact probabilities, the tile's 32 column masses, and O^T += V^T P^T.
 template <int D, bool FULL>
-__device__ __forceinline__ void tile_out(const Tile<D>& k, const Tile<D>& v, char* kst, char* vst,
-                                         const u32x4 (&qf)[2][D / 32], const float (&L2)[2],
-                                         const bool (&rowok)[2], f32x4 (&oacc)[2][D / 16],
-                                         float* mass_s, int key0, int S, float c, int lane, int l16,
-                                         int lg) {
-  constexpr int RB = 2 * D, DT = D / 16;
+__device__ __forceinline__ void tile_stats(const Tile<D>& k, char* kst, const u32x4 (&qf)[2][D / 32],
+                                           float (&m)[2], float (&l)[2], int key0, int S, float c,
+                                           int lane, int l16, int lg) {
   stage_tile<D, true>(k, kst, lane);
-  stage_tile<D, false>(v, vst, lane);
   f32x4 s[2][2];
   scores<D>(kst, qf, s, l16, lg);
+  stats_from<FULL>(s, m, l, key0, S, c, lg);
+}
+
+// Pass 2 on one tile, given its scores: exact probabilities, the tile's 32 column masses,
+// and O^T += V^T P^T.
+template <int D, bool FULL>
+__device__ __forceinline__ void out_from(const f32x4 (&s)[2][2], const Tile<D>& v, char* vst,
+                                         const float (&L2)[2], const bool (&rowok)[2],
+                                         f32x4 (&oacc)[2][D / 16], float* mass_s, int key0, int S,
+                                         float c, int lane, int l16, int lg) {
+  constexpr int RB = 2 * D, DT = D / 16;
+  stage_tile<D, false>(v, vst, lane);
   bf16x8 pb[2];
   float col[8];
 #pragma unroll
@@ -194,7 +197,22 @@ __device__ __forceinline__ void tile_out(const Tile<D>& k, const Tile<D>& v, cha
   }
 }
 
-template <int D>
+// Pass 2 on one tile, K staged again and its scores recomputed.
+template <int D, bool FULL>
+__device__ __forceinline__ void tile_out(const Tile<D>& k, const Tile<D>& v, char* kst, char* vst,
+                                         const u32x4 (&qf)[2][D / 32], const float (&L2)[2],
+                                         const bool (&rowok)[2], f32x4 (&oacc)[2][D / 16],
+                                         float* mass_s, int key0, int S, float c, int lane, int l16,
+                                         int lg) {
+  stage_tile<D, true>(k, kst, lane);
+  f32x4 s[2][2];
+  scores<D>(kst, qf, s, l16, lg);
+  out_from<D, FULL>(s, v, vst, L2, rowok, oacc, mass_s, key0, S, c, lane, l16, lg);
+}
+
+// TPW > 0: every wave has at most TPW tiles, and pass 1 keeps their scores in registers, so
+// pass 2 reads only V (no second K pass, no recomputed scores).  TPW = 0: K is streamed twice.
+template <int D, int TPW>
 __global__ __launch_bounds__(256) void attn_fused(AttnArgs a) {
   constexpr int DS = D / 32, DT = D / 16, RB = 2 * D;
   constexpr int TB = kKeys * RB;                 // one K or V tile in LDS
@@ -240,7 +258,27 @@ __global__ __launch_bounds__(256) void attn_fused(AttnArgs a) {
     if (key0 + kKeys <= S) tile_stats<D, true>(k, kst, qf, m, l, key0, S, c, lane, l16, lg);
     else tile_stats<D, false>(k, kst, qf, m, l, key0, S, c, lane, l16, lg);
   };
-  {
+  constexpr int KT = TPW > 0 ? TPW : 1;
+  f32x4 sk[KT][2][2];                            // TPW > 0: the scores of this wave's tiles
+  if constexpr (TPW > 0) {
+    constexpr int DK = 2;                        // K tiles in flight
+    Tile<D> kr[DK];
+#pragma unroll
+    for (int u = 0; u < DK; ++u) load_tile<D>(kr[u], kh, key0_of(min(u, iters - 1)), S, lane);
+#pragma unroll
+    for (int it = 0; it < TPW; ++it) {
+      if (it < iters) {
+        if (live(it)) {
+          const int key0 = key0_of(it);
+          stage_tile<D, true>(kr[it % DK], kst, lane);
+          scores<D>(kst, qf, sk[it], l16, lg);
+          if (key0 + kKeys <= S) stats_from<true>(sk[it], m, l, key0, S, c, lg);
+          else stats_from<false>(sk[it], m, l, key0, S, c, lg);
+        }
+        load_tile<D>(kr[it % DK], kh, key0_of(min(it + DK, iters - 1)), S, lane);
+      }
+    }
+  } else {
     Tile<D> kr[kDepth1];
 #pragma unroll
     for (int u = 0; u < kDepth1; ++u) load_tile<D>(kr[u], kh, key0_of(min(u, iters - 1)), S, lane);
@@ -294,7 +332,25 @@ __global__ __launch_bounds__(256) void attn_fused(AttnArgs a) {
     if (key0 + kKeys <= S) tile_out<D, true>(k, v, kst, vst, qf, L2, rowok, oacc, mass_s, key0, S, c, lane, l16, lg);
     else tile_out<D, false>(k, v, kst, vst, qf, L2, rowok, oacc, mass_s, key0, S, c, lane, l16, lg);
   };
-  {
+  if constexpr (TPW > 0) {
+    constexpr int DV = 2;                        // V tiles in flight
+    Tile<D> vr[DV];
+#pragma unroll
+    for (int u = 0; u < DV; ++u) load_tile<D>(vr[u], vh, key0_of(min(u, iters - 1)), S, lane);
+#pragma unroll
+    for (int it = 0; it < TPW; ++it) {
+      if (it < iters) {
+        if (live(it)) {
+          const int key0 = key0_of(it);
+          if (key0 + kKeys <= S)
+            out_from<D, true>(sk[it], vr[it % DV], vst, L2, rowok, oacc, mass_s, key0, S, c, lane, l16, lg);
+          else
+            out_from<D, false>(sk[it], vr[it % DV], vst, L2, rowok, oacc, mass_s, key0, S, c, lane, l16, lg);
+        }
+        load_tile<D>(vr[it % DV], vh, key0_of(min(it + DV, iters - 1)), S, lane);
+      }
+    }
+  } else {
     Tile<D> kr[kDepth2], vr[kDepth2];
 #pragma unroll
     for (int u = 0; u < kDepth2; ++u) {
@@ -368,8 +424,14 @@ bool attn_fused_fits(const AttnArgs& a, const AttnPlan& p) {
 hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.B * a.Hkv);
   const size_t lds = (size_t)a.S * sizeof(float);
-  if (a.D == 128) attn_fused<128><<<grid, 256, lds, s>>>(a);
-  else attn_fused<64><<<grid, 256, lds, s>>>(a);
+  const int iters = ((a.S + kKeys - 1) / kKeys + kWaves - 1) / kWaves;   // tiles per wave
+  if (a.D == 128) {
+    if (iters <= 6) attn_fused<128, 6><<<grid, 256, lds, s>>>(a);
+    else attn_fused<128, 0><<<grid, 256, lds, s>>>(a);
+  } else {
+    if (iters <= 6) attn_fused<64, 6><<<grid, 256, lds, s>>>(a);
+    else attn_fused<64, 0><<<grid, 256, lds, s>>>(a);
+  }
   return hipGetLastError();
 }
 

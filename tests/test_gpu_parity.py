@@ -221,6 +221,9 @@ ATT_CASES = {
                                seq=70, prompt=30, block_start=32, block_len=32, seed=47),
     "fused_s1": C(batch=16, hidden=256, q_heads=32, kv_heads=32, head_dim=64, seq=1, prompt=0,
                   block_start=0, block_len=1, seed=48),
+    # more than six key tiles per wave: scores not kept in registers, K read in both passes
+    "fused_d128_two_k_passes": C(batch=16, hidden=256, q_heads=32, kv_heads=32, head_dim=128,
+                                 seq=900, prompt=450, block_start=451, block_len=24, seed=49),
     # n * G = 8800 packed rows: more log-sum-exp values than the mass pass stages in LDS
     "bf16_mass_rows_over_lds": C(batch=1, hidden=256, q_heads=8, kv_heads=1, head_dim=64,
                                  seq=1100, prompt=0, block_start=0, block_len=1100, seed=45),
