@@ -453,12 +453,13 @@ AttnPlan plan_attention(int B, int n, int Hq, int Hkv, int S, int D, int act, in
   p.qt = rows >= 512 ? 128 : rows > 32 ? 64 : 32;
   const int qtiles = (rows + p.qt - 1) / p.qt;
   const long wgs = (long)B * Hkv * qtiles;
-  // Enough workgroups to cover the 256 compute units about twice, keeping at least one key
-  // tile per wave.
+  // Enough workgroups to cover the 256 compute units about twice (once for FP8 caches with
+  // four key groups, whose rings fill a CU's LDS), keeping at least one key tile per wave.
   const int kw = 4 / (p.qt / 32);
   const int tiles = (S + kKeys - 1) / kKeys;
+  const long target = (kind == kCacheFP8 && kw == 4) ? 256 : 512;
   int splits = 1;
-  while (wgs * splits < 512 && tiles / (splits * 2) >= kw) splits *= 2;
+  while (wgs * splits < target && tiles / (splits * 2) >= kw) splits *= 2;
   p.splits = splits;
   p.kps = ((tiles + splits - 1) / splits) * kKeys;
   p.splits = (S + p.kps - 1) / p.kps;
