@@ -316,7 +316,9 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     fp8_store<KIND, QW, D>(f, st0, gt);
     for (int it = 0; it < iters; ++it) {
       const int tile = it * KW + kw;
-      __syncthreads();
+      // One wave per key group stages and reads its own tiles (LDS operations of a wave take
+      // effect in issue order), so only groups of several waves need the barrier.
+      if constexpr (QW > 1) __syncthreads();
       if (it + 1 < iters) fp8_load<KIND, QW, D>(f, a, kc, vc, head_base, kbeg + (tile + KW) * kKeys, kbeg, kend, gt);
       if (tile < ntiles && kbeg + (tile + 1) * kKeys <= kend)
         tile_compute<KIND, QW, D, false>((it & 1) ? st1 : st0, qf, oacc, m, lsum, kbeg + tile * kKeys,
