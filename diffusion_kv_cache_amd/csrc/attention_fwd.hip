@@ -364,7 +364,9 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
         // already issued are outstanding
         if (it + NST - 2 < iters) DLLM_WAIT_VMCNT(PEND * (NST - 2));
         else DLLM_WAIT_VMCNT(0);
-        lds_barrier();                           // tile `it` visible; slot of it - 1 free
+        // tile `it` visible; slot of it - 1 free (a one-wave group owns its ring: no barrier)
+        if constexpr (QW == 1) lds_wave_fence();
+        else lds_barrier();
         if (it + NST - 1 < iters)
           dma_tile<KIND, QW, D>(ring_st + ((u + NST - 1) % NST) * C::STAGE, kh, vh,
                                 kbeg + ((it + NST - 1) * KW + kw) * kKeys, kbeg, kend, qw, lane, koff,

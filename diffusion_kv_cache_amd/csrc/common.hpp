@@ -102,6 +102,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The same wait without the barrier, for LDS that only the issuing wave reads and writes: its
+// LDS reads have completed (so a transfer may overwrite what they read).
+__device__ __forceinline__ void lds_wave_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));
+  asm volatile("" ::: "memory");
+}
+
 // s_waitcnt with only the vector-memory count set (N outstanding allowed, 0..63).
 #define DLLM_WAIT_VMCNT(N) \
   __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
