@@ -18,6 +18,8 @@
 // Rotary pairing (i, i + D/2): every wave owns column tiles in pairs (c, c + D/2), so both
 // members of a pair sit in the same lane and register of the MFMA accumulator and the
 // rotation needs no data exchange.
+#include <stdlib.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -457,9 +459,11 @@ hipError_t launch_gemm(const RefreshArgs& a, hipStream_t s) {
   const int heads = a.Hq + 2 * a.Hkv;
   dim3 grid(heads, (a.M + TM - 1) / TM);
   // 32-bit per-lane offsets reach every chunk when both operands span less than 4 GB
+  // (DLLM_GEMM_WIDE_OFFSETS=1 takes the 64-bit form regardless, so it can be tested).
   const uint64_t hid_bytes = (uint64_t)a.B * a.S * a.H * sizeof(bf16_t);
   const uint64_t w_bytes = (uint64_t)heads * D * a.H * sizeof(bf16_t);
-  if (hid_bytes < (1ull << 32) && w_bytes < (1ull << 32))
+  const char* wide = getenv("DLLM_GEMM_WIDE_OFFSETS");
+  if (hid_bytes < (1ull << 32) && w_bytes < (1ull << 32) && !(wide && wide[0] == '1'))
     refresh_gemm<KIND, TM, D, BKC, NST, WM, true><<<grid, 128 * WM, 0, s>>>(a);
   else
     refresh_gemm<KIND, TM, D, BKC, NST, WM, false><<<grid, 128 * WM, 0, s>>>(a);

@@ -44,6 +44,9 @@
  *     returns DLLM_EINVAL otherwise; every call synchronises its stream and reports launch
  *     failures.  Without debug mode an index list that breaks the contract is undefined
  *     behaviour.
+ *   - DLLM_GEMM_WIDE_OFFSETS=1 makes the refresh of more than 64 rows address its operands
+ *     with 64-bit per-lane pointers, the form it otherwise takes only when the hidden states
+ *     or the weights span 4 GB or more (same results; for testing that form).
  */
 #ifndef DLLM_CACHE_H
 #define DLLM_CACHE_H

@@ -134,6 +134,24 @@ def test_step_reproduces_full_refresh_bitwise(name):
         assert torch.equal(q_full[b, torch.from_numpy(inp.idx[b]).long().cuda()], q_step[b])
 
 
+@pytest.mark.parametrize("name", ["skinny_bf16_d128", "fp8_tiled_d128"])
+def test_gemm_wide_offsets_match(name, monkeypatch):
+    """The refresh GEMM's 64-bit operand addressing (taken for operands of 4 GB or more)
+    stores exactly what the 32-bit-offset form stores."""
+    wl = REFRESH_CASES[name]
+    say(f"[wide offsets] {name}")
+    inp = synth.make_inputs(wl)
+    h_prev = to_dev(inp.hidden_prev, ACT_TORCH[wl.act])
+    base = GpuLayer(wl, inp.w)
+    q_base = base.prefill(h_prev)
+    monkeypatch.setenv("DLLM_GEMM_WIDE_OFFSETS", "1")
+    wide = GpuLayer(wl, inp.w)
+    q_wide = wide.prefill(h_prev)
+    torch.cuda.synchronize()
+    assert torch.equal(base.cache.region, wide.cache.region)
+    assert torch.equal(q_base, q_wide)
+
+
 def test_tiled128_prefill_matches_oracle_and_step():
     """A prefill large enough for the 128-row tiles, against the oracle and against a
     step on the small-M kernel (bitwise)."""
