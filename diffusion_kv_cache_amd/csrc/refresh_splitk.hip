@@ -121,6 +121,17 @@ __global__ __launch_bounds__(64) void refresh_reduce(RefreshArgs a, const float*
   const bool ok = item < a.M * heads;
   const int it = ok ? item : 0;
   const int m = it / heads, j = it % heads;
+  // All the partials and the row position are requested first: one round trip, and the
+  // rotation frequencies below (fp64) are formed while it is in flight.
+  const int pos = a.idx[m];
+  fvec px[kKSplit], py[kKSplit];
+#pragma unroll
+  for (int p = 0; p < kKSplit; ++p) {
+    const float* row = part + ((size_t)p * a.M + m) * N + j * D + L * PPL;
+    px[p] = *(const fvec*)row;
+    py[p] = *(const fvec*)(row + HALF);
+  }
+  __builtin_amdgcn_sched_barrier(0);             // keep every load ahead of the arithmetic
   // every lane forms the rotation frequency of pair (lane mod D/2); the group's lanes
   // fetch theirs by shuffle
   float hi_own, lo_own;
@@ -128,11 +139,9 @@ __global__ __launch_bounds__(64) void refresh_reduce(RefreshArgs a, const float*
   fvec x = {}, y = {};
 #pragma unroll
   for (int p = 0; p < kKSplit; ++p) {
-    const float* row = part + ((size_t)p * a.M + m) * N + j * D + L * PPL;
-    x = x + *(const fvec*)row;
-    y = y + *(const fvec*)(row + HALF);
+    x = x + px[p];
+    y = y + py[p];
   }
-  const int pos = a.idx[m];
   const bool rot = j < a.Hq + a.Hkv;
 #pragma unroll
   for (int e = 0; e < PPL; ++e) {
