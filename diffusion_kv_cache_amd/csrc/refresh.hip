@@ -39,6 +39,16 @@ __device__ __forceinline__ size_t out_row_offset(const RefreshArgs& a, int m, in
   return (((size_t)b * a.Hkv + g) * a.S + pos) * (size_t)a.D;
 }
 
+// Rotation frequencies (in turns, hi + lo) of the column pairs this lane rotates in the
+// epilogue; formed before the main loop, so their fp64 arithmetic overlaps the first
+// transfers instead of delaying the epilogue.
+template <int D>
+__device__ __forceinline__ void epilogue_turns(const RefreshArgs& a, float (&hi)[D / 64], float (&lo)[D / 64]) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+#pragma unroll
+  for (int sb = 0; sb < D / 64; ++sb) rope_turns(wn * (D / 4) + sb * 16 + (lane & 15), D, a.rope_base, hi[sb], lo[sb]);
+}
+
 // Epilogue of a finished (TM rows) x (one head) tile held as per-wave accumulators tot:
 // rotary embedding of Q and K heads in registers, the fp32 tile staged in LDS (smem, at least
 // TM * (D + 4) floats, free when called), then whole rows out: bf16 / fp32 rows, or per-row
@@ -48,7 +58,8 @@ __device__ __forceinline__ size_t out_row_offset(const RefreshArgs& a, int m, in
 template <typename T, int KIND, int TM, int D, int WM>
 __device__ __forceinline__ void tile_epilogue(const RefreshArgs& a,
                                               f32x4 (&tot)[TM / (16 * WM)][D / 32], char* smem,
-                                              int j, int m0, const int (&colv)[D / 32]) {
+                                              int j, int m0, const int (&colv)[D / 32],
+                                              const float (&hi)[D / 64], const float (&lo)[D / 64]) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int RT = TM / (16 * WM), CT = D / 32, CH = CT / 2;
   constexpr int NT = 128 * WM;
@@ -70,9 +81,6 @@ __device__ __forceinline__ void tile_epilogue(const RefreshArgs& a,
 
   // Rotary embedding of Q and K heads, in registers.
   if (j < a.Hq + a.Hkv) {
-    float hi[CH], lo[CH];
-#pragma unroll
-    for (int sb = 0; sb < CH; ++sb) rope_turns(wn * (D / 4) + sb * 16 + l16, D, a.rope_base, hi[sb], lo[sb]);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -248,6 +256,8 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
   const int stages = a.H / BK;
   const int per_part = stages / kKSplit;
   DLLM_LOAD_STAGE(0);
+  float hi[D / 64], lo[D / 64];
+  epilogue_turns<D>(a, hi, lo);
   DLLM_STORE_STAGE(0);
   __syncthreads();
   for (int s = 0; s < stages; ++s) {
@@ -307,7 +317,7 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
     __syncthreads();
   }
 
-  tile_epilogue<T, KIND, TM, D, 2>(a, tot, smem, j, m0, colv);
+  tile_epilogue<T, KIND, TM, D, 2>(a, tot, smem, j, m0, colv, hi, lo);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -407,6 +417,8 @@ __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
 #pragma unroll
   for (int st = 0; st < NST - 1; ++st)
     if (st < stages) issue(st, st);
+  float hi[D / 64], lo[D / 64];
+  epilogue_turns<D>(a, hi, lo);
   for (int s0 = 0; s0 < stages; s0 += NST) {
 #pragma unroll
   for (int u = 0; u < NST; ++u) {
@@ -451,7 +463,7 @@ __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
   }
   }
   lds_barrier();  // every wave is done reading the ring before the epilogue reuses it
-  tile_epilogue<bf16_t, KIND, TM, D, WM>(a, tot, smem, j, m0, colv);
+  tile_epilogue<bf16_t, KIND, TM, D, WM>(a, tot, smem, j, m0, colv, hi, lo);
 }
 
 template <int KIND, int TM, int D, int BKC, int NST, int WM>
