@@ -10,10 +10,10 @@
 // merged across workgroups: its four waves take every fourth 32-key tile and
 //   pass 1 streams K and keeps each query row's running max and normaliser,
 //   the waves combine their row states in wave order (exact log-sum-exp of every row),
-//   pass 2 streams K (again; the head's rows are in L2 by then) and V, forms the exact
-//     probabilities p = exp2(s * scale * log2 e - lse_2), adds them down each key column
-//     (the column mass, finished inside the wave: all query rows are here) and accumulates
-//     O^T += V^T P^T,
+//   pass 2 streams V (and K again, unless every wave has at most six tiles: then pass 1
+//     kept its raw scores in registers), forms the exact probabilities
+//     p = exp2(s * scale * log2 e - lse_2), adds them down each key column (the column mass,
+//     finished inside the wave: all query rows are here) and accumulates O^T += V^T P^T,
 //   the four partial outputs are added in wave order through LDS.
 // K and V tiles are loaded row-contiguous into registers (whole 128-byte lines per load, several
 // tiles in flight per wave), then written to one LDS stage per wave, from which the MFMA

@@ -7,7 +7,7 @@
 //
 // A workgroup owns (b, KV head g, a tile of packed query rows r = i * G + (h - g * G), one
 // key split).  Its four waves form KW groups of QW waves; each wave holds 32 query rows, each
-// group streams its own share of the split's 32-key tiles through a two-stage LDS ring.
+// group streams its own share of the split's 32-key tiles through an LDS ring of its own.
 //
 // Layout of a tile in LDS: K and V rows as in the cache (row-major, bf16), 16-byte chunks
 // XOR-swizzled per row.  bf16 caches are copied global -> LDS by the DMA path of the vector
