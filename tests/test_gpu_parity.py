@@ -239,6 +239,9 @@ ATT_CASES = {
                                seq=70, prompt=30, block_start=32, block_len=32, seed=47),
     "fused_s1": C(batch=16, hidden=256, q_heads=32, kv_heads=32, head_dim=64, seq=1, prompt=0,
                   block_start=0, block_len=1, seed=48),
+    # few heads (the keys are split; the mass pass merges the splits), ragged last key tile
+    "few_heads_d128_ragged": C(batch=2, hidden=256, q_heads=16, kv_heads=16, head_dim=128, seq=1000,
+                            prompt=500, block_start=501, block_len=24, seed=50),
     # more than six key tiles per wave: scores not kept in registers, K read in both passes
     "fused_d128_two_k_passes": C(batch=16, hidden=256, q_heads=32, kv_heads=32, head_dim=128,
                                  seq=900, prompt=450, block_start=451, block_len=24, seed=49),
