@@ -329,7 +329,7 @@ def main():
                     help="after timing, run a plain device copy of this size (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path; each GPU serves its own sequences (--gpus {args.gpus} "
               f"requested).", file=sys.stderr)
         sys.exit(2)
     run(args)
