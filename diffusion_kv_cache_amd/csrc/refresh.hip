@@ -509,13 +509,20 @@ hipError_t launch_d(const RefreshArgs& a, hipStream_t s) {
   // 128 rows x one head per workgroup, eight waves of 32 rows x half the head's column pairs.
   // Small M streams W at the HBM rate and wants a third stage in flight; large M wants the
   // occupancy of two stages.
+  // At most 256 rows (two row tiles, fewer workgroups than compute units, one per CU) run
+  // sixteen waves of 16 rows for D = 128: the extra waves hide the stage latency (49.2 against
+  // 50.2 us on a 256-row, 4096-hidden step); with more rows two 8-wave workgroups share a CU.
   const bool bk8 = (a.H / kKSplit) % 64 == 0;
   const bool deep = a.M <= 512;
+  const bool wide = D == 128 && a.M <= 256;
+  constexpr int WW = D == 128 ? 8 : 4;
   if (a.kind == kCacheFP8) {
     if (!bk8) return launch_gemm<kCacheFP8, 128, D, 4, 2, (D == 64 ? 2 : 4)>(a, s);
+    if (wide) return launch_gemm<kCacheFP8, 128, D, 8, 3, WW>(a, s);
     return deep ? launch_gemm<kCacheFP8, 128, D, 8, 3, 4>(a, s) : launch_gemm<kCacheFP8, 128, D, 8, 2, 4>(a, s);
   }
   if (!bk8) return launch_gemm<kCacheBF16, 128, D, 4, 2, (D == 64 ? 2 : 4)>(a, s);
+  if (wide) return launch_gemm<kCacheBF16, 128, D, 8, 3, WW>(a, s);
   return deep ? launch_gemm<kCacheBF16, 128, D, 8, 3, 4>(a, s) : launch_gemm<kCacheBF16, 128, D, 8, 2, 4>(a, s);
 }
 
