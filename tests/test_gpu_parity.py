@@ -282,6 +282,10 @@ DRIFT_CASES = {
     "bf16_k64_d64": dict(B=2, Hq=4, Hkv=4, S=500, D=64, k=64, dt="bf16"),
     "bf16_S_below_k": dict(B=2, Hq=2, Hkv=1, S=20, D=128, k=32, dt="bf16"),
     "f32": dict(B=2, Hq=4, Hkv=2, S=50, D=64, k=8, dt="f32"),
+    # rows past 4096 keys: further rounds of mass loads and of the selection walk
+    "bf16_long_S": dict(B=2, Hq=2, Hkv=2, S=6000, D=64, k=32, dt="bf16"),
+    # a long row that is not a multiple of 4 (scalar mass loads), GQA
+    "bf16_long_ragged_gqa": dict(B=2, Hq=4, Hkv=2, S=4099, D=128, k=32, dt="bf16"),
 }
 
 
