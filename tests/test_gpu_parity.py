@@ -203,6 +203,9 @@ def test_exact_values_on_integer_grid(n_rows):
 ATT_CASES = {
     "bf16_g1_splits": C(batch=1, hidden=256, q_heads=2, kv_heads=2, head_dim=128, seq=1000,
                         prompt=500, block_start=500, block_len=20, seed=31),
+    # 8192 keys over two heads: 64 key splits, more than one merge batch
+    "bf16_many_splits": C(batch=1, hidden=256, q_heads=2, kv_heads=2, head_dim=128, seq=8192,
+                          prompt=4096, block_start=4096, block_len=20, seed=41),
     "bf16_g7_qt128_ragged": C(batch=2, hidden=256, q_heads=7, kv_heads=1, head_dim=128, seq=300,
                               prompt=150, refresh="window+subset", window=8, subset=72, seed=32),
     "bf16_g3_qt64_d64": C(batch=2, hidden=256, q_heads=6, kv_heads=2, head_dim=64, seq=257,
@@ -271,6 +274,11 @@ def test_attention_parity(name):
     assert slice_rel_err(mass.cpu().numpy(), m_ref, (0, 1)) <= 2e-2
     # each query's probabilities sum to one: every head's mass sums to n
     np.testing.assert_allclose(mass.sum(-1).cpu().numpy(), wl.n_refresh, rtol=1e-3)
+    # without the mass the key splits are merged by their own kernel
+    out2, lse2, _ = layer.attention(q, want_mass=False)
+    torch.cuda.synchronize()
+    assert slice_rel_err(out2.float().cpu().numpy(), o_ref, (0, 2)) <= 2e-2
+    np.testing.assert_allclose(lse2.cpu().numpy(), l_ref, rtol=0, atol=1e-2)
     if wl.seq == 1:
         vg = layer.cache.v.float()
         for h in range(wl.q_heads):
