@@ -301,6 +301,11 @@ DRIFT_CASES = {
     "bf16_long_S": dict(B=2, Hq=2, Hkv=2, S=6000, D=64, k=32, dt="bf16"),
     # a long row that is not a multiple of 4 (scalar mass loads), GQA
     "bf16_long_ragged_gqa": dict(B=2, Hq=4, Hkv=2, S=4099, D=128, k=32, dt="bf16"),
+    # degenerate budgets: one tracked token; exactly as many positions as the budget
+    "bf16_k1": dict(B=2, Hq=2, Hkv=1, S=100, D=128, k=1, dt="bf16"),
+    "bf16_S_equals_k": dict(B=2, Hq=2, Hkv=2, S=32, D=64, k=32, dt="bf16"),
+    # the largest row and budget the tracking update takes (S = 16384, k = 64)
+    "bf16_max_S_max_k": dict(B=2, Hq=2, Hkv=2, S=16384, D=64, k=64, dt="bf16"),
 }
 
 
