@@ -213,6 +213,9 @@ ATT_CASES = {
     # 8192 keys over two heads: 64 key splits, more than one merge batch
     "bf16_many_splits": C(batch=1, hidden=256, q_heads=2, kv_heads=2, head_dim=128, seq=8192,
                           prompt=4096, block_start=4096, block_len=20, seed=41),
+    # FP8 cache, 8192 keys of one head: 32 key splits
+    "fp8_many_splits": C(batch=1, hidden=256, q_heads=1, kv_heads=1, head_dim=128, seq=8192,
+                         prompt=4096, cache="fp8", block_start=4096, block_len=20, seed=42),
     "bf16_g7_qt128_ragged": C(batch=2, hidden=256, q_heads=7, kv_heads=1, head_dim=128, seq=300,
                               prompt=150, refresh="window+subset", window=8, subset=72, seed=32),
     "bf16_g3_qt64_d64": C(batch=2, hidden=256, q_heads=6, kv_heads=2, head_dim=64, seq=257,
