@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "DLLM_OK", 1: "DLLM_EINVAL", 2: "DLLM_ESIZE", 3: "DLLM_EUNSUP
 EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatter",
            "dllm_refresh_workspace_bytes", "dllm_attention_workspace_bytes",
            "dllm_block_attention", "dllm_drift_check", "dllm_fp8_e4m3_roundtrip",
-           "dllm_last_error")
+           "dllm_set_options", "dllm_last_error")
+DLLM_OPT_DEBUG, DLLM_OPT_WIDE_OFFSETS = 1, 2
 
 _TORCH_DTYPE = {DLLM_F32: torch.float32, DLLM_BF16: torch.bfloat16, DLLM_FP8_E4M3: torch.uint8}
 _DTYPE_CODE = {torch.float32: DLLM_F32, torch.bfloat16: DLLM_BF16}
@@ -73,6 +74,8 @@ def _load():
                                      P, P]
     lib.dllm_fp8_e4m3_roundtrip.restype = i32
     lib.dllm_fp8_e4m3_roundtrip.argtypes = [P, i64, ctypes.c_float, P, P, P]
+    lib.dllm_set_options.restype = i32
+    lib.dllm_set_options.argtypes = [i32]
     lib.dllm_last_error.restype = ctypes.c_char_p
     lib.dllm_last_error.argtypes = []
     return lib
@@ -93,6 +96,16 @@ def _ptr(t):
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _scratch(nbytes: int, device, stream):
+    """A workspace allocated here for one call.  The caching allocator ties a block to the
+    stream current at allocation, so the block is recorded on the launch stream too: it is
+    not handed out again before the library's kernels there are done with it."""
+    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None:
+        t.record_stream(stream)
+    return t
 
 
 class Cache:
@@ -175,7 +188,7 @@ def dllm_refresh_qkv_rope_scatter(cache: Cache, hidden: torch.Tensor, refresh_id
     _expect(q_out, "q_out", (d.batch, n, num_q_heads, d.head_dim), hidden.dtype)
     if workspace is None:
         need = dllm_refresh_workspace_bytes(cache, H, act, n, num_q_heads)
-        workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device) if need else None
+        workspace = _scratch(need, hidden.device, stream) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib.dllm_refresh_qkv_rope_scatter(
         ctypes.byref(cache.c), _ptr(hidden), H, act, _ptr(refresh_idx), n,
@@ -204,8 +217,8 @@ def dllm_block_attention(cache: Cache, q: torch.Tensor, num_q_heads: int, softma
     if attn_mass is not None:
         _expect(attn_mass, "attn_mass", (d.batch, num_q_heads, d.max_seq), torch.float32)
     if workspace is None:
-        workspace = torch.empty(max(1, dllm_attention_workspace_bytes(cache, num_q_heads, n)),
-                                dtype=torch.uint8, device=q.device)
+        workspace = _scratch(max(1, dllm_attention_workspace_bytes(cache, num_q_heads, n)),
+                             q.device, stream)
     _check(lib.dllm_block_attention(
         ctypes.byref(cache.c), _ptr(q), act, num_q_heads, n, float(softmax_scale), _ptr(out),
         _ptr(lse), _ptr(attn_mass), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -237,6 +250,11 @@ def dllm_fp8_e4m3_roundtrip(x: torch.Tensor, scale: float, codes: torch.Tensor,
         _expect(decoded, "decoded", tuple(x.shape), torch.float32)
     _check(lib.dllm_fp8_e4m3_roundtrip(_ptr(x), x.numel(), float(scale), _ptr(codes),
                                        _ptr(decoded), _stream(stream)))
+
+
+def dllm_set_options(flags: int) -> int:
+    """Replace the process-wide DLLM_OPT_* switches; returns the previous value."""
+    return lib.dllm_set_options(int(flags))
 
 
 def dllm_last_error() -> str:

@@ -1,15 +1,47 @@
-// C ABI of the library: argument validation, launch planning and the thread-local error.
-// The operations themselves are documented in include/dllm_cache.h.
+// C ABI of the library: argument validation, launch planning, the process-wide options and
+// the thread-local error.  The operations themselves are documented in include/dllm_cache.h.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
-#include <vector>
+#include <atomic>
+#include <mutex>
 
 #include "dllm_cache.h"
 #include "kernels.hpp"
+
+namespace dllm {
+
+// Process-wide switches (DLLM_OPT_*): read from the environment once, on first use, then
+// only through dllm_set_options.
+namespace {
+std::atomic<int> g_options{-1};
+
+int env_options() {
+  int f = 0;
+  const char* d = getenv("DLLM_DEBUG");
+  if (d && d[0] == '1') f |= DLLM_OPT_DEBUG;
+  const char* w = getenv("DLLM_GEMM_WIDE_OFFSETS");
+  if (w && w[0] == '1') f |= DLLM_OPT_WIDE_OFFSETS;
+  return f;
+}
+}  // namespace
+
+void set_options(int f) { g_options.store(f, std::memory_order_relaxed); }
+
+int options() {
+  int f = g_options.load(std::memory_order_relaxed);
+  if (f < 0) {
+    int expect = -1;
+    g_options.compare_exchange_strong(expect, env_options(), std::memory_order_relaxed);
+    f = g_options.load(std::memory_order_relaxed);
+  }
+  return f;
+}
+
+}  // namespace dllm
 
 namespace {
 
@@ -23,9 +55,55 @@ dllm_status fail(dllm_status code, const char* fmt, ...) {
   return code;
 }
 
-bool debug_mode() {
-  const char* e = getenv("DLLM_DEBUG");
-  return e && e[0] == '1';
+bool debug_mode() { return (dllm::options() & DLLM_OPT_DEBUG) != 0; }
+
+// ---- library-owned device memory (one copy per GPU, zero at load, kept to process end) ----
+
+// First invalid position found by the debug-mode index check: the flat index b * n + i, or
+// 0x7f7f7f7f when every list is valid.
+__device__ __align__(256) int32_t debug_index_report[64];
+
+// Per-device addresses of the library's __device__ arrays.  In host code an array's name is
+// only a host-side stand-in; its device address comes from hipGetSymbolAddress, taken once
+// per device with that device current.
+struct DeviceSymbols {
+  int32_t* debug_report = nullptr;
+  bool ready = false;
+};
+constexpr int kMaxDevices = 64;
+DeviceSymbols g_symbols[kMaxDevices];
+std::mutex g_symbols_mutex;
+
+dllm_status device_symbols(DeviceSymbols** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DLLM_ELAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DLLM_EUNSUPPORTED, "device id %d", dev);
+  std::lock_guard<std::mutex> lock(g_symbols_mutex);
+  DeviceSymbols& d = g_symbols[dev];
+  if (!d.ready) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(debug_index_report));
+    if (e != hipSuccess) return fail(DLLM_ELAUNCH, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+    d.debug_report = (int32_t*)p;
+    d.ready = true;
+  }
+  *out = &d;
+  return DLLM_OK;
+}
+
+// Debug-mode device pass over the refresh index lists: one workgroup per sequence; every
+// position that is out of [0, S) or not above its predecessor is reported, the lowest flat
+// index winning.
+__global__ __launch_bounds__(256) void check_index_lists(const int32_t* idx, int n, int S,
+                                                         int32_t* report) {
+  const int b = blockIdx.x;
+  const int32_t* row = idx + (size_t)b * n;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int32_t x = row[i];
+    const bool bad = x < 0 || x >= S || (i > 0 && x <= row[i - 1]);
+    if (bad) atomicMin(&report[0], (int32_t)((size_t)b * n + i));
+  }
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -77,6 +155,12 @@ dllm_status finish(hipError_t e, hipStream_t s, const char* what) {
 extern "C" {
 
 const char* dllm_last_error(void) { return g_err; }
+
+int32_t dllm_set_options(int32_t flags) {
+  const int prev = dllm::options();
+  dllm::set_options(flags & (DLLM_OPT_DEBUG | DLLM_OPT_WIDE_OFFSETS));
+  return prev;
+}
 
 size_t dllm_cache_bytes(const dllm_cache_desc* d) {
   if (check_desc(d) != DLLM_OK) return 0;
@@ -151,18 +235,28 @@ dllm_status dllm_refresh_qkv_rope_scatter(const dllm_cache* c, const void* hidde
   hipStream_t s = (hipStream_t)stream;
 
   if (debug_mode()) {
-    std::vector<int32_t> h((size_t)M);
-    hipError_t e = hipMemcpyAsync(h.data(), refresh_idx, (size_t)M * 4, hipMemcpyDeviceToHost, s);
+    // Device pass over the lists; the report comes back to the host and the stream is
+    // synchronised (debug mode only).
+    DeviceSymbols* sym = nullptr;
+    st = device_symbols(&sym);
+    if (st) return st;
+    hipError_t e = hipMemsetAsync(sym->debug_report, 0x7f, sizeof(int32_t), s);
+    if (e == hipSuccess) {
+      check_index_lists<<<d.batch, 256, 0, s>>>(refresh_idx, n, d.max_seq, sym->debug_report);
+      e = hipGetLastError();
+    }
+    int32_t flat = 0, val = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync(&flat, sym->debug_report, sizeof flat, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return fail(DLLM_ELAUNCH, "debug index copy: %s", hipGetErrorString(e));
-    for (int b = 0; b < d.batch; ++b)
-      for (int i = 0; i < n; ++i) {
-        const int32_t x = h[(size_t)b * n + i];
-        if (x < 0 || x >= d.max_seq)
-          return fail(DLLM_EINVAL, "refresh_idx[%d][%d] = %d outside [0, %d)", b, i, x, d.max_seq);
-        if (i > 0 && x <= h[(size_t)b * n + i - 1])
-          return fail(DLLM_EINVAL, "refresh_idx[%d] not strictly increasing at %d", b, i);
-      }
+    if (e == hipSuccess && flat != 0x7f7f7f7f)
+      e = hipMemcpy(&val, refresh_idx + flat, sizeof val, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(DLLM_ELAUNCH, "debug index check: %s", hipGetErrorString(e));
+    if (flat != 0x7f7f7f7f) {
+      const int b = flat / n, i = flat % n;
+      if (val < 0 || val >= d.max_seq)
+        return fail(DLLM_EINVAL, "refresh_idx[%d][%d] = %d outside [0, %d)", b, i, val, d.max_seq);
+      return fail(DLLM_EINVAL, "refresh_idx[%d] not strictly increasing at %d (value %d)", b, i, val);
+    }
   }
 
   dllm::RefreshArgs a;

@@ -9,6 +9,10 @@
 
 namespace dllm {
 
+// Process-wide DLLM_OPT_* switches (dllm_set_options; initially from the environment).
+int options();
+void set_options(int flags);
+
 struct RefreshArgs {
   const void* hidden;    // [B, S, H]
   const void* w;         // [N, H]

@@ -39,14 +39,11 @@
  *   - Layouts.  Contiguous, row-major, in the order given.  Indices are int32.
  *   - Errors.  A call returns DLLM_OK or an error code and enqueues nothing on error;
  *     dllm_last_error() then describes the failure.  No C++ exception crosses the ABI.
- *   - Debug mode.  With the environment variable DLLM_DEBUG=1 the refresh call copies the
- *     index list to the host, checks that every list is sorted, unique and in [0, S), and
- *     returns DLLM_EINVAL otherwise; every call synchronises its stream and reports launch
- *     failures.  Without debug mode an index list that breaks the contract is undefined
- *     behaviour.
- *   - DLLM_GEMM_WIDE_OFFSETS=1 makes the refresh of more than 64 rows address its operands
- *     with 64-bit per-lane pointers, the form it otherwise takes only when the hidden states
- *     or the weights span 4 GB or more (same results; for testing that form).
+ *   - Debug mode (option DLLM_OPT_DEBUG, below).  Before launching, the refresh call runs a
+ *     device pass over the index list that checks every list is sorted, unique and in
+ *     [0, S), copies its finding to the host and returns DLLM_EINVAL if a list breaks the
+ *     contract; every call then synchronises its stream and reports launch failures.
+ *     Without debug mode an index list that breaks the contract is undefined behaviour.
  */
 #ifndef DLLM_CACHE_H
 #define DLLM_CACHE_H
@@ -110,7 +107,7 @@ DLLM_API dllm_status dllm_cache_alloc(const dllm_cache_desc *d, void *base, size
 /* Refresh: gather, QKV projection, RoPE, cache scatter (the fused kernel of the
  * Flash-dLLM summary; the positions outside LaCache's invariant region).
  *   hidden       device, [B, S, H] of act_dtype: current hidden states (already normalised)
- *   hidden_size  H; a multiple of 256 (bf16) or 32 (fp32)
+ *   hidden_size  H; a positive multiple of 256 (both activation dtypes)
  *   act_dtype    DLLM_BF16 (cache BF16 or FP8) or DLLM_F32 (cache F32)
  *   refresh_idx  device, [B, n] int32: per sequence, the rows to recompute, sorted,
  *                unique, in [0, S)
@@ -205,6 +202,20 @@ DLLM_API dllm_status dllm_drift_check(const dllm_cache *c, int32_t num_q_heads, 
  * decoded may be NULL. */
 DLLM_API dllm_status dllm_fp8_e4m3_roundtrip(const float *x, int64_t n, float scale, uint8_t *codes,
                                     float *decoded, void *stream);
+
+/* Process-wide switches, for debugging and testing.  Their initial value is read once from
+ * the environment (DLLM_DEBUG=1 sets DLLM_OPT_DEBUG, DLLM_GEMM_WIDE_OFFSETS=1 sets
+ * DLLM_OPT_WIDE_OFFSETS); afterwards only dllm_set_options changes them.
+ *   DLLM_OPT_DEBUG         index lists checked on the device before the refresh, and every
+ *                          call synchronises its stream and reports launch failures
+ *   DLLM_OPT_WIDE_OFFSETS  the refresh of more than 64 rows addresses its operands with 64-bit
+ *                          per-lane pointers, the form it otherwise takes only when the hidden
+ *                          states or the weights span 4 GB or more (same results)
+ * dllm_set_options(flags) replaces the switches (unknown bits are ignored) and returns the
+ * previous value.  Calls already enqueued are not affected. */
+#define DLLM_OPT_DEBUG 1
+#define DLLM_OPT_WIDE_OFFSETS 2
+DLLM_API int32_t dllm_set_options(int32_t flags);
 
 /* Message describing the last error on this thread ("" if none). */
 DLLM_API const char *dllm_last_error(void);

@@ -137,3 +137,14 @@ def test_attention_and_drift_reject_bad_arguments_on_host():
     assert dr(_fake_cache(dt=dkv.DLLM_FP8_E4M3)) == dkv.DLLM_EUNSUPPORTED
     assert L.dllm_fp8_e4m3_roundtrip(ADDR, 10, ctypes.c_float(0.0), ADDR, None, None) == dkv.DLLM_EINVAL
     assert L.dllm_fp8_e4m3_roundtrip(ADDR, 0, ctypes.c_float(1.0), ADDR, None, None) == dkv.DLLM_OK
+
+
+def test_options_switch_round_trips():
+    """dllm_set_options replaces the process-wide switches and returns the previous value;
+    unknown bits are dropped."""
+    prev = dkv.dllm_set_options(dkv.DLLM_OPT_DEBUG | 0x100)
+    try:
+        assert dkv.dllm_set_options(dkv.DLLM_OPT_WIDE_OFFSETS) == dkv.DLLM_OPT_DEBUG
+        assert dkv.dllm_set_options(0) == dkv.DLLM_OPT_WIDE_OFFSETS
+    finally:
+        dkv.dllm_set_options(prev)

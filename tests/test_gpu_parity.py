@@ -57,6 +57,9 @@ REFRESH_CASES = {
     # a hidden size past the split-K limit: ten rows through the tiled GEMM
     "gemm_few_rows_h16896": C(batch=1, hidden=16896, q_heads=1, kv_heads=1, head_dim=64,
                               seq=40, prompt=20, block_start=20, block_len=10, seed=26),
+    # the largest hidden size of the split-K path (its LDS slice is largest here)
+    "splitk_h16384_m64": C(batch=2, hidden=16384, q_heads=1, kv_heads=1, head_dim=128, seq=48,
+                           prompt=16, block_start=16, block_len=32, seed=28),
     # 256 rows, D = 128: the sixteen-wave GEMM form, two row tiles
     "gemm_wide_m256_fp8": C(batch=8, hidden=512, q_heads=2, kv_heads=2, head_dim=128, seq=64,
                             prompt=32, cache="fp8", block_start=32, block_len=32, seed=27),
@@ -120,7 +123,8 @@ def test_refresh_parity_and_untouched_rows(name):
                                   "tiled64_bf16_ragged", "fp8_tiled_d128", "f32_d64",
                                   "f32_d128_gqa", "splitk_fp8_h768_m64", "splitk_bf16_h768_d64",
                                   "splitk_gqa_d64", "splitk_d64_129_heads",
-                                  "splitk_d128_33_heads", "gemm_few_rows_h16896",
+                                  "splitk_d128_33_heads", "splitk_h16384_m64",
+                                  "gemm_few_rows_h16896",
                                   "gemm_wide_m256_fp8"])
 def test_step_reproduces_full_refresh_bitwise(name):
     """Cached step (prefill on H_prev, refresh of R on H_cur) stores exactly what a full
@@ -142,7 +146,7 @@ def test_step_reproduces_full_refresh_bitwise(name):
 
 
 @pytest.mark.parametrize("name", ["skinny_bf16_d128", "fp8_tiled_d128"])
-def test_gemm_wide_offsets_match(name, monkeypatch):
+def test_gemm_wide_offsets_match(name):
     """The refresh GEMM's 64-bit operand addressing (taken for operands of 4 GB or more)
     stores exactly what the 32-bit-offset form stores."""
     wl = REFRESH_CASES[name]
@@ -151,10 +155,13 @@ def test_gemm_wide_offsets_match(name, monkeypatch):
     h_prev = to_dev(inp.hidden_prev, ACT_TORCH[wl.act])
     base = GpuLayer(wl, inp.w)
     q_base = base.prefill(h_prev)
-    monkeypatch.setenv("DLLM_GEMM_WIDE_OFFSETS", "1")
-    wide = GpuLayer(wl, inp.w)
-    q_wide = wide.prefill(h_prev)
-    torch.cuda.synchronize()
+    prev = dkv.dllm_set_options(dkv.DLLM_OPT_WIDE_OFFSETS)
+    try:
+        wide = GpuLayer(wl, inp.w)
+        q_wide = wide.prefill(h_prev)
+        torch.cuda.synchronize()
+    finally:
+        dkv.dllm_set_options(prev)
     assert torch.equal(base.cache.region, wide.cache.region)
     assert torch.equal(q_base, q_wide)
 
@@ -432,13 +439,20 @@ def test_zero_rows_is_a_no_op():
     assert q.numel() == 0 and torch.equal(snap, layer.cache.storage)
 
 
-def test_debug_mode_rejects_bad_index_lists(monkeypatch):
-    """DLLM_DEBUG=1: index lists are checked on the host before any launch."""
+def test_debug_mode_rejects_bad_index_lists():
+    """Debug mode: index lists are checked by a device pass before the refresh launches."""
     wl = REFRESH_CASES["skinny_bf16_d128"]
     inp = synth.make_inputs(wl)
     layer = GpuLayer(wl, inp.w)
     h = to_dev(inp.hidden_prev, torch.bfloat16)
-    monkeypatch.setenv("DLLM_DEBUG", "1")
+    prev = dkv.dllm_set_options(dkv.DLLM_OPT_DEBUG)
+    try:
+        _debug_rejections(layer, h, inp, wl)
+    finally:
+        dkv.dllm_set_options(prev)
+
+
+def _debug_rejections(layer, h, inp, wl):
     unsorted = inp.idx.copy()
     unsorted[0, [0, 1]] = unsorted[0, [1, 0]]          # in range: harmless if not checked
     with pytest.raises(dkv.DllmError) as e:
@@ -450,8 +464,13 @@ def test_debug_mode_rejects_bad_index_lists(monkeypatch):
         layer.refresh(h, dup)
     oob = inp.idx.copy()
     oob[0, -1] = wl.seq                                 # rejected before launching
-    with pytest.raises(dkv.DllmError):
+    with pytest.raises(dkv.DllmError) as e:
         layer.refresh(h, oob)
+    assert "outside" in str(e.value)
+    neg = inp.idx.copy()
+    neg[0, 0] = -1
+    with pytest.raises(dkv.DllmError):
+        layer.refresh(h, neg)
     layer.refresh(h, inp.idx)                           # a valid list still runs
     torch.cuda.synchronize()
 
