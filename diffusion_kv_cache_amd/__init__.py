@@ -25,8 +25,9 @@ STATUS_NAMES = {0: "DLLM_OK", 1: "DLLM_EINVAL", 2: "DLLM_ESIZE", 3: "DLLM_EUNSUP
 EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatter",
            "dllm_refresh_workspace_bytes", "dllm_attention_workspace_bytes",
            "dllm_block_attention", "dllm_drift_check", "dllm_fp8_e4m3_roundtrip",
-           "dllm_set_options", "dllm_last_error")
+           "dllm_set_options", "dllm_block_attention_noalloc", "dllm_last_error")
 DLLM_OPT_DEBUG, DLLM_OPT_WIDE_OFFSETS = 1, 2
+DLLM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _TORCH_DTYPE = {DLLM_F32: torch.float32, DLLM_BF16: torch.bfloat16, DLLM_FP8_E4M3: torch.uint8}
 _DTYPE_CODE = {torch.float32: DLLM_F32, torch.bfloat16: DLLM_BF16}
@@ -69,6 +70,9 @@ def _load():
     lib.dllm_block_attention.restype = i32
     lib.dllm_block_attention.argtypes = [ctypes.POINTER(CCache), P, i32, i32, i32, ctypes.c_float,
                                          P, P, P, P, ctypes.c_size_t, P]
+    lib.dllm_block_attention_noalloc.restype = i32
+    lib.dllm_block_attention_noalloc.argtypes = [ctypes.POINTER(CCache), P, i32, i32, i32,
+                                                 ctypes.c_float, P, P, P, P]
     lib.dllm_drift_check.restype = i32
     lib.dllm_drift_check.argtypes = [ctypes.POINTER(CCache), i32, i32, ctypes.c_float, P, P, P, P,
                                      P, P]
@@ -222,6 +226,26 @@ def dllm_block_attention(cache: Cache, q: torch.Tensor, num_q_heads: int, softma
     _check(lib.dllm_block_attention(
         ctypes.byref(cache.c), _ptr(q), act, num_q_heads, n, float(softmax_scale), _ptr(out),
         _ptr(lse), _ptr(attn_mass), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dllm_block_attention_noalloc(cache: Cache, q: torch.Tensor, num_q_heads: int,
+                                 softmax_scale: float, out: torch.Tensor, lse=None,
+                                 attn_mass=None, stream=None):
+    """dllm_block_attention without a workspace: the library's per-GPU scratch serves instead
+    (calls that overlap on one GPU race)."""
+    d = cache.desc
+    if q.dtype not in _DTYPE_CODE or q.dim() != 4:
+        raise DllmError(DLLM_EINVAL, f"q: expected [B,n,Hq,D] fp32/bf16, got {q.dtype} {tuple(q.shape)}")
+    n = q.shape[1]
+    _expect(q, "q", (d.batch, n, num_q_heads, d.head_dim), q.dtype)
+    _expect(out, "out", (d.batch, n, num_q_heads, d.head_dim), q.dtype)
+    if lse is not None:
+        _expect(lse, "lse", (d.batch, num_q_heads, n), torch.float32)
+    if attn_mass is not None:
+        _expect(attn_mass, "attn_mass", (d.batch, num_q_heads, d.max_seq), torch.float32)
+    _check(lib.dllm_block_attention_noalloc(
+        ctypes.byref(cache.c), _ptr(q), _DTYPE_CODE[q.dtype], num_q_heads, n,
+        float(softmax_scale), _ptr(out), _ptr(lse), _ptr(attn_mass), _stream(stream)))
 
 
 def dllm_drift_check(cache: Cache, num_q_heads: int, k: int, gamma: float,

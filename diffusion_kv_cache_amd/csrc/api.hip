@@ -66,8 +66,14 @@ __device__ __align__(256) int32_t debug_index_report[64];
 // Per-device addresses of the library's __device__ arrays.  In host code an array's name is
 // only a host-side stand-in; its device address comes from hipGetSymbolAddress, taken once
 // per device with that device current.
+// Scratch of the allocation-free attention call (dllm_block_attention_noalloc): the split
+// partial states and, when the caller passes no lse, the log-sum-exp.  Every call on one GPU
+// shares it; nothing in it has to start at zero (each launch writes what it later reads).
+__device__ __align__(256) unsigned char scratch[DLLM_NOALLOC_SCRATCH_BYTES];
+
 struct DeviceSymbols {
   int32_t* debug_report = nullptr;
+  void* scratch = nullptr;       // device address of `scratch` on this GPU
   bool ready = false;
 };
 constexpr int kMaxDevices = 64;
@@ -86,6 +92,10 @@ dllm_status device_symbols(DeviceSymbols** out) {
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(debug_index_report));
     if (e != hipSuccess) return fail(DLLM_ELAUNCH, "hipGetSymbolAddress: %s", hipGetErrorString(e));
     d.debug_report = (int32_t*)p;
+    p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(DLLM_ELAUNCH, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    d.scratch = p;
     d.ready = true;
   }
   *out = &d;
@@ -304,10 +314,16 @@ size_t dllm_attention_workspace_bytes(const dllm_cache_desc* d, int32_t num_q_he
   return round_up(p.part_bytes, 256) + round_up(lse, 256) + 256;
 }
 
-dllm_status dllm_block_attention(const dllm_cache* c, const void* q, int32_t act_dtype,
-                                 int32_t num_q_heads, int32_t n, float softmax_scale, void* out,
-                                 float* lse, float* attn_mass, void* workspace, size_t ws_bytes,
-                                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Body of both attention calls.  noalloc: the workspace is the library's scratch on the
+// current GPU (looked up here), and a shape that needs more than it holds is rejected.
+dllm_status attention_call(const dllm_cache* c, const void* q, int32_t act_dtype,
+                           int32_t num_q_heads, int32_t n, float softmax_scale, void* out,
+                           float* lse, float* attn_mass, void* workspace, size_t ws_bytes,
+                           bool noalloc, void* stream) {
   dllm_status st = check_cache(c);
   if (st) return st;
   const dllm_cache_desc& d = c->desc;
@@ -332,6 +348,16 @@ dllm_status dllm_block_attention(const dllm_cache* c, const void* q, int32_t act
   if (!q || !out) return fail(DLLM_EINVAL, "null q or out");
   if (!aligned16(q) || !aligned16(out)) return fail(DLLM_EINVAL, "q and out must be 16-byte aligned");
   const size_t need = dllm_attention_workspace_bytes(&d, num_q_heads, n);
+  if (noalloc) {
+    if (need > (size_t)DLLM_NOALLOC_SCRATCH_BYTES)
+      return fail(DLLM_ESIZE, "attention needs %zu bytes of scratch; the allocation-free call "
+                  "has %zu", need, (size_t)DLLM_NOALLOC_SCRATCH_BYTES);
+    DeviceSymbols* sym = nullptr;
+    st = device_symbols(&sym);
+    if (st) return st;
+    workspace = sym->scratch;
+    ws_bytes = DLLM_NOALLOC_SCRATCH_BYTES;
+  }
   if (ws_bytes < need) return fail(DLLM_ESIZE, "attention workspace needs %zu bytes, got %zu", need, ws_bytes);
   if (!workspace) return fail(DLLM_EINVAL, "null workspace");
   dllm::AttnPlan p = dllm::plan_attention(d.batch, n, num_q_heads, d.num_kv_heads, d.max_seq,
@@ -358,6 +384,25 @@ dllm_status dllm_block_attention(const dllm_cache* c, const void* q, int32_t act
   a.scale = softmax_scale;
   hipStream_t s = (hipStream_t)stream;
   return finish(dllm::launch_attention(a, p, s), s, "attention");
+}
+
+}  // namespace
+
+extern "C" {
+
+dllm_status dllm_block_attention(const dllm_cache* c, const void* q, int32_t act_dtype,
+                                 int32_t num_q_heads, int32_t n, float softmax_scale, void* out,
+                                 float* lse, float* attn_mass, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  return attention_call(c, q, act_dtype, num_q_heads, n, softmax_scale, out, lse, attn_mass,
+                        workspace, ws_bytes, false, stream);
+}
+
+dllm_status dllm_block_attention_noalloc(const dllm_cache* c, const void* q, int32_t act_dtype,
+                                         int32_t num_q_heads, int32_t n, float softmax_scale,
+                                         void* out, float* lse, float* attn_mass, void* stream) {
+  return attention_call(c, q, act_dtype, num_q_heads, n, softmax_scale, out, lse, attn_mass,
+                        nullptr, 0, true, stream);
 }
 
 dllm_status dllm_drift_check(const dllm_cache* c, int32_t num_q_heads, int32_t k, float gamma,

@@ -172,6 +172,22 @@ DLLM_API dllm_status dllm_block_attention(const dllm_cache *c, const void *q, in
                                  void *out, float *lse, float *attn_mass, void *workspace,
                                  size_t ws_bytes, void *stream);
 
+/* Block attention that allocates nothing and takes no workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Arguments and results are those of dllm_block_attention without
+ * `workspace` / `ws_bytes`.  The split partial states (and the log-sum-exp when lse is NULL)
+ * go to a library-owned device array of DLLM_NOALLOC_SCRATCH_BYTES bytes, one per GPU the
+ * library runs on, held until the process ends.  Every call on one GPU shares that array,
+ * so calls that overlap on one GPU (different streams or threads) race: issue them one
+ * after another.  The call itself allocates and frees nothing.
+ * Errors: those of dllm_block_attention, and DLLM_ESIZE when the shape needs more scratch
+ * than DLLM_NOALLOC_SCRATCH_BYTES (dllm_attention_workspace_bytes gives the need). */
+#define DLLM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+DLLM_API dllm_status dllm_block_attention_noalloc(const dllm_cache *c, const void *q,
+                                                  int32_t act_dtype, int32_t num_q_heads,
+                                                  int32_t n, float softmax_scale, void *out,
+                                                  float *lse, float *attn_mass, void *stream);
+
 /* Attention-aware drift test and tracking update (Elastic-Cache core idea; Flash-dLLM
  * tracking budget).  Call after this step's refresh and attention.
  *   k            tracked tokens per (b, h), 1..64 (32 by default)

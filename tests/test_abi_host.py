@@ -73,8 +73,8 @@ def test_cache_alloc_carves_regions_without_touching_memory():
     assert st == dkv.DLLM_EUNSUPPORTED
 
 
-def _fake_cache(dt=dkv.DLLM_BF16, D=128, Hkv=4):
-    d = _desc(B=2, Hkv=Hkv, S=64, D=D, dt=dt, group=D if dt == dkv.DLLM_FP8_E4M3 else 0)
+def _fake_cache(dt=dkv.DLLM_BF16, D=128, Hkv=4, S=64):
+    d = _desc(B=2, Hkv=Hkv, S=S, D=D, dt=dt, group=D if dt == dkv.DLLM_FP8_E4M3 else 0)
     st, c = _alloc(d, 1 << 40, dkv.dllm_cache_bytes(d))
     assert st == 0
     return c
@@ -135,6 +135,16 @@ def test_attention_and_drift_reject_bad_arguments_on_host():
     assert dr(c, k=0) == dkv.DLLM_EINVAL and dr(c, k=65) == dkv.DLLM_EINVAL
     assert dr(c, hq=3) == dkv.DLLM_EINVAL
     assert dr(_fake_cache(dt=dkv.DLLM_FP8_E4M3)) == dkv.DLLM_EUNSUPPORTED
+    # the allocation-free call validates the same way, and refuses shapes beyond its scratch
+    na = lambda cc, **kw: L.dllm_block_attention_noalloc(
+        ctypes.byref(cc), kw.get("q", ADDR), 1, kw.get("hq", 4), kw.get("n", 8), 0.088, ADDR,
+        None, None, None)
+    assert na(c, hq=5) == dkv.DLLM_EINVAL and na(c, q=None) == dkv.DLLM_EINVAL
+    assert na(c, n=0) == dkv.DLLM_OK
+    big = _fake_cache(S=65536, Hkv=1)
+    assert L.dllm_attention_workspace_bytes(ctypes.byref(big.desc), 8, 1024) > \
+        dkv.DLLM_NOALLOC_SCRATCH_BYTES
+    assert na(big, hq=8, n=1024) == dkv.DLLM_ESIZE and "scratch" in dkv.dllm_last_error()
     assert L.dllm_fp8_e4m3_roundtrip(ADDR, 10, ctypes.c_float(0.0), ADDR, None, None) == dkv.DLLM_EINVAL
     assert L.dllm_fp8_e4m3_roundtrip(ADDR, 0, ctypes.c_float(1.0), ADDR, None, None) == dkv.DLLM_OK
 
