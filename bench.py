@@ -10,7 +10,9 @@ Default workload: the LLaDA-8B-shaped bf16 layer, B=1, hidden 4096, 32 heads x 1
 (512 prompt + 512 response), 32 refreshed rows per step.
 
 Prints one JSON line (metric, value in refreshed tokens/s, roofline of the dominant kernel,
-the CPU oracle's rate on a bounded sample of the same workload).
+the CPU oracle's rate on a bounded sample of the same workload).  The other workloads (batched,
+GQA scattered refresh with drift, long-context FP8) are measured in the same run and reported
+under "configs", each with its step time, rate and per-call rooflines.
 """
 from __future__ import annotations
 
@@ -123,14 +125,14 @@ class Layer:
             self.buf = torch.zeros((wl.batch, wl.q_heads, k, 2, wl.head_dim), dtype=tdt, device=dev)
 
 
-def run(args):
+def measure(args, wl):
+    """Time K steps of workload `wl` (after W warm-up steps) and each call of the step alone;
+    returns the per-workload record and the host inputs (for the CPU baseline)."""
     import torch
 
     import diffusion_kv_cache_amd as dkv
 
-    wl = synth.WORKLOADS[args.config]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     act = torch.float32 if wl.act == "f32" else torch.bfloat16
     log(f"[bench] workload {wl.name}: {wl.description}")
     t0 = time.time()
@@ -190,14 +192,14 @@ def run(args):
         for nm in names:
             calls[nm](ly)
 
-    for s in range(args.warmup):
-        step(layers[s % L])
+    for s_ in range(args.warmup):
+        step(layers[s_ % L])
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
-    for s in range(args.steps):
-        step(layers[(args.warmup + s) % L])
+    for s_ in range(args.steps):
+        step(layers[(args.warmup + s_) % L])
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -232,28 +234,27 @@ def run(args):
         e1.record()
         torch.cuda.synchronize()
         per[nm] = e0.elapsed_time(e1) / burst * 1e3
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; per call (us, {burst} back to "
-        f"back): " + ", ".join(f"{k_}={v:.1f}" for k_, v in per.items()))
+    log(f"[bench] {wl.name}: {args.steps} steps: {ms_per_step * 1e3:.1f} us/step; per call (us, "
+        f"{burst} back to back): " + ", ".join(f"{k_}={v:.1f}" for k_, v in per.items()))
 
     works = work_model(wl)
     dtype = "f32" if wl.act == "f32" else "bf16"
     entries = {nm: roofline_entry(nm, works[nm], per[nm], dtype) for nm in names}
     for nm, e in entries.items():
-        log(f"[bench] {nm}: {e['achieved']} {e['unit']} ({100 * e['frac']:.1f}% of {e['bound']} peak)")
+        log(f"[bench] {wl.name} {nm}: {e['achieved']} {e['unit']} ({100 * e['frac']:.1f}% of "
+            f"{e['bound']} peak)")
     dom = max(names, key=lambda nm: per[nm])
     roof = dict(entries[dom])
     roof["traffic"] = measured_traffic(wl.name, dom)
-
-    result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "refreshed tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if wl.act == "f32" else "bf16",
-        "data": "synthetic (seeded, shaped like the workload; random-init weights)",
-        "config": {"workload": f"{wl.name}: {wl.description}", "global_batch": B, "seq_len": S,
-                   "refreshed_per_seq": n, "hidden": wl.hidden, "q_heads": Hq,
-                   "kv_heads": wl.kv_heads, "head_dim": D, "cache_dtype": wl.cache,
-                   "tracking": track, "layer_instances": L, "parallelism": "none (1 GPU)"},
+    for nm, e in entries.items():
+        e["traffic"] = measured_traffic(wl.name, nm)
+    rec = {
+        "value": round(value, 1), "unit": "refreshed tokens/s",
+        "ms_per_step": round(ms_per_step, 5),
+        "workload": f"{wl.name}: {wl.description}",
+        "global_batch": B, "seq_len": S, "refreshed_per_seq": n, "hidden": wl.hidden,
+        "q_heads": Hq, "kv_heads": wl.kv_heads, "head_dim": D, "cache_dtype": wl.cache,
+        "tracking": track, "layer_instances": L,
         "per_call_us": {k_: round(v, 2) for k_, v in per.items()},
         "per_call_back_to_back": burst,
         "rooflines": entries,
@@ -261,9 +262,44 @@ def run(args):
     }
     del layers
     torch.cuda.empty_cache()
+    return rec, inp
+
+
+def run(args):
+    import torch
+
+    wl = synth.WORKLOADS[args.config]
+    torch.cuda.set_device(torch.device("cuda:0"))
+    head, inp = measure(args, wl)
+    others = {}
+    for name in [c for c in args.also.split(",") if c and c != args.config]:
+        rec, _ = measure(args, synth.WORKLOADS[name])
+        others[name] = rec
+
+    result = {
+        "metric": METRIC, "value": head["value"], "unit": head["unit"],
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if wl.act == "f32" else "bf16",
+        "data": "synthetic (seeded, shaped like the workload; random-init weights)",
+        "config": {"workload": head["workload"], "global_batch": head["global_batch"],
+                   "seq_len": head["seq_len"], "refreshed_per_seq": head["refreshed_per_seq"],
+                   "hidden": head["hidden"], "q_heads": head["q_heads"],
+                   "kv_heads": head["kv_heads"], "head_dim": head["head_dim"],
+                   "cache_dtype": head["cache_dtype"], "tracking": head["tracking"],
+                   "layer_instances": head["layer_instances"], "parallelism": "none (1 GPU)"},
+        "per_call_us": head["per_call_us"],
+        "per_call_back_to_back": head["per_call_back_to_back"],
+        "rooflines": head["rooflines"],
+        "roofline": head["roofline"],
+    }
+    if others:
+        # the other workloads, measured the same way in the same run (not the headline)
+        result["configs"] = others
     if args.copy_calibration:
         # A plain device copy of known size, so HBM byte counters read under a profiler can be
         # scaled by what they report for a copy (reads = writes = the buffer size).
+        dev = torch.device("cuda:0")
         nb = args.copy_calibration << 20
         src = torch.empty(nb, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -275,6 +311,17 @@ def run(args):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, inp, budget_s: float):
@@ -296,24 +343,32 @@ def cpu_baseline(wl, inp, budget_s: float):
         _, _, mp = oracle.attend(ws, qp, cache, want_mass=True)
         T, buf = oracle.track(cache, mp, ws.track_k)
     log(f"[cpu] oracle setup {time.time() - t0:.1f}s on {cores} threads")
-    runs, t_total = 0, 0.0
-    while runs == 0 or t_total < budget_s / 2:
-        t0 = time.time()
-        oracle.refresh_rows(cache, h_cur, sub.w, sub.idx)
-        q = oracle.queries(ws, h_cur, sub.w, sub.idx)
-        _, _, m = oracle.attend(ws, q, cache, want_mass=track)
-        if track:
-            oracle.drift(buf, T, cache.k, cache.v, float(np.float32(ws.gamma)))
-            oracle.track(cache, m, ws.track_k)
-        t_total += time.time() - t0
-        runs += 1
-    rate = runs * nb * wl.n_refresh / t_total
-    log(f"[cpu] {runs} oracle step(s) in {t_total:.2f}s: {rate:.1f} tokens/s")
+    # Three runs, each repeating the cached step for a third of the budget; the median rate
+    # is reported.
+    rates, total_runs = [], 0
+    for _ in range(3):
+        runs, t_total = 0, 0.0
+        while runs == 0 or t_total < budget_s / 3:
+            t0 = time.time()
+            oracle.refresh_rows(cache, h_cur, sub.w, sub.idx)
+            q = oracle.queries(ws, h_cur, sub.w, sub.idx)
+            _, _, m = oracle.attend(ws, q, cache, want_mass=track)
+            if track:
+                oracle.drift(buf, T, cache.k, cache.v, float(np.float32(ws.gamma)))
+                oracle.track(cache, m, ws.track_k)
+            t_total += time.time() - t0
+            runs += 1
+        rates.append(runs * nb * wl.n_refresh / t_total)
+        total_runs += runs
+    rate = float(np.median(rates))
+    log(f"[cpu] {total_runs} oracle step(s) in 3 runs: " + ", ".join(f"{r:.1f}" for r in rates)
+        + f" tokens/s; median {rate:.1f}")
     return {"value": round(rate, 2), "unit": "refreshed tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "runs_tokens_per_s": [round(r, 2) for r in rates],
             "sample": f"cached step (refresh + attention{' + mass + drift + top-k' if track else ''})"
-                      f" of {nb} of {wl.batch} sequence(s), {runs} run(s), prefill untimed, "
-                      f"fp64 C oracle with OpenMP"}
+                      f" of {nb} of {wl.batch} sequence(s), median of 3 runs ({total_runs} steps "
+                      f"in all), prefill untimed, fp64 C oracle with OpenMP"}
 
 
 def main():
@@ -321,7 +376,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--config", default="c2", choices=sorted(synth.WORKLOADS),
+                    help="the headline workload of the JSON line")
+    ap.add_argument("--also", default="c3,c4,c5",
+                    help="other workloads measured in the same run, reported under 'configs' "
+                         "(comma-separated; '' for none)")
     ap.add_argument("--layers", type=int, default=0, help="layer instances to rotate (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
