@@ -226,8 +226,12 @@ __device__ __forceinline__ void rope_turns(int i, int D, double base, float& hi,
 // (fma), its integer turns are dropped exactly, and the hardware sin/cos (argument in turns)
 // see a fraction in [-0.5, 0.5].
 // Every multiply-add is written as an explicit fmaf so that all kernels using these helpers
-// round identically, whatever the compiler contracts elsewhere.
+// round identically, whatever the compiler contracts elsewhere.  Contraction is off here: the
+// split needs a - rint(a) of the ROUNDED product a; fused into fma(pos, hi, -rint(a)) it would
+// count the product's rounding residual twice (an angle error of up to half an ulp of
+// pos * hi turns, 2e-4 rad at position 4000).
 __device__ __forceinline__ void rope_sincos(int pos, float hi, float lo, float& s, float& c) {
+#pragma clang fp contract(off)
   const float p = (float)pos;
   const float a = p * hi;
   const float e = fmaf(p, hi, -a);

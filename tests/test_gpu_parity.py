@@ -1,9 +1,11 @@
 """GPU parity: the HIP path, called through the C ABI, against the CPU oracle on the same
 seeded inputs, at sizes that span several tiles and ragged tails.
 
-Bars: K/V rows written to the cache <= 1e-2 max relative error per (b, head) slice, FP8
-codes <= 1 e4m3 step (scales <= 1e-2), attention output <= 2e-2; untouched rows, guard bands
-and index outputs bit-exact; drift decisions exact (away from |sigma - gamma| < 1e-5).
+Bars: K/V rows written to the cache <= 1e-2 max relative error per (b, head) slice; FP8 codes
+each the correct rounding of a value within the fp32 projection's error bound of the oracle's
+exact value (codes more than one e4m3 step from the oracle's at most 1 in 10^4; scales
+<= 1e-2); attention output <= 2e-2; untouched rows, guard bands and index outputs bit-exact;
+drift decisions exact (away from |sigma - gamma| < 1e-5).
 """
 import math
 
@@ -13,7 +15,8 @@ import torch
 
 import oracle
 import synth
-from gpu_cases import (ACT_TORCH, GpuLayer, check_fp8_rows, say, slice_rel_err, to_dev)
+from gpu_cases import (ACT_TORCH, GpuLayer, check_fp8_rows, elem_rel_err, fp8_delta, say,
+                       slice_rel_err, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -107,12 +110,15 @@ def test_refresh_parity_and_untouched_rows(name):
         if wl.cache != "fp8":
             assert slice_rel_err(kg[b][:, rows], ref.k[b][:, rows], (0,)) <= 1e-2
             assert slice_rel_err(vg[b][:, rows], ref.v[b][:, rows], (0,)) <= 1e-2
+            say(f"  b={b} elementwise (floor 1e-2): K {elem_rel_err(kg[b][:, rows], ref.k[b][:, rows], (0,)):.2e} "
+                f"V {elem_rel_err(vg[b][:, rows], ref.v[b][:, rows], (0,)):.2e}")
         else:  # one e4m3 step near amax is 1/14 of the row's range: the bar is on codes
             for nm in ("k", "v"):
                 gc = getattr(c, nm).cpu().numpy()[b][:, rows]
                 gs = getattr(c, nm + "_scale").cpu().numpy()[b][:, rows]
+                delta = fp8_delta(wl, h_cur[b, rows], inp.w, nm).transpose(1, 0, 2)
                 far = check_fp8_rows(gc, gs, getattr(ref, nm + "_exact")[b][:, rows],
-                                     getattr(ref, nm + "_codes")[b][:, rows])
+                                     getattr(ref, nm + "_codes")[b][:, rows], delta)
                 assert far <= gc.size // 10000
                 np.testing.assert_allclose(gs, getattr(ref, nm + "_scale")[b][:, rows], rtol=1e-2)
     qg = q.float().cpu().numpy()
