@@ -71,6 +71,8 @@ def _load():
         lib.orc_linear.argtypes = [P, i64, i64, P, P, i64, P]
         lib.orc_rope_rows.argtypes = [P, i64, i32, i32, P, f64]
         lib.orc_attention.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, f64, P, P, P]
+        lib.orc_attention_state.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f64, P, P,
+                                            P]
         lib.orc_topk.argtypes = [P, i64, i32, i32, P]
         lib.orc_drift.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, f64, P, P]
         _lib = lib
@@ -162,6 +164,24 @@ def attention(q, k, v, scale: float, want_lse=True, want_mass=False):
     _load().orc_attention(_p(q), _p(k), _p(v), B, n, Hq, Hkv, S, D, float(scale), _p(out),
                           _p(lse), _p(mass))
     return out, lse, mass
+
+
+def attention_state(q, k, v, scale: float, keep):
+    """Online-softmax state over the keys kept by keep [B, S] (bool): q [B, n, Hq, D], k, v
+    [B, Hkv, S, D] -> (m [B, Hq, n], l [B, Hq, n], o_tilde [B, n, Hq, D]), natural log."""
+    q = _c(q, np.float64)
+    k = _c(k, np.float64)
+    v = _c(v, np.float64)
+    B, n, Hq, D = q.shape
+    _, Hkv, S, _ = k.shape
+    keep = _c(np.asarray(keep, dtype=bool).astype(np.uint8), np.uint8)
+    assert keep.shape == (B, S) and k.shape == v.shape == (B, Hkv, S, D) and Hq % Hkv == 0
+    m = np.empty((B, Hq, n), np.float64)
+    ll = np.empty((B, Hq, n), np.float64)
+    o = np.empty_like(q)
+    _load().orc_attention_state(_p(q), _p(k), _p(v), _p(keep), B, n, Hq, Hkv, S, D, float(scale),
+                                _p(m), _p(ll), _p(o))
+    return m, ll, o
 
 
 def topk(a: np.ndarray, k: int) -> np.ndarray:
@@ -302,6 +322,22 @@ def queries(wl, hidden: np.ndarray, w: np.ndarray, idx, batches=None, q_heads=No
 def attend(wl, q: np.ndarray, cache: Cache, want_mass=False):
     """O5/O6 over the stored cache values: (out, lse, mass); out is left in float64."""
     return attention(q, cache.k, cache.v, 1.0 / math.sqrt(wl.head_dim), True, want_mass)
+
+
+def facache_reference(wl, q_all: np.ndarray, cache: Cache, block_start):
+    """What a FACache attention step must give for query rows of every position: the
+    attention output and log-sum-exp of every row over all keys (the plain definition), and,
+    for the rows outside each sequence's block [block_start[b], + n), the online-softmax
+    state over the keys outside the block (LaCache Technical Summary, Methodology 1).
+    q_all: [B, S, Hq, D].  Returns out [B,S,Hq,D], lse [B,Hq,S], (m, l, o_tilde) as in
+    attention_state and the invariant-row mask [B, S]."""
+    B, S, n = wl.batch, wl.seq, wl.n_refresh
+    out, lse, _ = attend(wl, q_all, cache)
+    inv = np.ones((B, S), bool)
+    for b in range(B):
+        inv[b, block_start[b]:block_start[b] + n] = False
+    m, ll, o = attention_state(q_all, cache.k, cache.v, 1.0 / math.sqrt(wl.head_dim), inv)
+    return out, lse, (m, ll, o), inv
 
 
 def track(cache: Cache, mass: np.ndarray, k: int):

@@ -31,6 +31,11 @@
  *                       attention over the full context), plus log-sum-exp and the column
  *                       attention mass used to rank the most-attended tokens (Flash-dLLM
  *                       summary, paragraph on selective cache tracking).
+ *   orc_attention_state the online-softmax state (running maximum m, normaliser l,
+ *                       unnormalised output O~) of attention over a subset of the keys, the
+ *                       quantities FACache keeps for query rows outside the current block
+ *                       over the keys of the invariant region (LaCache Technical Summary,
+ *                       Methodology 1, FACache).
  *   orc_topk            the k most-attended tokens per head (tracking budget 32).
  *   orc_drift           Elastic-Cache core idea: cosine similarity of the previous step's
  *                       most-attended tokens; refresh when it drops below gamma.
@@ -237,6 +242,50 @@ void orc_attention(const double *q, const double *k, const double *v, int B, int
                     for (int j = 0; j < S; j++) a[j] += p[j];
             }
             free(p);
+        }
+}
+
+/* Online-softmax state over the keys j with keep[b * S + j] != 0, for every (b, i, h):
+ *   z_j = <q_i, K_j> * scale,  m = max z_j,  l = sum exp(z_j - m),  O~ = sum exp(z_j - m) V_j
+ * (the running maximum, normaliser and unnormalised output accumulator that FACache stores;
+ * O = O~ / l and m + log l are then the attention output and log-sum-exp over those keys).
+ * No key kept: m = -inf, l = 0, O~ = 0.  m, l: [B, Hq, n]; o: [B, n, Hq, D]. */
+void orc_attention_state(const double *q, const double *k, const double *v, const uint8_t *keep,
+                         int B, int n, int Hq, int Hkv, int S, int D, double scale,
+                         double *m_out, double *l_out, double *o_out)
+{
+    int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < Hq; h++) {
+            int g = h / G;
+            const double *K = k + ((int64_t)(b * Hkv + g) * S) * D;
+            const double *V = v + ((int64_t)(b * Hkv + g) * S) * D;
+            const uint8_t *kp = keep + (int64_t)b * S;
+            double *z = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+            for (int i = 0; i < n; i++) {
+                const double *qi = q + (((int64_t)b * n + i) * Hq + h) * D;
+                double *oi = o_out + (((int64_t)b * n + i) * Hq + h) * D;
+                double m = -INFINITY;
+                for (int j = 0; j < S; j++) {
+                    if (!kp[j]) continue;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; d++) dot += qi[d] * K[(int64_t)j * D + d];
+                    z[j] = dot * scale;
+                    if (z[j] > m) m = z[j];
+                }
+                double l = 0.0;
+                for (int d = 0; d < D; d++) oi[d] = 0.0;
+                for (int j = 0; j < S; j++) {
+                    if (!kp[j]) continue;
+                    double p = exp(z[j] - m);
+                    l += p;
+                    for (int d = 0; d < D; d++) oi[d] += p * V[(int64_t)j * D + d];
+                }
+                m_out[((int64_t)(b * Hq + h)) * n + i] = m;
+                l_out[((int64_t)(b * Hq + h)) * n + i] = l;
+            }
+            free(z);
         }
 }
 

@@ -270,6 +270,55 @@ def test_attention_split_merge_identity():
     np.testing.assert_allclose(m + np.log(wts.sum(0)), lse, rtol=1e-13)
 
 
+@pytest.mark.parametrize("B,n,Hq,Hkv,S,D", [(1, 3, 2, 2, 9, 4), (2, 4, 6, 2, 33, 8)])
+def test_attention_state_matches_library_softmax_on_the_kept_keys(B, n, Hq, Hkv, S, D):
+    """FACache state over a key subset: o_tilde / l is the library attention over the kept
+    keys only, and m + log l their log-sum-exp; m is the largest kept logit."""
+    r = rng(16 + S)
+    q = r.standard_normal((B, n, Hq, D))
+    k = r.standard_normal((B, Hkv, S, D))
+    v = r.standard_normal((B, Hkv, S, D))
+    keep = r.random((B, S)) < 0.6
+    keep[:, 0] = True
+    m, ll, o = oracle.attention_state(q, k, v, 0.4, keep)
+    G = Hq // Hkv
+    for b in range(B):
+        ks, vs = k[b:b + 1, :, keep[b]], v[b:b + 1, :, keep[b]]
+        o2, l2, _ = _torch_sdpa(q[b:b + 1], ks, vs, 0.4)
+        np.testing.assert_allclose(o[b] / ll[b].transpose(1, 0)[..., None], o2[0], rtol=1e-12,
+                                   atol=1e-13)
+        np.testing.assert_allclose(m[b] + np.log(ll[b]), l2[0], rtol=1e-12)
+        logits = np.einsum("nhd,hsd->hns", q[b], np.repeat(ks[0], G, axis=0)) * 0.4
+        np.testing.assert_allclose(m[b], logits.max(-1), rtol=1e-14)
+
+
+def test_attention_state_of_a_partition_merges_to_full_attention():
+    """The FACache identity on the state itself: the states over the invariant keys and over
+    the block keys, merged with their maxima, reproduce full attention; all keys kept gives
+    full attention directly; no key kept gives (-inf, 0, 0)."""
+    r = rng(17)
+    B, n, Hq, Hkv, S, D = 2, 5, 4, 2, 70, 16
+    q = r.standard_normal((B, n, Hq, D))
+    k = r.standard_normal((B, Hkv, S, D))
+    v = r.standard_normal((B, Hkv, S, D))
+    full, lse, _ = oracle.attention(q, k, v, 0.25)
+    blk = np.zeros((B, S), bool)
+    blk[0, 20:52] = True
+    blk[1, 38:70] = True
+    mu, lu, ou = oracle.attention_state(q, k, v, 0.25, ~blk)
+    mg, lg, og = oracle.attention_state(q, k, v, 0.25, blk)
+    mm = np.maximum(mu, mg)
+    wu, wg = np.exp(mu - mm), np.exp(mg - mm)              # B Hq n
+    den = (lu * wu + lg * wg).transpose(0, 2, 1)[..., None]
+    merged = (ou * wu.transpose(0, 2, 1)[..., None] + og * wg.transpose(0, 2, 1)[..., None]) / den
+    np.testing.assert_allclose(merged, full, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(mm + np.log(lu * wu + lg * wg), lse, rtol=1e-13)
+    ma, la, oa = oracle.attention_state(q, k, v, 0.25, np.ones((B, S), bool))
+    np.testing.assert_allclose(oa / la.transpose(0, 2, 1)[..., None], full, rtol=1e-12, atol=1e-14)
+    m0, l0, o0 = oracle.attention_state(q, k, v, 0.25, np.zeros((B, S), bool))
+    assert np.all(m0 == -np.inf) and not l0.any() and not o0.any()
+
+
 # ---------------------------------------------------------------- top-k + drift ----------
 
 def test_topk_brute_force_with_ties():
