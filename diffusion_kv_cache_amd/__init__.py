@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "DLLM_OK", 1: "DLLM_EINVAL", 2: "DLLM_ESIZE", 3: "DLLM_EUNSUP
 EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatter",
            "dllm_refresh_workspace_bytes", "dllm_attention_workspace_bytes",
            "dllm_block_attention", "dllm_drift_check", "dllm_fp8_e4m3_roundtrip",
-           "dllm_set_options", "dllm_block_attention_noalloc", "dllm_last_error")
+           "dllm_set_options", "dllm_block_attention_noalloc", "dllm_facache_state_bytes",
+           "dllm_facache_attention", "dllm_last_error")
 DLLM_OPT_DEBUG, DLLM_OPT_WIDE_OFFSETS = 1, 2
 DLLM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -73,6 +74,11 @@ def _load():
     lib.dllm_block_attention_noalloc.restype = i32
     lib.dllm_block_attention_noalloc.argtypes = [ctypes.POINTER(CCache), P, i32, i32, i32,
                                                  ctypes.c_float, P, P, P, P]
+    lib.dllm_facache_state_bytes.restype = ctypes.c_size_t
+    lib.dllm_facache_state_bytes.argtypes = [ctypes.POINTER(CacheDesc), i32]
+    lib.dllm_facache_attention.restype = i32
+    lib.dllm_facache_attention.argtypes = [ctypes.POINTER(CCache), P, P, P, i32, i32, ctypes.c_float,
+                                           P, i32, P, P, P]
     lib.dllm_drift_check.restype = i32
     lib.dllm_drift_check.argtypes = [ctypes.POINTER(CCache), i32, i32, ctypes.c_float, P, P, P, P,
                                      P, P]
@@ -246,6 +252,37 @@ def dllm_block_attention_noalloc(cache: Cache, q: torch.Tensor, num_q_heads: int
     _check(lib.dllm_block_attention_noalloc(
         ctypes.byref(cache.c), _ptr(q), _DTYPE_CODE[q.dtype], num_q_heads, n,
         float(softmax_scale), _ptr(out), _ptr(lse), _ptr(attn_mass), _stream(stream)))
+
+
+def dllm_facache_state_bytes(cache: Cache, num_q_heads: int) -> int:
+    return lib.dllm_facache_state_bytes(ctypes.byref(cache.desc), num_q_heads)
+
+
+def dllm_facache_attention(cache: Cache, q_cache: torch.Tensor, q_block: torch.Tensor,
+                           block_start: torch.Tensor, num_q_heads: int, softmax_scale: float,
+                           fa_state: torch.Tensor, build: bool, out: torch.Tensor, lse=None,
+                           stream=None):
+    """q_cache [B,S,Hq,D] bf16 (in/out), q_block [B,n,Hq,D] bf16, block_start [B] int32,
+    fa_state a float32 tensor of dllm_facache_state_bytes(...) bytes, out [B,S,Hq,D] bf16,
+    lse [B,Hq,S] fp32 or None."""
+    d = cache.desc
+    B, S, D = d.batch, d.max_seq, d.head_dim
+    n = q_block.shape[1] if q_block.dim() == 4 else -1
+    _expect(q_cache, "q_cache", (B, S, num_q_heads, D), torch.bfloat16)
+    _expect(q_block, "q_block", (B, n, num_q_heads, D), torch.bfloat16)
+    _expect(block_start, "block_start", (B,), torch.int32)
+    _expect(out, "out", (B, S, num_q_heads, D), torch.bfloat16)
+    if lse is not None:
+        _expect(lse, "lse", (B, num_q_heads, S), torch.float32)
+    need = dllm_facache_state_bytes(cache, num_q_heads)
+    if fa_state.dtype != torch.float32 or not fa_state.is_contiguous() or \
+            fa_state.numel() * 4 < need or fa_state.device.type != "cuda":
+        raise DllmError(DLLM_EINVAL, f"fa_state: expected a contiguous cuda float32 tensor of at "
+                                     f"least {need} bytes")
+    _check(lib.dllm_facache_attention(
+        ctypes.byref(cache.c), _ptr(q_cache), _ptr(q_block), _ptr(block_start), n, num_q_heads,
+        float(softmax_scale), _ptr(fa_state), int(bool(build)), _ptr(out), _ptr(lse),
+        _stream(stream)))
 
 
 def dllm_drift_check(cache: Cache, num_q_heads: int, k: int, gamma: float,

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdllm_cache.so")
 SOURCES = ["api.hip", "refresh.hip", "refresh_splitk.hip", "attention.hip", "attention_fwd.hip",
-           "attention_fused.hip", "drift.hip"]
+           "attention_fused.hip", "attention_facache.hip", "drift.hip"]
 ARCH = os.environ.get("DLLM_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -30,6 +30,7 @@ FLAGS = [
 # scores of finite inputs are finite, and masked keys are -inf, which stays honoured.
 EXTRA = {"attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
          "attention_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+         "attention_facache.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
          "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 

@@ -405,6 +405,54 @@ dllm_status dllm_block_attention_noalloc(const dllm_cache* c, const void* q, int
                         nullptr, 0, true, stream);
 }
 
+size_t dllm_facache_state_bytes(const dllm_cache_desc* d, int32_t num_q_heads) {
+  if (check_desc(d) != DLLM_OK || num_q_heads <= 0 || num_q_heads % d->num_kv_heads) return 0;
+  return (size_t)d->batch * num_q_heads * d->max_seq * (d->head_dim + 2) * sizeof(float);
+}
+
+dllm_status dllm_facache_attention(const dllm_cache* c, void* q_cache, const void* q_block,
+                                   const int32_t* block_start, int32_t n, int32_t num_q_heads,
+                                   float softmax_scale, float* fa_state, int32_t build, void* out,
+                                   float* lse, void* stream) {
+  dllm_status st = check_cache(c);
+  if (st) return st;
+  const dllm_cache_desc& d = c->desc;
+  if (d.kv_dtype != DLLM_BF16) return fail(DLLM_EUNSUPPORTED, "FACache attention needs a bf16 cache");
+  if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
+    return fail(DLLM_EINVAL, "num_q_heads %d is not a positive multiple of Hkv %d", num_q_heads,
+                d.num_kv_heads);
+  if (n < 1 || n > d.max_seq) return fail(DLLM_EINVAL, "n=%d outside [1, S=%d]", n, d.max_seq);
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f))
+    return fail(DLLM_EINVAL, "softmax_scale must be positive and finite");
+  if (build != 0 && build != 1) return fail(DLLM_EINVAL, "build must be 0 or 1");
+  if (!q_cache || !q_block || !block_start || !fa_state || !out)
+    return fail(DLLM_EINVAL, "null q_cache, q_block, block_start, fa_state or out");
+  if (!aligned16(q_cache) || !aligned16(q_block) || !aligned16(fa_state) || !aligned16(out))
+    return fail(DLLM_EINVAL, "q_cache, q_block, fa_state and out must be 16-byte aligned");
+  const int G = num_q_heads / d.num_kv_heads;
+  const long long grid = (long long)d.batch * d.num_kv_heads * (((long long)d.max_seq * G + 31) / 32);
+  if (grid > 0x7fffffffLL) return fail(DLLM_EINVAL, "too many query tiles");
+  dllm::FacArgs a;
+  a.q_cache = q_cache;
+  a.q_blk = q_block;
+  a.block_start = block_start;
+  a.state = fa_state;
+  a.out = out;
+  a.lse = lse;
+  a.kc = c->k;
+  a.vc = c->v;
+  a.B = d.batch;
+  a.S = d.max_seq;
+  a.n = n;
+  a.Hq = num_q_heads;
+  a.Hkv = d.num_kv_heads;
+  a.D = d.head_dim;
+  a.build = build;
+  a.scale = softmax_scale;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dllm::launch_facache(a, s), s, "facache attention");
+}
+
 dllm_status dllm_drift_check(const dllm_cache* c, int32_t num_q_heads, int32_t k, float gamma,
                              int32_t* track_idx, void* track_buf, const float* attn_mass,
                              float* sigma_out, uint8_t* refresh_out, void* stream) {

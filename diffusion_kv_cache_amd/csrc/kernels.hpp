@@ -75,6 +75,22 @@ hipError_t launch_attn_fused(const AttnArgs& a, hipStream_t s);
 template <int KIND, int D>
 hipError_t launch_attn_fwd(const AttnArgs& a, const AttnPlan& p, int qtiles, hipStream_t s);
 
+// Attention of every row with cached softmax statistics of the invariant rows (FACache).
+struct FacArgs {
+  void* q_cache;             // [B, S, Hq, D] bf16, in/out: cached queries of every row
+  const void* q_blk;         // [B, n, Hq, D] bf16: this step's queries of the block rows
+  const int32_t* block_start;  // [B]: first row of each sequence's block
+  float* state;              // O~ [B, Hq, S, D] fp32, then (m2, l) [B, Hq, S, 2] fp32
+  void* out;                 // [B, S, Hq, D] bf16
+  float* lse;                // [B, Hq, S] or null
+  const void* kc;            // [B, Hkv, S, D] bf16
+  const void* vc;
+  int B, S, n, Hq, Hkv, D;
+  int build;                 // 1: first step of the block (state written), 0: state reused
+  float scale;
+};
+hipError_t launch_facache(const FacArgs& a, hipStream_t s);
+
 struct DriftArgs {
   const void* kc;
   const void* vc;

@@ -188,6 +188,46 @@ DLLM_API dllm_status dllm_block_attention_noalloc(const dllm_cache *c, const voi
                                                   int32_t n, float softmax_scale, void *out,
                                                   float *lse, float *attn_mass, void *stream);
 
+/* Bytes of the FACache state of dllm_facache_attention for cache `d` and Hq query heads:
+ * B * Hq * S * (D + 2) * 4.  Returns 0 for invalid arguments. */
+DLLM_API size_t dllm_facache_state_bytes(const dllm_cache_desc *d, int32_t num_q_heads);
+
+/* Attention of every row of a block step, with cached softmax statistics of the rows outside
+ * the block (FACache; LaCache explainer, Technical Summary, Methodology 1 and Inference
+ * Workflow).  For every sequence b the block is the rows [g0, g0 + n), g0 = block_start[b];
+ * every other row is invariant within the block's denoising steps.  The call computes, for
+ * every row i < S and query head h,
+ *   out[b, i, h] = sum_j softmax_j(<q[b, i, h], K[b, g, j]> * softmax_scale) V[b, g, j]
+ * over all S rows j (no mask), where q of a block row is q_block[b, i - g0, h] and q of any
+ * other row is q_cache[b, i, h].
+ *   q_cache      device, [B, S, Hq, D] bf16, in/out: the queries of every row (after RoPE);
+ *                the block rows are overwritten with q_block
+ *   q_block      device, [B, n, Hq, D] bf16: this step's queries of the block rows (the
+ *                refresh call's q_out for refresh_idx = the block)
+ *   block_start  device, [B] int32: g0 per sequence; clamped to [0, S - n]
+ *   fa_state     device, dllm_facache_state_bytes(...) bytes, 16-byte aligned, in/out: for
+ *                every invariant row (b, h, i), the online-softmax state over the invariant
+ *                keys: O~ [B, Hq, S, D] fp32 (the unnormalised output), then (m2, l)
+ *                [B, Hq, S, 2] fp32, where m2 is a running maximum of the logits in log2
+ *                units (the logits times log2(e)) and l the normaliser relative to 2^m2;
+ *                O~ / l is the attention output over the invariant keys and
+ *                (m2 + log2 l) ln 2 their log-sum-exp.  Rows of the block are not written.
+ *   build        1 at the first step of a block: everything is computed and fa_state
+ *                written; 0 at later steps of the same block (same g0, same invariant rows
+ *                and keys): a tile of 32 invariant (row, head) pairs skips every invariant
+ *                key and starts from fa_state; tiles holding block rows are computed in full.
+ *   out          device, [B, S, Hq, D] bf16
+ *   lse          device, [B, Hq, S] fp32 natural log-sum-exp, or NULL
+ * Only bf16 caches (the first layer, where the state is kept, runs in 16-bit precision).
+ * Results are deterministic.  A reuse step whose invariant rows or keys changed since the
+ * build step returns stale results for those rows (the caller's contract).
+ * Errors: DLLM_EINVAL, DLLM_EUNSUPPORTED (cache not bf16), DLLM_ELAUNCH. */
+DLLM_API dllm_status dllm_facache_attention(const dllm_cache *c, void *q_cache,
+                                            const void *q_block, const int32_t *block_start,
+                                            int32_t n, int32_t num_q_heads, float softmax_scale,
+                                            float *fa_state, int32_t build, void *out,
+                                            float *lse, void *stream);
+
 /* Attention-aware drift test and tracking update (Elastic-Cache core idea; Flash-dLLM
  * tracking budget).  Call after this step's refresh and attention.
  *   k            tracked tokens per (b, h), 1..64 (32 by default)
