@@ -265,6 +265,103 @@ def measure(args, wl):
     return rec, inp
 
 
+def burst_us(torch, fn, count, layers):
+    """Average duration of fn(layer), `count` calls back to back with the layers rotating,
+    between two events on the launch stream; a spin kernel ahead of the first event keeps the
+    GPU busy while the host enqueues (host launch cost stays out of the interval)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(1 << 20)
+    e1.record()
+    torch.cuda.synchronize()
+    spin_per_ms = (1 << 20) / e0.elapsed_time(e1)
+    t0 = time.perf_counter()
+    for r in range(count):
+        fn(layers[r % len(layers)])
+    host_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(spin_per_ms * (2.0 * host_ms + 0.2)))
+    e0.record()
+    for r in range(count):
+        fn(layers[r % len(layers)])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / count * 1e3
+
+
+def measure_facache(args, wl):
+    """FACache attention of every row (first layer of a block step) on the workload's shape,
+    the block being the refreshed rows: the build step, a reuse step, and plain attention of
+    every row for comparison."""
+    import torch
+
+    import diffusion_kv_cache_amd as dkv
+
+    dev = torch.device("cuda:0")
+    B, n, S, Hq, Hkv, D = wl.batch, wl.n_refresh, wl.seq, wl.q_heads, wl.kv_heads, wl.head_dim
+    inp = synth.make_inputs(wl)
+    h_prev = torch.from_numpy(inp.hidden_prev).to(dev).to(torch.bfloat16)
+    w = torch.from_numpy(inp.w).to(dev).to(torch.bfloat16)
+    idx = torch.from_numpy(inp.idx).to(dev)
+    starts = idx[:, 0].contiguous()
+    all_rows = torch.arange(S, dtype=torch.int32, device=dev).repeat(B, 1)
+    state_bytes = B * Hq * S * (D + 2) * 4
+    per = 2 * B * Hkv * S * D * 2 + 2 * B * S * Hq * D * 2 + state_bytes
+    L = max(3, math.ceil(3 * MALL_BYTES / per))
+
+    class FL:
+        pass
+
+    layers = []
+    for _ in range(L):
+        ly = FL()
+        ly.cache = dkv.Cache(B, Hkv, S, D, dkv.DLLM_BF16)
+        ly.q_all = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=dev)
+        dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_prev, all_rows, w, Hq, wl.rope_base, ly.q_all)
+        ly.q_blk = ly.q_all[:, wl.block_start:wl.block_start + n].contiguous()
+        ly.state = torch.empty((state_bytes // 4,), dtype=torch.float32, device=dev)
+        ly.out = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=dev)
+        ly.lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+        dkv.dllm_facache_attention(ly.cache, ly.q_all, ly.q_blk, starts, Hq, 1 / math.sqrt(D),
+                                   ly.state, True, ly.out, ly.lse)
+        layers.append(ly)
+    ws = torch.empty(max(1, dkv.dllm_attention_workspace_bytes(layers[0].cache, Hq, S)),
+                     dtype=torch.uint8, device=dev)
+    scale = 1 / math.sqrt(D)
+    calls = {
+        "build": lambda ly: dkv.dllm_facache_attention(ly.cache, ly.q_all, ly.q_blk, starts, Hq,
+                                                       scale, ly.state, True, ly.out, ly.lse),
+        "reuse": lambda ly: dkv.dllm_facache_attention(ly.cache, ly.q_all, ly.q_blk, starts, Hq,
+                                                       scale, ly.state, False, ly.out, ly.lse),
+        "plain_all_rows": lambda ly: dkv.dllm_block_attention(ly.cache, ly.q_all, Hq, scale,
+                                                              ly.out, ly.lse, None, ws),
+    }
+    for fn in calls.values():
+        for r in range(3):
+            fn(layers[r % L])
+    torch.cuda.synchronize()
+    count = max(10, args.steps)
+    us = {k_: burst_us(torch, fn, count, layers) for k_, fn in calls.items()}
+    q_out = 2 * B * S * Hq * D * 2 + B * Hq * S * 4          # every row's Q in, output + lse out
+    kv = 2 * B * Hkv * S * D * 2
+    st_inv = B * Hq * (S - n) * (D + 2) * 4                   # the invariant rows' state
+    works = {
+        "plain_all_rows": dict(bytes=q_out + kv, flops=4 * B * Hq * S * S * D),
+        "build": dict(bytes=q_out + kv + st_inv, flops=4 * B * Hq * S * S * D),
+        "reuse": dict(bytes=q_out + kv + st_inv + B * n * Hq * D * 2,
+                      flops=4 * B * Hq * n * S * D + 4 * B * Hq * (S - n) * n * D),
+    }
+    entries = {k_: roofline_entry(k_, works[k_], us[k_], "bf16") for k_ in calls}
+    log(f"[bench] facache on {wl.name}: " + ", ".join(f"{k_}={v:.1f} us" for k_, v in us.items()))
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": f"{wl.name} shape, every row's attention, block = the refreshed rows",
+            "layer_instances": L, "per_call_us": {k_: round(v, 2) for k_, v in us.items()},
+            "per_call_back_to_back": count, "rooflines": entries,
+            "reuse_speedup_vs_plain": round(us["plain_all_rows"] / us["reuse"], 3)}
+
+
 def run(args):
     import torch
 
@@ -296,6 +393,8 @@ def run(args):
     if others:
         # the other workloads, measured the same way in the same run (not the headline)
         result["configs"] = others
+    if not args.no_facache and wl.cache == "bf16":
+        result["facache"] = measure_facache(args, wl)
     if args.copy_calibration:
         # A plain device copy of known size, so HBM byte counters read under a profiler can be
         # scaled by what they report for a copy (reads = writes = the buffer size).
@@ -382,6 +481,9 @@ def main():
                     help="other workloads measured in the same run, reported under 'configs' "
                          "(comma-separated; '' for none)")
     ap.add_argument("--layers", type=int, default=0, help="layer instances to rotate (0: auto)")
+    ap.add_argument("--no-facache", action="store_true",
+                    help="skip the FACache measurement (every row's attention with cached "
+                         "statistics of the invariant rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
