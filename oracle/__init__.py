@@ -166,6 +166,31 @@ def attention(q, k, v, scale: float, want_lse=True, want_mass=False):
     return out, lse, mass
 
 
+def attention_varlen(q, k, v, scale: float, cu, lens, want_mass=False):
+    """Attention of a variable-length batch (Elastic-Cache card, deployment notes: variable-
+    length sequences concatenated): q [T, Hq, D] packed rows, rows cu[b] .. cu[b+1] belonging
+    to sequence b, which attends to the first lens[b] rows of k[b], v[b] ([B, Hkv, S, D]).
+    Returns out [T, Hq, D], lse [T * Hq] (sequence b's block at cu[b] * Hq laid out [Hq][rows])
+    and mass [B, Hq, S] (0 at and past lens[b])."""
+    q = _c(q, np.float64)
+    B, Hkv, S, D = k.shape
+    T, Hq, _ = q.shape
+    out = np.zeros((T, Hq, D))
+    lse = np.zeros(T * Hq)
+    mass = np.zeros((B, Hq, S)) if want_mass else None
+    for b in range(B):
+        r0, r1, L = int(cu[b]), int(cu[b + 1]), int(lens[b])
+        if r1 == r0:
+            continue
+        o, ls, m = attention(q[None, r0:r1], k[b:b + 1, :, :L], v[b:b + 1, :, :L], scale, True,
+                             want_mass)
+        out[r0:r1] = o[0]
+        lse[r0 * Hq:r1 * Hq] = ls[0].reshape(-1)
+        if want_mass:
+            mass[b, :, :L] = m[0]
+    return out, lse, mass
+
+
 def attention_state(q, k, v, scale: float, keep):
     """Online-softmax state over the keys kept by keep [B, S] (bool): q [B, n, Hq, D], k, v
     [B, Hkv, S, D] -> (m [B, Hq, n], l [B, Hq, n], o_tilde [B, n, Hq, D]), natural log."""

@@ -270,6 +270,40 @@ def test_attention_split_merge_identity():
     np.testing.assert_allclose(m + np.log(wts.sum(0)), lse, rtol=1e-13)
 
 
+def test_attention_varlen_reduces_to_the_fixed_batch_and_ignores_keys_past_the_length():
+    """Variable-length batches: equal row counts and full lengths give the fixed-batch
+    attention (packed rows, lse and mass in the same layout); a sequence's keys at and past
+    its length change nothing, and get no mass."""
+    r = rng(18)
+    B, n, Hq, Hkv, S, D = 3, 4, 4, 2, 21, 8
+    q = r.standard_normal((B, n, Hq, D))
+    k = r.standard_normal((B, Hkv, S, D))
+    v = r.standard_normal((B, Hkv, S, D))
+    cu = np.arange(B + 1) * n
+    full, lse, mass = oracle.attention(q, k, v, 0.3, True, True)
+    o2, l2, m2 = oracle.attention_varlen(q.reshape(B * n, Hq, D), k, v, 0.3, cu, [S] * B, True)
+    np.testing.assert_array_equal(o2, full.reshape(B * n, Hq, D))
+    np.testing.assert_array_equal(l2, lse.reshape(-1))
+    np.testing.assert_array_equal(m2, mass)
+    # uneven counts (one empty sequence) and lengths; keys past each length redrawn
+    cu = np.array([0, 3, 3, 7])
+    lens = [21, 9, 1]
+    qp = r.standard_normal((7, Hq, D))
+    o3, l3, m3 = oracle.attention_varlen(qp, k, v, 0.3, cu, lens, True)
+    k2, v2 = k.copy(), v.copy()
+    for b, L in enumerate(lens):
+        k2[b, :, L:] = 50 * r.standard_normal(k2[b, :, L:].shape)
+        v2[b, :, L:] = 50 * r.standard_normal(v2[b, :, L:].shape)
+    o4, l4, m4 = oracle.attention_varlen(qp, k2, v2, 0.3, cu, lens, True)
+    np.testing.assert_array_equal(o3, o4)
+    np.testing.assert_array_equal(l3, l4)
+    np.testing.assert_array_equal(m3, m4)
+    assert not m3[1].any()                                   # no rows: no mass
+    assert not m3[2, :, 1:].any() and np.allclose(m3[2, :, 0], 4)   # one key takes it all
+    np.testing.assert_allclose(o3[3:7, :, :], np.repeat(v[2:3, :, 0], 2, axis=1)
+                               .repeat(4, axis=0).reshape(4, Hq, D), rtol=1e-14)
+
+
 @pytest.mark.parametrize("B,n,Hq,Hkv,S,D", [(1, 3, 2, 2, 9, 4), (2, 4, 6, 2, 33, 8)])
 def test_attention_state_matches_library_softmax_on_the_kept_keys(B, n, Hq, Hkv, S, D):
     """FACache state over a key subset: o_tilde / l is the library attention over the kept
