@@ -26,7 +26,9 @@ EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatte
            "dllm_refresh_workspace_bytes", "dllm_attention_workspace_bytes",
            "dllm_block_attention", "dllm_drift_check", "dllm_fp8_e4m3_roundtrip",
            "dllm_set_options", "dllm_block_attention_noalloc", "dllm_facache_state_bytes",
-           "dllm_facache_attention", "dllm_last_error")
+           "dllm_facache_attention", "dllm_refresh_qkv_rope_scatter_varlen",
+           "dllm_attention_varlen_workspace_bytes", "dllm_block_attention_varlen",
+           "dllm_last_error")
 DLLM_OPT_DEBUG, DLLM_OPT_WIDE_OFFSETS = 1, 2
 DLLM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -79,6 +81,16 @@ def _load():
     lib.dllm_facache_attention.restype = i32
     lib.dllm_facache_attention.argtypes = [ctypes.POINTER(CCache), P, P, P, i32, i32, ctypes.c_float,
                                            P, i32, P, P, P]
+    lib.dllm_refresh_qkv_rope_scatter_varlen.restype = i32
+    lib.dllm_refresh_qkv_rope_scatter_varlen.argtypes = [ctypes.POINTER(CCache), P, i32, i32, P, P,
+                                                         i32, i32, P, i32, ctypes.c_float, P, P,
+                                                         ctypes.c_size_t, P]
+    lib.dllm_attention_varlen_workspace_bytes.restype = ctypes.c_size_t
+    lib.dllm_attention_varlen_workspace_bytes.argtypes = [ctypes.POINTER(CacheDesc), i32, i32, i32]
+    lib.dllm_block_attention_varlen.restype = i32
+    lib.dllm_block_attention_varlen.argtypes = [ctypes.POINTER(CCache), P, i32, i32, P, P, i32,
+                                                i32, ctypes.c_float, P, P, P, P, ctypes.c_size_t,
+                                                P]
     lib.dllm_drift_check.restype = i32
     lib.dllm_drift_check.argtypes = [ctypes.POINTER(CCache), i32, i32, ctypes.c_float, P, P, P, P,
                                      P, P]
@@ -204,6 +216,76 @@ def dllm_refresh_qkv_rope_scatter(cache: Cache, hidden: torch.Tensor, refresh_id
         ctypes.byref(cache.c), _ptr(hidden), H, act, _ptr(refresh_idx), n,
         _ptr(w_qkv), num_q_heads, float(rope_base), _ptr(q_out), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def dllm_refresh_qkv_rope_scatter_varlen(cache: Cache, hidden: torch.Tensor,
+                                         refresh_idx: torch.Tensor, cu_rows: torch.Tensor,
+                                         max_rows: int, w_qkv: torch.Tensor, num_q_heads: int,
+                                         rope_base: float, q_out: torch.Tensor, workspace=None,
+                                         stream=None):
+    """Packed rows of a variable-length batch: refresh_idx [T] int32, cu_rows [B+1] int32
+    (device), q_out [T, Hq, D]; T = cu_rows[B] = refresh_idx.numel()."""
+    d = cache.desc
+    if hidden.dtype not in _DTYPE_CODE:
+        raise DllmError(DLLM_EINVAL, f"hidden dtype {hidden.dtype}")
+    act = _DTYPE_CODE[hidden.dtype]
+    H = hidden.shape[-1]
+    T = refresh_idx.numel()
+    _expect(hidden, "hidden", (d.batch, d.max_seq, H), hidden.dtype)
+    _expect(refresh_idx, "refresh_idx", (T,), torch.int32)
+    _expect(cu_rows, "cu_rows", (d.batch + 1,), torch.int32)
+    _expect(w_qkv, "w_qkv", ((num_q_heads + 2 * d.num_kv_heads) * d.head_dim, H), hidden.dtype)
+    _expect(q_out, "q_out", (T, num_q_heads, d.head_dim), hidden.dtype)
+    if workspace is None:
+        need = _refresh_ws_for_rows(cache, H, act, T, num_q_heads)
+        workspace = _scratch(need, hidden.device, stream) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(lib.dllm_refresh_qkv_rope_scatter_varlen(
+        ctypes.byref(cache.c), _ptr(hidden), H, act, _ptr(refresh_idx), _ptr(cu_rows), T,
+        int(max_rows), _ptr(w_qkv), num_q_heads, float(rope_base), _ptr(q_out),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _refresh_ws_for_rows(cache: Cache, H: int, act: int, rows: int, num_q_heads: int) -> int:
+    """Workspace of a refresh of `rows` rows in all (what a one-sequence batch of that many
+    rows needs)."""
+    d = cache.desc
+    one = CacheDesc(1, d.num_kv_heads, max(d.max_seq, rows), d.head_dim, d.kv_dtype, d.group_size)
+    return lib.dllm_refresh_workspace_bytes(ctypes.byref(one), H, act, rows, num_q_heads)
+
+
+def dllm_attention_varlen_workspace_bytes(cache: Cache, num_q_heads: int, total_rows: int,
+                                          max_rows: int) -> int:
+    return lib.dllm_attention_varlen_workspace_bytes(ctypes.byref(cache.desc), num_q_heads,
+                                                     total_rows, max_rows)
+
+
+def dllm_block_attention_varlen(cache: Cache, q: torch.Tensor, num_q_heads: int,
+                                cu_rows: torch.Tensor, seq_lens: torch.Tensor, max_rows: int,
+                                softmax_scale: float, out: torch.Tensor, lse=None, attn_mass=None,
+                                workspace=None, stream=None):
+    """q, out [T, Hq, D] bf16 (packed rows), cu_rows [B+1] int32, seq_lens [B] int32 (device),
+    lse [T * Hq] fp32 or None, attn_mass [B, Hq, S] fp32 or None."""
+    d = cache.desc
+    T = q.shape[0] if q.dim() == 3 else -1
+    if q.dtype not in _DTYPE_CODE:
+        raise DllmError(DLLM_EINVAL, f"q dtype {q.dtype}")
+    _expect(q, "q", (T, num_q_heads, d.head_dim), q.dtype)
+    _expect(out, "out", (T, num_q_heads, d.head_dim), q.dtype)
+    _expect(cu_rows, "cu_rows", (d.batch + 1,), torch.int32)
+    _expect(seq_lens, "seq_lens", (d.batch,), torch.int32)
+    if lse is not None:
+        _expect(lse, "lse", (T * num_q_heads,), torch.float32)
+    if attn_mass is not None:
+        _expect(attn_mass, "attn_mass", (d.batch, num_q_heads, d.max_seq), torch.float32)
+    if workspace is None:
+        workspace = _scratch(max(1, dllm_attention_varlen_workspace_bytes(cache, num_q_heads, T,
+                                                                          max_rows)),
+                             q.device, stream)
+    _check(lib.dllm_block_attention_varlen(
+        ctypes.byref(cache.c), _ptr(q), _DTYPE_CODE[q.dtype], num_q_heads, _ptr(cu_rows),
+        _ptr(seq_lens), T, int(max_rows), float(softmax_scale), _ptr(out), _ptr(lse),
+        _ptr(attn_mass), _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def dllm_attention_workspace_bytes(cache: Cache, num_q_heads: int, n: int) -> int:

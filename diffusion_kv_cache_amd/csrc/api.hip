@@ -103,17 +103,44 @@ dllm_status device_symbols(DeviceSymbols** out) {
 }
 
 // Debug-mode device pass over the refresh index lists: one workgroup per sequence; every
-// position that is out of [0, S) or not above its predecessor is reported, the lowest flat
-// index winning.
-__global__ __launch_bounds__(256) void check_index_lists(const int32_t* idx, int n, int S,
-                                                         int32_t* report) {
+// position that is out of [0, S) or not above its predecessor is reported, the lowest packed
+// index winning.  With row offsets cu (a variable-length batch) sequence b's list is
+// idx[cu[b] .. cu[b + 1]); offsets that are not non-decreasing from 0 to T with at most
+// max_rows rows per sequence are reported as -1 - b.
+__global__ __launch_bounds__(256) void check_index_lists(const int32_t* idx, const int32_t* cu, int n,
+                                                         int T, int S, int32_t* report) {
   const int b = blockIdx.x;
-  const int32_t* row = idx + (size_t)b * n;
-  for (int i = threadIdx.x; i < n; i += 256) {
+  int r0 = b * n, cnt = n;
+  if (cu) {
+    r0 = cu[b];
+    cnt = cu[b + 1] - r0;
+    const bool bad_cu = (b == 0 && r0 != 0) || r0 < 0 || cnt < 0 || cnt > n || cu[b + 1] > T ||
+                        (b == (int)gridDim.x - 1 && cu[b + 1] != T);
+    if (bad_cu) {
+      if (threadIdx.x == 0) atomicMin(&report[0], -1 - b);
+      return;
+    }
+  }
+  const int32_t* row = idx + r0;
+  for (int i = threadIdx.x; i < cnt; i += 256) {
     const int32_t x = row[i];
     const bool bad = x < 0 || x >= S || (i > 0 && x <= row[i - 1]);
-    if (bad) atomicMin(&report[0], (int32_t)((size_t)b * n + i));
+    if (bad) atomicMin(&report[0], r0 + i);
   }
+}
+
+// Debug-mode pass over the offsets of a variable-length attention call: sequence b is
+// reported as -1 - b when its row offsets leave [0, T], decrease, give it more than n rows, or
+// miss 0 / T at the ends, or when its key count is outside [1, S].
+__global__ __launch_bounds__(256) void check_varlen_offsets(const int32_t* cu, const int32_t* lens,
+                                                            int B, int n, int T, int S,
+                                                            int32_t* report) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= B) return;
+  const int r0 = cu[b], r1 = cu[b + 1], len = lens[b];
+  const bool bad = r0 < 0 || r1 < r0 || r1 - r0 > n || r1 > T || (b == 0 && r0 != 0) ||
+                   (b == B - 1 && r1 != T) || len < 1 || len > S;
+  if (bad) atomicMin(report, -1 - b);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -158,6 +185,99 @@ dllm_status finish(hipError_t e, hipStream_t s, const char* what) {
   }
   g_err[0] = '\0';
   return DLLM_OK;
+}
+
+// Body of both refresh calls.  cu: row offsets [B + 1] of a variable-length batch (n is then
+// the largest rows per sequence and total all rows), or null (n rows per sequence).
+dllm_status refresh_call(const dllm_cache* c, const void* hidden, int32_t hidden_size,
+                         int32_t act_dtype, const int32_t* refresh_idx, const int32_t* cu,
+                         int32_t n, long long total, const void* w_qkv, int32_t num_q_heads,
+                         float rope_base, void* q_out, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  dllm_status st = check_cache(c);
+  if (st) return st;
+  const dllm_cache_desc& d = c->desc;
+  if (n < 0 || n > d.max_seq) return fail(DLLM_EINVAL, "n=%d outside [0, S=%d]", n, d.max_seq);
+  if (total < 0 || total > (long long)d.batch * n)
+    return fail(DLLM_EINVAL, "total rows %lld outside [0, B * max rows = %lld]", total,
+                (long long)d.batch * n);
+  if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
+    return fail(DLLM_EINVAL, "num_q_heads %d is not a positive multiple of Hkv %d", num_q_heads,
+                d.num_kv_heads);
+  if (hidden_size <= 0 || hidden_size % 256)
+    return fail(DLLM_EUNSUPPORTED, "hidden_size %d: must be a positive multiple of 256", hidden_size);
+  if (act_dtype == DLLM_F32) {
+    if (d.kv_dtype != DLLM_F32) return fail(DLLM_EUNSUPPORTED, "fp32 activations need an fp32 cache");
+  } else if (act_dtype == DLLM_BF16) {
+    if (d.kv_dtype == DLLM_F32) return fail(DLLM_EUNSUPPORTED, "bf16 activations need a bf16 or FP8 cache");
+  } else {
+    return fail(DLLM_EINVAL, "act_dtype %d: DLLM_F32 or DLLM_BF16", act_dtype);
+  }
+  if (!(rope_base > 0.f)) return fail(DLLM_EINVAL, "rope_base must be positive");
+  if (total == 0) {
+    g_err[0] = '\0';
+    return DLLM_OK;
+  }
+  if (!hidden || !refresh_idx || !w_qkv || !q_out) return fail(DLLM_EINVAL, "null input/output pointer");
+  if (!aligned16(hidden) || !aligned16(w_qkv) || !aligned16(q_out))
+    return fail(DLLM_EINVAL, "hidden, w_qkv and q_out must be 16-byte aligned");
+  const long long M = total;
+  if (M > (1LL << 30)) return fail(DLLM_EINVAL, "too many rows");
+  const int N = (num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
+  const size_t need = dllm::refresh_workspace_bytes(act_dtype, (int)M, N, hidden_size);
+  if (ws_bytes < need) return fail(DLLM_ESIZE, "refresh workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (need && (!workspace || !aligned16(workspace)))
+    return fail(DLLM_EINVAL, "refresh workspace must be a 16-byte aligned device pointer");
+  hipStream_t s = (hipStream_t)stream;
+
+  if (debug_mode()) {
+    // Device pass over the lists (and the row offsets); the report comes back to the host and
+    // the stream is synchronised (debug mode only).
+    DeviceSymbols* sym = nullptr;
+    st = device_symbols(&sym);
+    if (st) return st;
+    hipError_t e = hipMemsetAsync(sym->debug_report, 0x7f, sizeof(int32_t), s);
+    if (e == hipSuccess) {
+      check_index_lists<<<d.batch, 256, 0, s>>>(refresh_idx, cu, n, (int)M, d.max_seq, sym->debug_report);
+      e = hipGetLastError();
+    }
+    int32_t flat = 0, val = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync(&flat, sym->debug_report, sizeof flat, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess && flat >= 0 && flat != 0x7f7f7f7f)
+      e = hipMemcpy(&val, refresh_idx + flat, sizeof val, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(DLLM_ELAUNCH, "debug index check: %s", hipGetErrorString(e));
+    if (flat < 0) return fail(DLLM_EINVAL, "row offsets broken at sequence %d", -1 - flat);
+    if (flat != 0x7f7f7f7f) {
+      if (val < 0 || val >= d.max_seq)
+        return fail(DLLM_EINVAL, "refresh_idx[%d] = %d outside [0, %d)", flat, val, d.max_seq);
+      return fail(DLLM_EINVAL, "refresh_idx not strictly increasing at packed row %d (value %d)", flat, val);
+    }
+  }
+
+  dllm::RefreshArgs a;
+  a.hidden = hidden;
+  a.w = w_qkv;
+  a.idx = refresh_idx;
+  a.q_out = q_out;
+  a.kc = c->k;
+  a.vc = c->v;
+  a.ks = c->k_scale;
+  a.vs = c->v_scale;
+  a.B = d.batch;
+  a.S = d.max_seq;
+  a.H = hidden_size;
+  a.n = n;
+  a.M = (int)M;
+  a.Hq = num_q_heads;
+  a.Hkv = d.num_kv_heads;
+  a.D = d.head_dim;
+  a.act = act_dtype;
+  a.kind = d.kv_dtype;
+  a.rope_base = (double)rope_base;
+  a.ws = (float*)workspace;
+  a.cu = cu;
+  return finish(dllm::launch_refresh(a, s), s, "refresh");
 }
 
 }  // namespace
@@ -211,86 +331,21 @@ dllm_status dllm_refresh_qkv_rope_scatter(const dllm_cache* c, const void* hidde
                                           const void* w_qkv, int32_t num_q_heads,
                                           float rope_base, void* q_out, void* workspace,
                                           size_t ws_bytes, void* stream) {
-  dllm_status st = check_cache(c);
-  if (st) return st;
-  const dllm_cache_desc& d = c->desc;
-  if (n < 0 || n > d.max_seq) return fail(DLLM_EINVAL, "n=%d outside [0, S=%d]", n, d.max_seq);
-  if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
-    return fail(DLLM_EINVAL, "num_q_heads %d is not a positive multiple of Hkv %d", num_q_heads,
-                d.num_kv_heads);
-  if (hidden_size <= 0 || hidden_size % 256)
-    return fail(DLLM_EUNSUPPORTED, "hidden_size %d: must be a positive multiple of 256", hidden_size);
-  if (act_dtype == DLLM_F32) {
-    if (d.kv_dtype != DLLM_F32) return fail(DLLM_EUNSUPPORTED, "fp32 activations need an fp32 cache");
-  } else if (act_dtype == DLLM_BF16) {
-    if (d.kv_dtype == DLLM_F32) return fail(DLLM_EUNSUPPORTED, "bf16 activations need a bf16 or FP8 cache");
-  } else {
-    return fail(DLLM_EINVAL, "act_dtype %d: DLLM_F32 or DLLM_BF16", act_dtype);
-  }
-  if (!(rope_base > 0.f)) return fail(DLLM_EINVAL, "rope_base must be positive");
-  if (n == 0) {
-    g_err[0] = '\0';
-    return DLLM_OK;
-  }
-  if (!hidden || !refresh_idx || !w_qkv || !q_out) return fail(DLLM_EINVAL, "null input/output pointer");
-  if (!aligned16(hidden) || !aligned16(w_qkv) || !aligned16(q_out))
-    return fail(DLLM_EINVAL, "hidden, w_qkv and q_out must be 16-byte aligned");
-  const long long M = (long long)d.batch * n;
-  if (M > (1LL << 30)) return fail(DLLM_EINVAL, "too many rows");
-  const int N = (num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
-  const size_t need = dllm::refresh_workspace_bytes(act_dtype, (int)M, N, hidden_size);
-  if (ws_bytes < need) return fail(DLLM_ESIZE, "refresh workspace needs %zu bytes, got %zu", need, ws_bytes);
-  if (need && (!workspace || !aligned16(workspace)))
-    return fail(DLLM_EINVAL, "refresh workspace must be a 16-byte aligned device pointer");
-  hipStream_t s = (hipStream_t)stream;
+  const long long total = c ? (long long)c->desc.batch * (n > 0 ? n : 0) : 0;
+  return refresh_call(c, hidden, hidden_size, act_dtype, refresh_idx, nullptr, n, total, w_qkv,
+                      num_q_heads, rope_base, q_out, workspace, ws_bytes, stream);
+}
 
-  if (debug_mode()) {
-    // Device pass over the lists; the report comes back to the host and the stream is
-    // synchronised (debug mode only).
-    DeviceSymbols* sym = nullptr;
-    st = device_symbols(&sym);
-    if (st) return st;
-    hipError_t e = hipMemsetAsync(sym->debug_report, 0x7f, sizeof(int32_t), s);
-    if (e == hipSuccess) {
-      check_index_lists<<<d.batch, 256, 0, s>>>(refresh_idx, n, d.max_seq, sym->debug_report);
-      e = hipGetLastError();
-    }
-    int32_t flat = 0, val = 0;
-    if (e == hipSuccess) e = hipMemcpyAsync(&flat, sym->debug_report, sizeof flat, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e == hipSuccess && flat != 0x7f7f7f7f)
-      e = hipMemcpy(&val, refresh_idx + flat, sizeof val, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return fail(DLLM_ELAUNCH, "debug index check: %s", hipGetErrorString(e));
-    if (flat != 0x7f7f7f7f) {
-      const int b = flat / n, i = flat % n;
-      if (val < 0 || val >= d.max_seq)
-        return fail(DLLM_EINVAL, "refresh_idx[%d][%d] = %d outside [0, %d)", b, i, val, d.max_seq);
-      return fail(DLLM_EINVAL, "refresh_idx[%d] not strictly increasing at %d (value %d)", b, i, val);
-    }
-  }
-
-  dllm::RefreshArgs a;
-  a.hidden = hidden;
-  a.w = w_qkv;
-  a.idx = refresh_idx;
-  a.q_out = q_out;
-  a.kc = c->k;
-  a.vc = c->v;
-  a.ks = c->k_scale;
-  a.vs = c->v_scale;
-  a.B = d.batch;
-  a.S = d.max_seq;
-  a.H = hidden_size;
-  a.n = n;
-  a.M = (int)M;
-  a.Hq = num_q_heads;
-  a.Hkv = d.num_kv_heads;
-  a.D = d.head_dim;
-  a.act = act_dtype;
-  a.kind = d.kv_dtype;
-  a.rope_base = (double)rope_base;
-  a.ws = (float*)workspace;
-  return finish(dllm::launch_refresh(a, s), s, "refresh");
+dllm_status dllm_refresh_qkv_rope_scatter_varlen(const dllm_cache* c, const void* hidden,
+                                                 int32_t hidden_size, int32_t act_dtype,
+                                                 const int32_t* refresh_idx, const int32_t* cu_rows,
+                                                 int32_t total_rows, int32_t max_rows,
+                                                 const void* w_qkv, int32_t num_q_heads,
+                                                 float rope_base, void* q_out, void* workspace,
+                                                 size_t ws_bytes, void* stream) {
+  if (total_rows > 0 && !cu_rows) return fail(DLLM_EINVAL, "null cu_rows");
+  return refresh_call(c, hidden, hidden_size, act_dtype, refresh_idx, cu_rows, max_rows, total_rows,
+                      w_qkv, num_q_heads, rope_base, q_out, workspace, ws_bytes, stream);
 }
 
 size_t dllm_refresh_workspace_bytes(const dllm_cache_desc* d, int32_t hidden_size,
@@ -304,14 +359,34 @@ size_t dllm_refresh_workspace_bytes(const dllm_cache_desc* d, int32_t hidden_siz
   return dllm::refresh_workspace_bytes(act_dtype, (int)M, N, hidden_size);
 }
 
-size_t dllm_attention_workspace_bytes(const dllm_cache_desc* d, int32_t num_q_heads, int32_t n) {
-  if (check_desc(d) != DLLM_OK || num_q_heads <= 0 || num_q_heads % d->num_kv_heads || n < 0)
+}  // extern "C"
+
+namespace {
+
+// Workspace of an attention call over `total` query rows, at most n per sequence.
+size_t attention_ws_bytes(const dllm_cache_desc* d, int32_t num_q_heads, int32_t n, long long total) {
+  if (check_desc(d) != DLLM_OK || num_q_heads <= 0 || num_q_heads % d->num_kv_heads || n < 0 ||
+      total < 0)
     return 0;
   const int act = d->kv_dtype == DLLM_F32 ? DLLM_F32 : DLLM_BF16;
   dllm::AttnPlan p = dllm::plan_attention(d->batch, n, num_q_heads, d->num_kv_heads,
-                                          d->max_seq, d->head_dim, act, d->kv_dtype);
-  const size_t lse = (size_t)d->batch * num_q_heads * n * sizeof(float);
+                                          d->max_seq, d->head_dim, act, d->kv_dtype, total);
+  const size_t lse = (size_t)total * num_q_heads * sizeof(float);
   return round_up(p.part_bytes, 256) + round_up(lse, 256) + 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dllm_attention_workspace_bytes(const dllm_cache_desc* d, int32_t num_q_heads, int32_t n) {
+  if (!d || n < 0) return 0;
+  return attention_ws_bytes(d, num_q_heads, n, (long long)d->batch * n);
+}
+
+size_t dllm_attention_varlen_workspace_bytes(const dllm_cache_desc* d, int32_t num_q_heads,
+                                             int32_t total_rows, int32_t max_rows) {
+  return attention_ws_bytes(d, num_q_heads, max_rows, total_rows);
 }
 
 }  // extern "C"
@@ -320,14 +395,24 @@ namespace {
 
 // Body of both attention calls.  noalloc: the workspace is the library's scratch on the
 // current GPU (looked up here), and a shape that needs more than it holds is rejected.
+// Variable-length batches: cu (row offsets [B + 1]) and lens (keys per sequence [B]) given, n
+// the largest rows per sequence and total all rows; otherwise n rows per sequence.
 dllm_status attention_call(const dllm_cache* c, const void* q, int32_t act_dtype,
                            int32_t num_q_heads, int32_t n, float softmax_scale, void* out,
                            float* lse, float* attn_mass, void* workspace, size_t ws_bytes,
-                           bool noalloc, void* stream) {
+                           bool noalloc, void* stream, const int32_t* cu = nullptr,
+                           const int32_t* lens = nullptr, long long total = -1) {
   dllm_status st = check_cache(c);
   if (st) return st;
   const dllm_cache_desc& d = c->desc;
   if (n < 0 || n > d.max_seq) return fail(DLLM_EINVAL, "n=%d outside [0, S=%d]", n, d.max_seq);
+  const bool varlen = total >= 0;
+  if (!varlen) total = (long long)d.batch * n;
+  if (total > (long long)d.batch * n)
+    return fail(DLLM_EINVAL, "total rows %lld above B * max rows = %lld", total, (long long)d.batch * n);
+  if (varlen && total > 0 && (!cu || !lens)) return fail(DLLM_EINVAL, "null cu_rows or seq_lens");
+  if (varlen && act_dtype == DLLM_F32)
+    return fail(DLLM_EUNSUPPORTED, "variable-length batches need bf16 queries");
   if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
     return fail(DLLM_EINVAL, "num_q_heads %d is not a positive multiple of Hkv %d", num_q_heads,
                 d.num_kv_heads);
@@ -341,13 +426,13 @@ dllm_status attention_call(const dllm_cache* c, const void* q, int32_t act_dtype
   }
   if (!(softmax_scale > 0.f) || !(softmax_scale < 1e30f))
     return fail(DLLM_EINVAL, "softmax_scale must be positive and finite");
-  if (n == 0) {
+  if (n == 0 || total == 0) {
     g_err[0] = '\0';
     return DLLM_OK;
   }
   if (!q || !out) return fail(DLLM_EINVAL, "null q or out");
   if (!aligned16(q) || !aligned16(out)) return fail(DLLM_EINVAL, "q and out must be 16-byte aligned");
-  const size_t need = dllm_attention_workspace_bytes(&d, num_q_heads, n);
+  const size_t need = attention_ws_bytes(&d, num_q_heads, n, total);
   if (noalloc) {
     if (need > (size_t)DLLM_NOALLOC_SCRATCH_BYTES)
       return fail(DLLM_ESIZE, "attention needs %zu bytes of scratch; the allocation-free call "
@@ -360,8 +445,26 @@ dllm_status attention_call(const dllm_cache* c, const void* q, int32_t act_dtype
   }
   if (ws_bytes < need) return fail(DLLM_ESIZE, "attention workspace needs %zu bytes, got %zu", need, ws_bytes);
   if (!workspace) return fail(DLLM_EINVAL, "null workspace");
+  hipStream_t s = (hipStream_t)stream;
+  if (varlen && debug_mode()) {
+    DeviceSymbols* sym = nullptr;
+    st = device_symbols(&sym);
+    if (st) return st;
+    hipError_t e = hipMemsetAsync(sym->debug_report, 0x7f, sizeof(int32_t), s);
+    if (e == hipSuccess) {
+      check_varlen_offsets<<<(d.batch + 255) / 256, 256, 0, s>>>(cu, lens, d.batch, n, (int)total,
+                                                                  d.max_seq, sym->debug_report);
+      e = hipGetLastError();
+    }
+    int32_t flat = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync(&flat, sym->debug_report, sizeof flat, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(DLLM_ELAUNCH, "debug offset check: %s", hipGetErrorString(e));
+    if (flat < 0)
+      return fail(DLLM_EINVAL, "row offsets or key count broken at sequence %d", -1 - flat);
+  }
   dllm::AttnPlan p = dllm::plan_attention(d.batch, n, num_q_heads, d.num_kv_heads, d.max_seq,
-                                          d.head_dim, act_dtype, d.kv_dtype);
+                                          d.head_dim, act_dtype, d.kv_dtype, total);
   char* ws = (char*)round_up((uintptr_t)workspace, 256);
   dllm::AttnArgs a;
   a.q = q;
@@ -382,7 +485,9 @@ dllm_status attention_call(const dllm_cache* c, const void* q, int32_t act_dtype
   a.act = act_dtype;
   a.kind = d.kv_dtype;
   a.scale = softmax_scale;
-  hipStream_t s = (hipStream_t)stream;
+  a.cu = cu;
+  a.lens = lens;
+  a.T = (int)total;
   return finish(dllm::launch_attention(a, p, s), s, "attention");
 }
 
@@ -396,6 +501,18 @@ dllm_status dllm_block_attention(const dllm_cache* c, const void* q, int32_t act
                                  void* stream) {
   return attention_call(c, q, act_dtype, num_q_heads, n, softmax_scale, out, lse, attn_mass,
                         workspace, ws_bytes, false, stream);
+}
+
+dllm_status dllm_block_attention_varlen(const dllm_cache* c, const void* q, int32_t act_dtype,
+                                        int32_t num_q_heads, const int32_t* cu_rows,
+                                        const int32_t* seq_lens, int32_t total_rows,
+                                        int32_t max_rows, float softmax_scale, void* out,
+                                        float* lse, float* attn_mass, void* workspace,
+                                        size_t ws_bytes, void* stream) {
+  if (total_rows < 0) return fail(DLLM_EINVAL, "total_rows < 0");
+  return attention_call(c, q, act_dtype, num_q_heads, max_rows, softmax_scale, out, lse,
+                        attn_mass, workspace, ws_bytes, false, stream, cu_rows, seq_lens,
+                        total_rows);
 }
 
 dllm_status dllm_block_attention_noalloc(const dllm_cache* c, const void* q, int32_t act_dtype,

@@ -102,17 +102,19 @@ __device__ __forceinline__ void merge_row(const float* part, const float* ml, si
 template <typename OutT, int D>
 __global__ __launch_bounds__(64) void attn_merge(AttnArgs a, int splits) {
   const int G = a.Hq / a.Hkv;
-  const int rows = a.n * G;
-  const size_t nrows_all = (size_t)a.B * a.Hkv * rows;
-  const size_t pr0 = blockIdx.x;  // bg * rows + r
-  const int bg = (int)(pr0 / rows), r = (int)(pr0 % rows);
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const size_t nrows_all = (size_t)a.T * a.Hq;
+  const size_t pr0 = blockIdx.x;  // q0 * Hq + g * rows + r (q0: the sequence's first row)
+  const int b = seq_of_row(a.cu, a.B, a.n, (int)(pr0 / a.Hq));
+  const int nb = seq_rows(a.cu, a.n, b), q0 = seq_row0(a.cu, a.n, b);
+  const int rows = nb * G;
+  const int local = (int)(pr0 - (size_t)q0 * a.Hq);
+  const int g = local / rows, r = local % rows;
   const float* ml = a.part + (size_t)splits * nrows_all * D;
   constexpr int PER = D / 64;
   float mm, L, o[PER];
   merge_row<D>(a.part, ml, nrows_all, pr0, splits, threadIdx.x, o, mm, L);
   const int i = r / G, h = g * G + r % G;
-  OutT* out = (OutT*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
+  OutT* out = (OutT*)a.out + (((size_t)q0 + i) * a.Hq + h) * D;
   const float inv = 1.f / L;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(64) void attn_merge(AttnArgs a, int splits) {
     if constexpr (sizeof(OutT) == 2) out[threadIdx.x + 64 * e] = f32_to_bf16(val);
     else out[threadIdx.x + 64 * e] = val;
   }
-  if (threadIdx.x == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = (mm + log2f(L)) * kLn2;
+  if (threadIdx.x == 0) a.lse[(size_t)q0 * a.Hq + (size_t)h * nb + i] = (mm + log2f(L)) * kLn2;
 }
 
 // Column attention mass, second pass after the log-sum-exp is known:
@@ -169,28 +171,37 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
   xcd_group_unit(blockIdx.x, a.B * a.Hkv, nkc, bg, kchunk);
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int rows = a.n * G;
+  const int nb = seq_rows(a.cu, a.n, b), q0 = seq_row0(a.cu, a.n, b);
+  const int klen = seq_keys(a.lens, a.S, b);
+  const int rows = nb * G;
   const int key0 = kchunk * 128 + wave * 32;
+  if (nb == 0) {                                 // a sequence without queries: no mass
+    for (int e = t; e < G * 128; e += 256) {
+      const int key = kchunk * 128 + (e & 127);
+      if (key < a.S) a.mass[((size_t)b * a.Hq + g * G + (e >> 7)) * a.S + key] = 0.f;
+    }
+    return;
+  }
   const size_t head_base = ((size_t)b * a.Hkv + g) * a.S;
   constexpr int ELT = (KIND == kCacheFP8) ? 1 : 2;
   const char* kc = (const char*)a.kc;
 
   // Query tiles: it = hh * ntq + (i0 / 32), rows i0 .. i0 + 31 of head g * G + hh (rows past
   // n read row n - 1 and are masked out of the sums).
-  const int ntq = (a.n + QR - 1) / QR;
+  const int ntq = (nb + QR - 1) / QR;
   const int iters = G * ntq;
   const bf16_t* q = (const bf16_t*)a.q;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform: scalar DMA bases
   const uint32_t ring_lds = lds_addr(dyn);
   auto issue = [&](int it, int slot) {
     const int hh = it / ntq, i0 = (it % ntq) * QR;
-    const bf16_t* qb = q + ((size_t)b * a.n * a.Hq + g * G + hh) * D;   // row 0 of this head
+    const bf16_t* qb = q + ((size_t)q0 * a.Hq + g * G + hh) * D;   // row 0 of this head
 #pragma unroll
     for (int u = 0; u < BPW; ++u) {
       const int blk = wave_u * BPW + u;
       if (blk < NBLK) {
         const int r = blk * RPI + lane / CPR, sc = lane % CPR;
-        const int i = min(i0 + r, a.n - 1);
+        const int i = min(i0 + r, nb - 1);
         const uint32_t voff = (uint32_t)(((size_t)i * a.Hq * D + (sc ^ swz_q<D>(r)) * 8) * sizeof(bf16_t));
         dma_16B_sbase(voff, qb, ring_lds + (uint32_t)(slot * QTILE + blk * 1024));
       }
@@ -226,18 +237,19 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
     }
   }
 
-  const size_t nrows_all = (size_t)a.B * a.Hkv * rows;
+  const size_t nrows_all = (size_t)a.T * a.Hq;
+  const size_t pr_base = (size_t)q0 * a.Hq + (size_t)g * rows;   // packed row of (b, g, r = 0)
   const float* ml = a.part + (size_t)splits * nrows_all * D;
   // The rows' outputs are merged first: their loads then travel with the prologue's.
   if constexpr (MERGE) {
     // outputs of the rows r = kchunk + nkc * (4 it + wave), one wave per row
     constexpr int PER = D / 64;
     for (int r = kchunk + nkc * wave; r < rows; r += 4 * nkc) {
-      const size_t pr0 = (size_t)bg * rows + r;
+      const size_t pr0 = pr_base + r;
       float mm, L, o[PER];
       merge_row<D>(a.part, ml, nrows_all, pr0, splits, lane, o, mm, L);
       const int i = r / G, h = g * G + r % G;
-      bf16_t* out = (bf16_t*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
+      bf16_t* out = (bf16_t*)a.out + (((size_t)q0 + i) * a.Hq + h) * D;
       const float inv = 1.f / L;
 #pragma unroll
       for (int e = 0; e < PER; ++e) out[lane + 64 * e] = f32_to_bf16(o[e] * inv);
@@ -249,12 +261,12 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
     const int i = r / G, h = g * G + r % G;
     if constexpr (MERGE) {
       float mm, L;
-      merged_ml(ml, nrows_all, (size_t)bg * rows + r, splits, mm, L);
+      merged_ml(ml, nrows_all, pr_base + r, splits, mm, L);
       const float l2 = mm + log2f(L);
       lse2_s[r] = l2;
-      if (kchunk == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = l2 * kLn2;
+      if (kchunk == 0) a.lse[(size_t)q0 * a.Hq + (size_t)h * nb + i] = l2 * kLn2;
     } else {
-      lse2_s[r] = a.lse[((size_t)b * a.Hq + h) * a.n + i] * kLog2e;
+      lse2_s[r] = a.lse[(size_t)q0 * a.Hq + (size_t)h * nb + i] * kLog2e;
     }
   }
   __syncthreads();
@@ -273,11 +285,11 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
     for (int ct = 0; ct < QR / 16; ++ct) {
       const int r = ct * 16 + l16;
       const int i = i0 + r;
-      const int ic = min(i, a.n - 1);
+      const int ic = min(i, nb - 1);
       // rows past n (they read row n - 1) take lse = +inf, so their terms are exp2(-inf) = 0
-      const float lse2 = (i < a.n) ? (LDS_LSE ? lse2_s[ic * G + hh]
-                                              : a.lse[((size_t)b * a.Hq + g * G + hh) * a.n + ic] * kLog2e)
-                                   : INFINITY;
+      const float lse2 = (i < nb) ? (LDS_LSE ? lse2_s[ic * G + hh]
+                                             : a.lse[(size_t)q0 * a.Hq + (size_t)(g * G + hh) * nb + ic] * kLog2e)
+                                  : INFINITY;
       bf16x8 qf[DS];
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
@@ -303,7 +315,8 @@ __global__ __launch_bounds__(256) void attn_mass_mfma(AttnArgs a, int splits) {
         for (int v = 0; v < 4; ++v) {
           const float x = row16_sum(acc[kt][v]);
           const int key = key0 + kt * 16 + lg * 4 + v;
-          if (l16 == 0 && key < a.S) a.mass[((size_t)b * a.Hq + h) * a.S + key] = x;
+          // keys past the sequence's length (a variable-length batch) get no mass
+          if (l16 == 0 && key < a.S) a.mass[((size_t)b * a.Hq + h) * a.S + key] = key < klen ? x : 0.f;
           acc[kt][v] = 0.f;
         }
     }
@@ -418,7 +431,7 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
   const bool lds_lse = rows <= kMassLdsRows;
   const bool fuse = a.mass && p.splits > 1 && lds_lse;
   if (p.splits > 1 && !fuse) {
-    attn_merge<bf16_t, D><<<a.B * a.Hkv * rows, 64, 0, s>>>(a, p.splits);
+    attn_merge<bf16_t, D><<<(unsigned)((size_t)a.T * a.Hq), 64, 0, s>>>(a, p.splits);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -443,7 +456,7 @@ hipError_t launch_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t s) {
 
 }  // namespace
 
-AttnPlan plan_attention(int B, int n, int Hq, int Hkv, int S, int D, int act, int kind) {
+AttnPlan plan_attention(int B, int n, int Hq, int Hkv, int S, int D, int act, int kind, long long T) {
   AttnPlan p{32, 1, 0, 0};
   if (act == DLLM_F32) {
     p.kps = S;
@@ -464,7 +477,7 @@ AttnPlan plan_attention(int B, int n, int Hq, int Hkv, int S, int D, int act, in
   p.kps = ((tiles + splits - 1) / splits) * kKeys;
   p.splits = (S + p.kps - 1) / p.kps;
   if (p.splits > 1) {
-    const size_t nrows_all = (size_t)B * Hkv * rows;
+    const size_t nrows_all = (size_t)T * Hq;
     p.part_bytes = (size_t)p.splits * nrows_all * (D + 2) * sizeof(float);
   }
   return p;

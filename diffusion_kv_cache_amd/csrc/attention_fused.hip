@@ -417,7 +417,8 @@ __global__ __launch_bounds__(256) void attn_fused(AttnArgs a) {
 }  // namespace
 
 bool attn_fused_fits(const AttnArgs& a, const AttnPlan& p) {
-  return a.act == DLLM_BF16 && a.kind == kCacheBF16 && a.mass != nullptr && a.Hq == a.Hkv &&
+  return a.cu == nullptr && a.lens == nullptr &&
+         a.act == DLLM_BF16 && a.kind == kCacheBF16 && a.mass != nullptr && a.Hq == a.Hkv &&
          a.n <= 32 && (a.D == 128 || a.D == 64) && a.S >= 1 && a.S <= kFusedMaxSeq && p.splits == 1;
 }
 

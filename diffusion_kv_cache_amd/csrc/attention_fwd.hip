@@ -54,7 +54,10 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
   const int qt = unit / splits;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int rows = a.n * G;
+  const int nb = seq_rows(a.cu, a.n, b), q0 = seq_row0(a.cu, a.n, b);
+  const int rows = nb * G;
+  // query tiles past this sequence's rows (a variable-length batch): nothing to do
+  if (qt * QT >= rows) return;
   const float c = a.scale * kLog2e;
 
   const bf16_t* q = (const bf16_t*)a.q;
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     const int r = row0 + ct * 16 + l16;
     const bool ok = r < rows;
     const int i = ok ? r / G : 0, hh = ok ? r % G : 0;
-    const bf16_t* src = q + (((size_t)b * a.n + i) * a.Hq + g * G + hh) * D + lg * 8;
+    const bf16_t* src = q + (((size_t)q0 + i) * a.Hq + g * G + hh) * D + lg * 8;
     // Rows past the end read row 0 (finite data): their score columns are never stored, and
     // not selecting here keeps these loads in flight together with the first tile's.
 #pragma unroll
@@ -73,8 +76,8 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
   }
 
   const int kbeg = split * kps;
-  const int kend = min(a.S, kbeg + kps);
-  const int ntiles = (kend - kbeg + kKeys - 1) / kKeys;
+  const int kend = min(seq_keys(a.lens, a.S, b), kbeg + kps);
+  const int ntiles = max(0, (kend - kbeg + kKeys - 1) / kKeys);   // 0: no key of this split counts
   const int iters = (ntiles + KW - 1) / KW;
   const size_t head_base = ((size_t)b * a.Hkv + g) * a.S;
   const char* kc = (const char*)a.kc;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
   group_merge<QW, D>((float*)ring, oacc, m, lsum, kw, qw, lane, ofin, dt0);
 
   // This wave's slice of the final output when unsplit, else of this split's partial state.
-  const size_t nrows_all = (size_t)a.B * a.Hkv * rows;
+  const size_t nrows_all = (size_t)a.T * a.Hq;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int r = row0 + ct * 16 + l16;
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
     const int i = r / G, h = g * G + r % G;
     if (splits == 1) {
       const float inv = 1.f / lsum[ct];
-      bf16_t* o = (bf16_t*)a.out + (((size_t)b * a.n + i) * a.Hq + h) * D;
+      bf16_t* o = (bf16_t*)a.out + (((size_t)q0 + i) * a.Hq + h) * D;
 #pragma unroll
       for (int u = 0; u < DTW; ++u) {
         const int d = (dt0 + u) * 16 + lg * 4;
@@ -196,9 +199,9 @@ __global__ __launch_bounds__(256) void attn_fwd(AttnArgs a, int qtiles, int spli
         w2.y = pack_bf16x2(ofin[ct][u][2] * inv, ofin[ct][u][3] * inv);
         *(uint2*)(o + d) = w2;
       }
-      if (lg == 0 && kw == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = (m[ct] + log2f(lsum[ct])) * kLn2;
+      if (lg == 0 && kw == 0) a.lse[(size_t)q0 * a.Hq + (size_t)h * nb + i] = (m[ct] + log2f(lsum[ct])) * kLn2;
     } else {
-      const size_t pr = (size_t)split * nrows_all + (size_t)bg * rows + r;
+      const size_t pr = (size_t)split * nrows_all + (size_t)q0 * a.Hq + (size_t)g * rows + r;
       float* po = a.part + pr * D;
 #pragma unroll
       for (int u = 0; u < DTW; ++u) {

@@ -177,6 +177,31 @@ __device__ __forceinline__ void xcd_group_unit(int id, int groups, int per, int&
   }
 }
 
+// ------------------------------------------------------------------- batch layout -----
+
+// Rows of a batch (refreshed rows, queries) are packed: the rows of sequence b are rows
+// [row0, row0 + count) of the packed arrays.  With a row-offset array cu ([B + 1], variable-
+// length batches: Elastic-Cache card, deployment notes) row0 = cu[b] and count = cu[b + 1] -
+// cu[b]; without one every sequence has n rows and row0 = b * n.  The keys of sequence b are
+// its first len cache rows: lens[b], or all S.
+__device__ __forceinline__ int seq_row0(const int32_t* cu, int n, int b) { return cu ? cu[b] : b * n; }
+__device__ __forceinline__ int seq_rows(const int32_t* cu, int n, int b) {
+  return cu ? cu[b + 1] - cu[b] : n;
+}
+__device__ __forceinline__ int seq_keys(const int32_t* lens, int S, int b) { return lens ? lens[b] : S; }
+// The sequence that packed row m belongs to (the last b with cu[b] <= m, so sequences without
+// rows are passed over).
+__device__ __forceinline__ int seq_of_row(const int32_t* cu, int B, int n, int m) {
+  if (!cu) return m / n;
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= m) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // ------------------------------------------------------------------------ reductions ----
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {

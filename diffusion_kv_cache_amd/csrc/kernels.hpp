@@ -27,6 +27,7 @@ struct RefreshArgs {
   int kind;              // cache dtype
   double rope_base;
   float* ws;             // split-K partials [8][M][N] (small-M path only)
+  const int32_t* cu;     // [B + 1] row offsets of a variable-length batch, or null (n rows each)
 };
 
 // Rows (B * n) up to which a bf16 refresh takes the split-K path.
@@ -54,6 +55,12 @@ struct AttnArgs {
   int B, n, Hq, Hkv, S, D;
   int act, kind;
   float scale;           // softmax scale
+  // Variable-length batches: query rows of sequence b are [cu[b], cu[b + 1]) of q and out
+  // (n is then the largest count), its keys the first lens[b] cache rows; null: n rows and S
+  // keys each.  T: all query rows (B * n without cu).
+  const int32_t* cu;
+  const int32_t* lens;
+  int T;
 };
 
 // Shape of the attention launch for a problem: splits over S and the workspace they need.
@@ -63,7 +70,8 @@ struct AttnPlan {
   int kps;       // keys per split (multiple of 32)
   size_t part_bytes;  // workspace for split partials
 };
-AttnPlan plan_attention(int B, int n, int Hq, int Hkv, int S, int D, int act, int kind);
+// n: query rows per sequence (the largest, for a variable-length batch); T: all query rows.
+AttnPlan plan_attention(int B, int n, int Hq, int Hkv, int S, int D, int act, int kind, long long T);
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t s);
 // Attention and column mass in one launch (one workgroup per (b, KV head)): taken when the

@@ -27,7 +27,7 @@ namespace {
 // Destination of output row m (= b * n + i, position pos) of head slot j; element type chosen
 // by caller.
 __device__ __forceinline__ size_t out_row_offset(const RefreshArgs& a, int m, int j, int pos, int& which) {
-  const int b = m / a.n;
+  const int b = seq_of_row(a.cu, a.B, a.n, m);
   if (j < a.Hq) {
     which = 0;
     return ((size_t)m * a.Hq + j) * (size_t)a.D;
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
     const int r = t / BKC + u * (256 / BKC);
     const int m = min(m0 + r, a.M - 1);
     aval[u] = m0 + r < a.M;
-    asrc[u] = hid + ((size_t)(m / a.n) * a.S + prow[u]) * a.H + cchunk * EPC;
+    asrc[u] = hid + ((size_t)seq_of_row(a.cu, a.B, a.n, m) * a.S + prow[u]) * a.H + cchunk * EPC;
   }
   const T* wsrc[W_PER_T];
 #pragma unroll
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
     size_t e;                                    // element offset of the chunk
     if (gi < IA) {
       const int r = gi * RPI + lane / BKC;
-      const size_t hrow = (size_t)(mrow[i] / a.n) * a.S + prow[i];
+      const size_t hrow = (size_t)seq_of_row(a.cu, a.B, a.n, mrow[i]) * a.S + prow[i];
       e = hrow * a.H + (cp ^ (r & (BKC - 1))) * EPC;
       src[i] = (const bf16_t*)a.hidden + e;
     } else {

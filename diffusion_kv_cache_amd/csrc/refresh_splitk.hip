@@ -50,7 +50,7 @@ void refresh_partial(RefreshArgs a, float* part) {
   __shared__ int s_row[32];                      // hidden row offset (b * S + pos) per A row
   if (t < 32) {
     const int m = min(m0 + t, a.M - 1);
-    s_row[t] = (m / a.n) * a.S + a.idx[m];
+    s_row[t] = seq_of_row(a.cu, a.B, a.n, m) * a.S + a.idx[m];
   }
   lds_barrier();
   const bf16_t* hid = (const bf16_t*)a.hidden;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(64) void refresh_reduce(RefreshArgs a, const float*
       y[e] = ye;
     }
   }
-  const int b = m / a.n;
+  const int b = seq_of_row(a.cu, a.B, a.n, m);
   const int i0 = L * PPL;
   if (j < a.Hq) {
     if (ok) {

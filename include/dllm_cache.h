@@ -137,6 +137,31 @@ DLLM_API dllm_status dllm_refresh_qkv_rope_scatter(const dllm_cache *c, const vo
                                           float rope_base, void *q_out, void *workspace,
                                           size_t ws_bytes, void *stream);
 
+/* Variable-length batches (Elastic-Cache paper card, deployment notes: a batch implementation
+ * that concatenates variable-length sequences to keep the GPU busy).  The refreshed rows of
+ * all sequences are packed without padding: sequence b's rows are packed rows
+ * [cu_rows[b], cu_rows[b + 1]) of refresh_idx and q_out, with cu_rows[0] = 0 and
+ * cu_rows[B] = total_rows; a sequence may have no rows.  Everything else is as in
+ * dllm_refresh_qkv_rope_scatter (same arithmetic and reduction order, so a row stores the same
+ * bits as in a full refresh):
+ *   refresh_idx  device, [total_rows] int32: per sequence sorted, unique, in [0, S)
+ *   cu_rows      device, [B + 1] int32 row offsets
+ *   total_rows   cu_rows[B] (0 enqueues nothing)
+ *   max_rows     the largest rows per sequence, <= S
+ *   q_out        device, [total_rows, Hq, D] of act_dtype
+ *   workspace    dllm_refresh_workspace_bytes(d, H, act, total_rows / B rounded up, Hq) is
+ *                enough; exactly: what the fixed call needs for B * n = total_rows rows
+ * Errors: those of dllm_refresh_qkv_rope_scatter; debug mode also checks cu_rows. */
+DLLM_API dllm_status dllm_refresh_qkv_rope_scatter_varlen(const dllm_cache *c, const void *hidden,
+                                                          int32_t hidden_size, int32_t act_dtype,
+                                                          const int32_t *refresh_idx,
+                                                          const int32_t *cu_rows,
+                                                          int32_t total_rows, int32_t max_rows,
+                                                          const void *w_qkv, int32_t num_q_heads,
+                                                          float rope_base, void *q_out,
+                                                          void *workspace, size_t ws_bytes,
+                                                          void *stream);
+
 /* Workspace bytes the refresh call needs for n rows per sequence (0 when the step runs as a
  * single fused kernel; 8 * B * n * (Hq + 2 Hkv) * D * 4 for the split-K path of small
  * bf16 steps, B * n <= 64).  Returns 0 also for invalid arguments. */
@@ -171,6 +196,35 @@ DLLM_API dllm_status dllm_block_attention(const dllm_cache *c, const void *q, in
                                  int32_t num_q_heads, int32_t n, float softmax_scale,
                                  void *out, float *lse, float *attn_mass, void *workspace,
                                  size_t ws_bytes, void *stream);
+
+/* Block attention of a variable-length batch (Elastic-Cache paper card, deployment notes):
+ * the query rows of all sequences are packed without padding, sequence b's rows being packed
+ * rows [cu_rows[b], cu_rows[b + 1]) of q and out, and sequence b attends over its own first
+ * seq_lens[b] cache rows only:
+ *   out[r, h] = sum_{j < seq_lens[b]} softmax_j(<q[r, h], K[b, g, j]> * softmax_scale) V[b, g, j]
+ * for every packed row r of sequence b.
+ *   q, out       device, [total_rows, Hq, D] bf16
+ *   cu_rows      device, [B + 1] int32 row offsets (cu_rows[0] = 0, cu_rows[B] = total_rows)
+ *   seq_lens     device, [B] int32, each in [1, S]
+ *   max_rows     the largest rows per sequence (<= S)
+ *   lse          device, [total_rows * Hq] fp32 or NULL: sequence b's block at
+ *                cu_rows[b] * Hq, laid out [Hq][rows of b]
+ *   attn_mass    device, [B, Hq, S] fp32 or NULL; keys at or past seq_lens[b] get 0
+ *   workspace    ws_bytes >= dllm_attention_varlen_workspace_bytes(...)
+ * Caches: bf16 or FP8.  Errors: those of dllm_block_attention; DLLM_EUNSUPPORTED for fp32;
+ * debug mode (DLLM_OPT_DEBUG) checks cu_rows, max_rows and seq_lens on the device first and
+ * returns DLLM_EINVAL naming the first broken sequence.  Outside debug mode offsets that break
+ * these rules are undefined behaviour. */
+DLLM_API size_t dllm_attention_varlen_workspace_bytes(const dllm_cache_desc *d,
+                                                      int32_t num_q_heads, int32_t total_rows,
+                                                      int32_t max_rows);
+DLLM_API dllm_status dllm_block_attention_varlen(const dllm_cache *c, const void *q,
+                                                 int32_t act_dtype, int32_t num_q_heads,
+                                                 const int32_t *cu_rows, const int32_t *seq_lens,
+                                                 int32_t total_rows, int32_t max_rows,
+                                                 float softmax_scale, void *out, float *lse,
+                                                 float *attn_mass, void *workspace,
+                                                 size_t ws_bytes, void *stream);
 
 /* Block attention that allocates nothing and takes no workspace, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
