@@ -17,7 +17,10 @@ composes them into the step the pages describe:
 * O5/O6  attention of the refreshed rows' queries over the whole cache, log-sum-exp and the
          column attention mass (``attention``);
 * O8-O10 top-k tracking set, drift test and tracking-buffer refill (``drift``, ``topk``,
-         ``track``), after Elastic-Cache's core idea.
+         ``track``), after Elastic-Cache's core idea;
+* O11-O14 the partial refresh chosen by feature similarity (dLLM-Cache abstract) and one layer
+         of the Elastic-Cache layer schedule (``feature_similarity``, ``similarity_select``,
+         ``schedule_rows``, ``schedule_layer``).
 
 "Storage" rounding: the cache holds K/V in its own dtype (fp32, bf16, or e4m3 codes with one
 fp32 scale per 128-value row) and Q is handed to attention in the activation dtype.  The oracle
@@ -380,3 +383,127 @@ def track(cache: Cache, mass: np.ndarray, k: int):
                     buf[b, h, t, 0] = cache.k[b, h // G, j]
                     buf[b, h, t, 1] = cache.v[b, h // G, j]
     return T, buf
+
+
+# ------------------------------------------------------------------------------------------
+# Partial refresh chosen by feature similarity (dLLM-Cache) and the layer schedule
+# (Elastic-Cache)
+# ------------------------------------------------------------------------------------------
+
+def feature_similarity(h_cur: np.ndarray, h_cached: np.ndarray) -> np.ndarray:
+    """O11: cosine of every row's current input feature with the feature its cache rows were
+    last computed from (dLLM-Cache record, abstract: partial response updates guided by
+    feature similarity).  [B, S, H] x [B, S, H] -> [B, S] fp64: <x, y> / (|x| |y|); two zero
+    rows -> 1, exactly one zero row -> 0 (the drift test's convention)."""
+    x = _c(h_cur, np.float64)
+    y = _c(h_cached, np.float64)
+    assert x.shape == y.shape and x.ndim == 3
+    dot = np.einsum("bsh,bsh->bs", x, y)
+    nx = np.sqrt(np.einsum("bsh,bsh->bs", x, x))
+    ny = np.sqrt(np.einsum("bsh,bsh->bs", y, y))
+    zx, zy = nx == 0, ny == 0
+    with np.errstate(invalid="ignore", divide="ignore"):
+        sim = dot / (nx * ny)
+    return np.where(zx & zy, 1.0, np.where(zx | zy, 0.0, sim))
+
+
+def similarity_select(h_cur, h_cached, lo: int, window_start, window: int, k: int):
+    """O12: the rows a sequence refreshes at this step: its window rows [ws_b, ws_b + window)
+    (Elastic-Cache core idea: the live tokens near the decoding position), plus the k rows of
+    the response [lo, S) outside that window whose features moved most, i.e. the k lowest
+    cosines of O11 (ties: lower position first; dLLM-Cache abstract).  Returns
+    (idx [B, window + k] int32 ascending, sim [B, S])."""
+    sim = feature_similarity(h_cur, h_cached)
+    B, S = sim.shape
+    ws = np.zeros(B, np.int64) if window_start is None else np.asarray(window_start)
+    out = np.empty((B, window + k), np.int32)
+    for b in range(B):
+        win = set(range(int(ws[b]), int(ws[b]) + window))
+        cand = [j for j in range(lo, S) if j not in win]
+        assert len(cand) >= k
+        chosen = sorted(cand, key=lambda j: (sim[b, j], j))[:k]
+        out[b] = sorted(win | set(chosen))
+    return out, sim
+
+
+def schedule_rows(S: int, idx, tracked, full):
+    """O13: rows each sequence refreshes at one layer of the Elastic-Cache schedule (card,
+    core idea): every row when its drift test fired at an earlier layer of this step
+    (recomputation from layer l + 1 to L), otherwise its step rows idx[b] together with its
+    tracked positions (tracked[b], -1 = empty slot), so that the drift test compares rows
+    computed at this step.  Returns (rows [T] int32, each sequence's rows ascending and
+    packed in sequence order, cu [B + 1] int32)."""
+    idx = np.asarray(idx)
+    B = idx.shape[0]
+    parts = []
+    for b in range(B):
+        if full is not None and full[b]:
+            parts.append(np.arange(S, dtype=np.int32))
+            continue
+        s = set(int(j) for j in np.asarray(idx[b]).ravel())
+        if tracked is not None:
+            s |= set(int(j) for j in np.asarray(tracked[b]).ravel() if j >= 0)
+        parts.append(np.array(sorted(s), dtype=np.int32))
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum([len(p) for p in parts])
+    rows = np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+    return rows, cu
+
+
+class LayerState:
+    """One layer of the schedule: its workload geometry, weights, cache, cached input features
+    ([B, S, H], the rows' inputs when their cache rows were last computed), tracked positions
+    [B, Hq, k] and tracking buffer [B, Hq, k, 2, D]."""
+
+    def __init__(self, wl, w, cache, feat, T, buf):
+        self.wl, self.w, self.cache, self.feat, self.T, self.buf = wl, w, cache, feat, T, buf
+
+
+def schedule_prepare(wl, w: np.ndarray, h_prev: np.ndarray, rows0, k_track: int) -> LayerState:
+    """A layer before the step: prefill from h_prev, then the previous step (rows0 [B, n]
+    refreshed from the same states, their attention with mass) sets the tracked positions and
+    the tracking buffer from that mass."""
+    cache = prefill(wl, h_prev, w)
+    rows0 = np.asarray(rows0, np.int32)
+    q = queries(wl, h_prev, w, rows0)
+    _, _, mass = attend(wl, q, cache, want_mass=True)
+    T, buf = track(cache, mass, k_track)
+    return LayerState(wl, w, cache, np.array(h_prev, np.float64), T, buf)
+
+
+def schedule_layer(st: LayerState, h_cur: np.ndarray, full, lo: int, window_start, window: int,
+                   k_select: int, gamma: float):
+    """O14: one layer of one denoising step under the Elastic-Cache schedule with a
+    similarity-chosen partial refresh.  full [B] (bool): the sequences whose drift test fired
+    at an earlier layer of this step.  In order:
+      1. step rows R_b: window plus the k_select least similar response rows (O12);
+      2. refreshed rows: all rows of a full sequence, else R_b with the tracked positions (O13);
+      3. their K/V rows recomputed from h_cur into the cache, their queries formed (O1-O4);
+      4. attention of those queries over each sequence's whole cache, with mass (O5/O6);
+      5. drift test of the previous tracked rows against the cache now (O9), then the
+         tracking update from this mass (O8/O10);
+      6. the refreshed rows' cached features become h_cur's;
+      7. full_next = full or the drift decision (Elastic-Cache: recompute from l + 1 to L).
+    Returns a dict of every intermediate; st is updated in place."""
+    wl = st.wl
+    B, S, Hq, D = wl.batch, wl.seq, wl.q_heads, wl.head_dim
+    R, sim = similarity_select(h_cur, st.feat, lo, window_start, window, k_select)
+    rows, cu = schedule_rows(S, R, st.T.reshape(B, -1), full)
+    q = np.zeros((int(cu[-1]), Hq, D))
+    for b in range(B):
+        r = rows[cu[b]:cu[b + 1]]
+        if len(r):
+            refresh_rows(st.cache, h_cur, st.w, [r] * B, batches=[b])
+            q[cu[b]:cu[b + 1]] = round_storage(qkv_rows(h_cur[b, r], r, st.w, wl, "q"), wl.act)
+    lens = np.full(B, S, np.int32)
+    out, lse, mass = attention_varlen(q, st.cache.k, st.cache.v, 1.0 / math.sqrt(D), cu, lens,
+                                      True)
+    sigma, decision = drift(st.buf, st.T, st.cache.k, st.cache.v, gamma)
+    T_prev = st.T
+    st.T, st.buf = track(st.cache, mass, st.T.shape[-1])
+    for b in range(B):
+        r = rows[cu[b]:cu[b + 1]]
+        st.feat[b, r] = h_cur[b, r]
+    full_next = np.asarray(full, bool) | decision.astype(bool)
+    return dict(R=R, sim=sim, rows=rows, cu=cu, q=q, out=out, lse=lse, mass=mass, sigma=sigma,
+                decision=decision, T_prev=T_prev, full_next=full_next)

@@ -191,3 +191,44 @@ def uniform_mass(rng: np.random.Generator, shape, ties: int = 0) -> np.ndarray:
 def small_integer_grid(rng: np.random.Generator, shape) -> np.ndarray:
     """Entries in {-2..2} * 2^-4: every fp32 partial sum of their products is exact."""
     return (rng.integers(-2, 3, size=shape).astype(np.float32) * np.float32(1.0 / 16.0))
+
+
+@dataclasses.dataclass
+class LayerStack:
+    """Seeded inputs of a step over L synthetic layers (one weight matrix and one pair of
+    hidden-state arrays per layer; no layer feeds the next)."""
+    wl: Workload
+    w: list                  # L x [N, H] float32
+    hidden_prev: list        # L x [B, S, H] float32: the states the caches were built from
+    hidden_cur: list         # L x [B, S, H] float32: this step's states
+    window_start: np.ndarray  # [B] int32: first row of each sequence's window
+    triggers: np.ndarray     # [B] int32: first layer whose states move (L = none)
+
+
+def layer_stack(wl: Workload, layers: int, triggers, window: int) -> LayerStack:
+    """Every row of layer l of sequence b is mixed as alpha * H_prev + sqrt(1 - alpha^2) * eps
+    with alpha = 0.99 before triggers[b] and 0.0 from that layer on, so the drift test at
+    layer triggers[b] sees a clear change and the earlier ones do not.  Window starts are
+    uniform over the response rows."""
+    ss = np.random.SeedSequence(wl.seed)
+    streams = [np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(3 * layers + 1)]
+    B, S, H = wl.batch, wl.seq, wl.hidden
+    trig = np.asarray(triggers, np.int32)
+    assert trig.shape == (B,)
+    ws = streams[-1].integers(wl.prompt, S - window + 1, size=B).astype(np.int32)
+    w, hp, hc = [], [], []
+    for l in range(layers):
+        r_w, r_h, r_e = streams[3 * l: 3 * l + 3]
+        w.append(_normal(r_w, (wl.n_cols, H), 0.02, wl.act))
+        prev = _normal(r_h, (B, S, H), 1.0, wl.act)
+        eps = r_e.standard_normal((B, S, H), dtype=np.float32)
+        cur = np.empty_like(prev)
+        for b in range(B):
+            alpha = np.float32(0.99 if l < trig[b] else 0.0)
+            beta = np.float32(math.sqrt(1.0 - float(alpha) ** 2))
+            cur[b] = alpha * prev[b] + beta * eps[b]
+        if wl.act == BF16:
+            cur = round_to_bf16(cur)
+        hp.append(prev)
+        hc.append(cur)
+    return LayerStack(wl, w, hp, hc, ws, trig)

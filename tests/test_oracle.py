@@ -534,3 +534,131 @@ def test_step_uses_absolute_row_positions():
     a = lp[0, 0:S - d] - lp[0, 0]
     b = lp[1, d:S] - lp[1, d]
     np.testing.assert_allclose(a, b, rtol=0, atol=2e-5)
+
+
+# ---------------------------------------------------------------- similarity refresh ----
+
+def test_feature_similarity_closed_forms():
+    """Cosine of planted pairs: x = e1, y = cos(t) e1 + sin(t) e2 gives cos(t); scaling either
+    row keeps it; the negation gives -1; zero rows follow the drift test's convention."""
+    H = 6
+    t = np.linspace(0.0, math.pi, 9)
+    x = np.zeros((1, 9, H)); y = np.zeros((1, 9, H))
+    x[0, :, 0] = 1.0
+    y[0, :, 0], y[0, :, 1] = np.cos(t), np.sin(t)
+    np.testing.assert_allclose(oracle.feature_similarity(x, y)[0], np.cos(t), atol=1e-15)
+    np.testing.assert_allclose(oracle.feature_similarity(3.0 * x, 0.5 * y)[0], np.cos(t),
+                               atol=1e-15)
+    r = rng(40).standard_normal((2, 5, H))
+    np.testing.assert_allclose(oracle.feature_similarity(r, -2.0 * r), -1.0, atol=1e-15)
+    z = np.zeros((1, 3, H)); o = np.ones((1, 3, H))
+    np.testing.assert_array_equal(oracle.feature_similarity(z, z), 1.0)
+    np.testing.assert_array_equal(oracle.feature_similarity(z, o), 0.0)
+    np.testing.assert_array_equal(oracle.feature_similarity(o, z), 0.0)
+    # the inner product runs over the feature axis, row by row
+    a = rng(41).standard_normal((2, 4, H)); bb = rng(42).standard_normal((2, 4, H))
+    for b in range(2):
+        for s in range(4):
+            ref = a[b, s] @ bb[b, s] / (np.linalg.norm(a[b, s]) * np.linalg.norm(bb[b, s]))
+            assert abs(oracle.feature_similarity(a, bb)[b, s] - ref) < 1e-14
+
+
+def test_similarity_select_planted_angles_window_and_ties():
+    """Planted angles: row j of the response turned by t_j; the k most-turned rows outside
+    the window are chosen, the window always, ties go to the lower position; nothing below
+    lo is ever chosen by similarity."""
+    B, S, H, lo, window, k = 2, 24, 4, 8, 3, 5
+    r = rng(43)
+    t = np.zeros((B, S))
+    t[:, lo:] = r.uniform(0, 3.0, size=(B, S - lo))
+    t[:, :lo] = 3.1                                   # prompt rows moved most, yet not eligible
+    t[1, lo:] = 1.0                                   # sequence 1: one clear top row, then
+    t[1, 15] = 2.9                                    # a three-way tie that the cut splits
+    t[1, 20] = t[1, 21] = t[1, 22] = 2.5
+    x = np.zeros((B, S, H)); y = np.zeros((B, S, H))
+    x[..., 0] = 1.0
+    y[..., 0], y[..., 1] = np.cos(t), np.sin(t)
+    ws = np.array([10, 10])
+    idx, sim = oracle.similarity_select(x, y, lo, ws, window, k)
+    idx3, _ = oracle.similarity_select(x, y, lo, ws, window, 3)
+    assert list(idx3[1]) == [10, 11, 12, 15, 20, 21]
+    for b in range(B):
+        win = set(range(ws[b], ws[b] + window))
+        cand = [j for j in range(lo, S) if j not in win]
+        brute = sorted(cand, key=lambda j: (-t[b, j], j))[:k]
+        assert list(idx[b]) == sorted(win | set(brute))
+        chosen = [j for j in idx[b] if j not in win]
+        rest = [j for j in cand if j not in chosen]
+        assert max(sim[b, chosen]) <= min(sim[b, rest])
+
+
+def test_schedule_rows_union_full_and_empty_slots():
+    S = 30
+    idx = np.array([[3, 7, 20], [5, 6, 7], [0, 29, 1]], np.int32)
+    tracked = np.array([[7, 2, -1, 20, 25], [-1, -1, -1, -1, -1], [29, 29, 0, 15, 3]], np.int32)
+    full = np.array([False, False, True])
+    rows, cu = oracle.schedule_rows(S, idx, tracked, full)
+    assert list(cu) == [0, 5, 8, 38]
+    assert list(rows[0:5]) == [2, 3, 7, 20, 25]
+    assert list(rows[5:8]) == [5, 6, 7]
+    assert list(rows[8:]) == list(range(S))
+    rows2, cu2 = oracle.schedule_rows(S, idx, None, None)
+    assert list(cu2) == [0, 3, 6, 9] and list(rows2) == [3, 7, 20, 5, 6, 7, 0, 1, 29]
+
+
+def _stack_case(layers=3, triggers=(1, 3), gamma=0.9):
+    wl = synth.custom(batch=2, hidden=64, q_heads=2, kv_heads=1, head_dim=16, seq=40, prompt=16,
+                      act="bf16", cache="bf16", seed=44, gamma=gamma, track_k=4)
+    return wl, synth.layer_stack(wl, layers, list(triggers), window=4)
+
+
+def test_layer_schedule_triggers_where_the_states_move_and_refreshes_deeper_layers():
+    """Sequence 0's states move from layer 1 on, sequence 1's never (trigger = L): the drift
+    test fires at layer 1 for sequence 0 only (the tracked rows were recomputed, so sigma
+    measures the change: about 0.99 before, about 0 at the trigger), and layer 2 then
+    recomputes every row of sequence 0, leaving exactly a full recompute from its states."""
+    wl, st = _stack_case()
+    L, B, S = 3, wl.batch, wl.seq
+    rows0 = np.stack([np.arange(s, s + 4) for s in st.window_start])
+    states = [oracle.schedule_prepare(wl, st.w[l], st.hidden_prev[l], rows0, wl.track_k)
+              for l in range(L)]
+    full = np.zeros(B, bool)
+    recs = []
+    for l in range(L):
+        rec = oracle.schedule_layer(states[l], st.hidden_cur[l], full, wl.prompt, st.window_start,
+                                    4, 6, wl.gamma)
+        recs.append(rec)
+        full = rec["full_next"]
+    assert list(recs[0]["decision"]) == [0, 0]
+    assert list(recs[1]["decision"])[0] == 1 and recs[1]["decision"][1] == 0
+    assert recs[0]["sigma"].min() > 0.95 and recs[1]["sigma"][0].max() < 0.5
+    assert list(recs[2]["cu"][1:2]) == [S]                     # sequence 0: every row
+    full2 = oracle.prefill(wl, st.hidden_cur[2], st.w[2])
+    np.testing.assert_array_equal(states[2].cache.k[0], full2.k[0])
+    np.testing.assert_array_equal(states[2].cache.v[0], full2.v[0])
+    np.testing.assert_array_equal(states[2].feat[0], st.hidden_cur[2][0])
+    # sequence 1 at layer 2 refreshed its window, the chosen rows and its tracked rows only
+    r1 = recs[2]["rows"][recs[2]["cu"][1]:]
+    prev = oracle.prefill(wl, st.hidden_prev[2], st.w[2])
+    other = np.setdiff1d(np.arange(S), r1)
+    np.testing.assert_array_equal(states[2].cache.k[1][:, other], prev.k[1][:, other])
+    np.testing.assert_array_equal(states[2].cache.k[1][:, r1], full2.k[1][:, r1])
+    assert set(recs[2]["T_prev"][1].ravel()) <= set(r1)
+
+
+def test_layer_schedule_threshold_extremes():
+    """gamma below -1 never fires (no deeper full refresh); gamma above 1 fires at the first
+    layer for every sequence, so every later layer recomputes all rows."""
+    for gamma, expect in ((-2.0, 0), (2.0, 1)):
+        wl, st = _stack_case(layers=2, triggers=(2, 2), gamma=gamma)
+        rows0 = np.stack([np.arange(s, s + 4) for s in st.window_start])
+        states = [oracle.schedule_prepare(wl, st.w[l], st.hidden_prev[l], rows0, wl.track_k)
+                  for l in range(2)]
+        full = np.zeros(wl.batch, bool)
+        rec0 = oracle.schedule_layer(states[0], st.hidden_cur[0], full, wl.prompt,
+                                     st.window_start, 4, 6, gamma)
+        assert list(rec0["decision"]) == [expect] * wl.batch
+        rec1 = oracle.schedule_layer(states[1], st.hidden_cur[1], rec0["full_next"], wl.prompt,
+                                     st.window_start, 4, 6, gamma)
+        sizes = np.diff(rec1["cu"])
+        assert (sizes == wl.seq).all() == bool(expect)
