@@ -28,7 +28,9 @@ EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatte
            "dllm_set_options", "dllm_block_attention_noalloc", "dllm_facache_state_bytes",
            "dllm_facache_attention", "dllm_refresh_qkv_rope_scatter_varlen",
            "dllm_attention_varlen_workspace_bytes", "dllm_block_attention_varlen",
-           "dllm_last_error")
+           "dllm_similarity_select_workspace_bytes", "dllm_similarity_select",
+           "dllm_schedule_rows_workspace_bytes", "dllm_schedule_rows", "dllm_copy_rows_varlen",
+           "dllm_layer_step_workspace_bytes", "dllm_elastic_layer_step", "dllm_last_error")
 DLLM_OPT_DEBUG, DLLM_OPT_WIDE_OFFSETS = 1, 2
 DLLM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -46,6 +48,16 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("max_seq", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+class LayerStep(ctypes.Structure):
+    """The C struct dllm_layer_step (device pointers and sizes)."""
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "hidden_cur", "hidden_feat", "w_qkv", "window_start", "track_idx", "track_buf", "full",
+        "decision", "step_rows", "rows", "cu_rows", "q", "out", "lse", "attn_mass", "sigma")] + \
+        [(name, ctypes.c_int32) for name in (
+            "hidden_size", "num_q_heads", "lo", "window", "k_select", "k_track")] + \
+        [(name, ctypes.c_float) for name in ("rope_base", "softmax_scale", "gamma")]
 
 
 class CCache(ctypes.Structure):
@@ -91,6 +103,23 @@ def _load():
     lib.dllm_block_attention_varlen.argtypes = [ctypes.POINTER(CCache), P, i32, i32, P, P, i32,
                                                 i32, ctypes.c_float, P, P, P, P, ctypes.c_size_t,
                                                 P]
+    lib.dllm_similarity_select_workspace_bytes.restype = ctypes.c_size_t
+    lib.dllm_similarity_select_workspace_bytes.argtypes = [i32, i32]
+    lib.dllm_similarity_select.restype = i32
+    lib.dllm_similarity_select.argtypes = [i32, i32, i32, i32, P, P, i32, P, i32, i32, P, P, P,
+                                           ctypes.c_size_t, P]
+    lib.dllm_schedule_rows_workspace_bytes.restype = ctypes.c_size_t
+    lib.dllm_schedule_rows_workspace_bytes.argtypes = [i32, i32]
+    lib.dllm_schedule_rows.restype = i32
+    lib.dllm_schedule_rows.argtypes = [i32, i32, P, i32, P, i32, P, P, P, P, i32, P, P,
+                                       ctypes.c_size_t, P]
+    lib.dllm_copy_rows_varlen.restype = i32
+    lib.dllm_copy_rows_varlen.argtypes = [i32, i32, i32, P, P, P, P, i32, P]
+    lib.dllm_layer_step_workspace_bytes.restype = ctypes.c_size_t
+    lib.dllm_layer_step_workspace_bytes.argtypes = [ctypes.POINTER(CacheDesc), i32, i32]
+    lib.dllm_elastic_layer_step.restype = i32
+    lib.dllm_elastic_layer_step.argtypes = [ctypes.POINTER(CCache), ctypes.POINTER(LayerStep), P,
+                                            ctypes.c_size_t, P]
     lib.dllm_drift_check.restype = i32
     lib.dllm_drift_check.argtypes = [ctypes.POINTER(CCache), i32, i32, ctypes.c_float, P, P, P, P,
                                      P, P]
@@ -264,7 +293,7 @@ def dllm_block_attention_varlen(cache: Cache, q: torch.Tensor, num_q_heads: int,
                                 cu_rows: torch.Tensor, seq_lens: torch.Tensor, max_rows: int,
                                 softmax_scale: float, out: torch.Tensor, lse=None, attn_mass=None,
                                 workspace=None, stream=None):
-    """q, out [T, Hq, D] bf16 (packed rows), cu_rows [B+1] int32, seq_lens [B] int32 (device),
+    """q, out [T, Hq, D] bf16 (packed rows), cu_rows [B+1] int32, seq_lens [B] int32 or None,
     lse [T * Hq] fp32 or None, attn_mass [B, Hq, S] fp32 or None."""
     d = cache.desc
     T = q.shape[0] if q.dim() == 3 else -1
@@ -273,7 +302,8 @@ def dllm_block_attention_varlen(cache: Cache, q: torch.Tensor, num_q_heads: int,
     _expect(q, "q", (T, num_q_heads, d.head_dim), q.dtype)
     _expect(out, "out", (T, num_q_heads, d.head_dim), q.dtype)
     _expect(cu_rows, "cu_rows", (d.batch + 1,), torch.int32)
-    _expect(seq_lens, "seq_lens", (d.batch,), torch.int32)
+    if seq_lens is not None:
+        _expect(seq_lens, "seq_lens", (d.batch,), torch.int32)
     if lse is not None:
         _expect(lse, "lse", (T * num_q_heads,), torch.float32)
     if attn_mass is not None:
@@ -383,6 +413,132 @@ def dllm_drift_check(cache: Cache, num_q_heads: int, k: int, gamma: float,
     _check(lib.dllm_drift_check(
         ctypes.byref(cache.c), num_q_heads, k, float(gamma), _ptr(track_idx), _ptr(track_buf),
         _ptr(attn_mass), _ptr(sigma_out), _ptr(refresh_out), _stream(stream)))
+
+
+def dllm_similarity_select(hidden_cur: torch.Tensor, hidden_cached: torch.Tensor, lo: int,
+                           window_start, window: int, k: int, idx_out: torch.Tensor,
+                           sim_out=None, workspace=None, stream=None):
+    """hidden_cur, hidden_cached [B, S, H] (bf16 or fp32), window_start [B] int32 or None,
+    idx_out [B, window + k] int32, sim_out [B, S] fp64 or None."""
+    if hidden_cur.dim() != 3 or hidden_cur.dtype not in _DTYPE_CODE:
+        raise DllmError(DLLM_EINVAL, "hidden_cur: [B, S, H] bf16 or fp32")
+    B, S, H = hidden_cur.shape
+    _expect(hidden_cur, "hidden_cur", (B, S, H), hidden_cur.dtype)
+    _expect(hidden_cached, "hidden_cached", (B, S, H), hidden_cur.dtype)
+    if window_start is not None:
+        _expect(window_start, "window_start", (B,), torch.int32)
+    _expect(idx_out, "idx_out", (B, window + k), torch.int32)
+    if sim_out is not None:
+        _expect(sim_out, "sim_out", (B, S), torch.float64)
+    elif workspace is None:
+        workspace = _scratch(lib.dllm_similarity_select_workspace_bytes(B, S), hidden_cur.device,
+                             stream)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(lib.dllm_similarity_select(B, S, H, _DTYPE_CODE[hidden_cur.dtype], _ptr(hidden_cur),
+                                      _ptr(hidden_cached), lo, _ptr(window_start), window, k,
+                                      _ptr(idx_out), _ptr(sim_out), _ptr(workspace), ws_bytes,
+                                      _stream(stream)))
+
+
+def dllm_schedule_rows(max_seq: int, idx: torch.Tensor, tracked, full_in, decision, full_out,
+                       rows_out: torch.Tensor, cu_out: torch.Tensor, workspace=None,
+                       stream=None):
+    """idx [B, n] int32, tracked [B, ...] int32 or None, full_in / decision / full_out [B]
+    uint8 or None, rows_out [capacity >= B * S] int32, cu_out [B + 1] int32."""
+    B = idx.shape[0]
+    n = idx.numel() // B if B else 0
+    _expect(idx, "idx", (B, n), torch.int32)
+    m = 0
+    if tracked is not None:
+        m = tracked.numel() // B
+        _expect(tracked.view(B, m), "tracked", (B, m), torch.int32)
+    for name, t in (("full_in", full_in), ("decision", decision), ("full_out", full_out)):
+        if t is not None:
+            _expect(t, name, (B,), torch.uint8)
+    if rows_out.dim() != 1:
+        raise DllmError(DLLM_EINVAL, "rows_out must be 1-D")
+    _expect(rows_out, "rows_out", (rows_out.numel(),), torch.int32)
+    _expect(cu_out, "cu_out", (B + 1,), torch.int32)
+    if workspace is None:
+        workspace = _scratch(lib.dllm_schedule_rows_workspace_bytes(B, max_seq) + 256,
+                             idx.device, stream)
+    base = (-workspace.data_ptr()) % 256
+    ws = workspace[base:]
+    _check(lib.dllm_schedule_rows(B, max_seq, _ptr(idx), n, _ptr(tracked), m, _ptr(full_in),
+                                  _ptr(decision), _ptr(full_out), _ptr(rows_out), rows_out.numel(),
+                                  _ptr(cu_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def dllm_copy_rows_varlen(src: torch.Tensor, dst: torch.Tensor, rows: torch.Tensor,
+                          cu_rows: torch.Tensor, stream=None):
+    """src, dst [B, S, ...] (same shape and dtype), rows [capacity] int32, cu_rows [B + 1]."""
+    if src.dim() < 2:
+        raise DllmError(DLLM_EINVAL, "src must be [B, S, ...]")
+    B, S = src.shape[:2]
+    _expect(src, "src", tuple(src.shape), src.dtype)
+    _expect(dst, "dst", tuple(src.shape), src.dtype)
+    _expect(rows, "rows", (rows.numel(),), torch.int32)
+    _expect(cu_rows, "cu_rows", (B + 1,), torch.int32)
+    row_bytes = src[0, 0].numel() * src.element_size()
+    _check(lib.dllm_copy_rows_varlen(B, S, row_bytes, _ptr(src), _ptr(dst), _ptr(rows),
+                                     _ptr(cu_rows), rows.numel(), _stream(stream)))
+
+
+def dllm_layer_step_workspace_bytes(cache: Cache, hidden_size: int, num_q_heads: int) -> int:
+    return lib.dllm_layer_step_workspace_bytes(ctypes.byref(cache.desc), hidden_size, num_q_heads)
+
+
+def dllm_elastic_layer_step(cache: Cache, *, hidden_cur, hidden_feat, w_qkv, window_start,
+                            track_idx, track_buf, full, decision, step_rows, rows, cu_rows, q,
+                            out, lse, attn_mass, sigma, num_q_heads: int, lo: int, window: int,
+                            k_select: int, k_track: int, rope_base: float, softmax_scale: float,
+                            gamma: float, workspace=None, stream=None):
+    """One layer of the schedule (see the header for the six stages).  Shapes (S, B from the
+    cache, cap = B * S): hidden_cur / hidden_feat [B, S, H] bf16, w_qkv [N, H] bf16,
+    window_start [B] int32, track_idx [B, Hq, k_track] int32, track_buf [B, Hq, k_track, 2, D]
+    bf16, full / decision [B] uint8, step_rows [B, window + k_select] int32, rows [cap] int32,
+    cu_rows [B + 1] int32, q / out [cap, Hq, D] bf16, lse [cap * Hq] fp32 or None,
+    attn_mass [B, Hq, S] fp32, sigma [B, Hq] fp32."""
+    d = cache.desc
+    B, S, D, Hq = d.batch, d.max_seq, d.head_dim, num_q_heads
+    H = hidden_cur.shape[-1]
+    cap = B * S
+    bf = torch.bfloat16
+    _expect(hidden_cur, "hidden_cur", (B, S, H), bf)
+    _expect(hidden_feat, "hidden_feat", (B, S, H), bf)
+    _expect(w_qkv, "w_qkv", ((Hq + 2 * d.num_kv_heads) * D, H), bf)
+    if window_start is not None:
+        _expect(window_start, "window_start", (B,), torch.int32)
+    _expect(track_idx, "track_idx", (B, Hq, k_track), torch.int32)
+    _expect(track_buf, "track_buf", (B, Hq, k_track, 2, D), bf)
+    _expect(full, "full", (B,), torch.uint8)
+    _expect(decision, "decision", (B,), torch.uint8)
+    _expect(step_rows, "step_rows", (B, window + k_select), torch.int32)
+    _expect(rows, "rows", (cap,), torch.int32)
+    _expect(cu_rows, "cu_rows", (B + 1,), torch.int32)
+    _expect(q, "q", (cap, Hq, D), bf)
+    _expect(out, "out", (cap, Hq, D), bf)
+    if lse is not None:
+        _expect(lse, "lse", (cap * Hq,), torch.float32)
+    _expect(attn_mass, "attn_mass", (B, Hq, S), torch.float32)
+    _expect(sigma, "sigma", (B, Hq), torch.float32)
+    if workspace is None:
+        need = dllm_layer_step_workspace_bytes(cache, H, Hq)
+        if need == 0:
+            raise DllmError(DLLM_EINVAL, "invalid layer step shape")
+        workspace = _scratch(need, hidden_cur.device, stream)
+    a = LayerStep()
+    for name, t in (("hidden_cur", hidden_cur), ("hidden_feat", hidden_feat), ("w_qkv", w_qkv),
+                    ("window_start", window_start), ("track_idx", track_idx),
+                    ("track_buf", track_buf), ("full", full), ("decision", decision),
+                    ("step_rows", step_rows), ("rows", rows), ("cu_rows", cu_rows), ("q", q),
+                    ("out", out), ("lse", lse), ("attn_mass", attn_mass), ("sigma", sigma)):
+        setattr(a, name, None if t is None else t.data_ptr())
+    a.hidden_size, a.num_q_heads, a.lo, a.window = H, Hq, lo, window
+    a.k_select, a.k_track = k_select, k_track
+    a.rope_base, a.softmax_scale, a.gamma = rope_base, softmax_scale, gamma
+    _check(lib.dllm_elastic_layer_step(ctypes.byref(cache.c), ctypes.byref(a), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
 
 
 def dllm_fp8_e4m3_roundtrip(x: torch.Tensor, scale: float, codes: torch.Tensor,

@@ -105,8 +105,8 @@ dllm_status device_symbols(DeviceSymbols** out) {
 // Debug-mode device pass over the refresh index lists: one workgroup per sequence; every
 // position that is out of [0, S) or not above its predecessor is reported, the lowest packed
 // index winning.  With row offsets cu (a variable-length batch) sequence b's list is
-// idx[cu[b] .. cu[b + 1]); offsets that are not non-decreasing from 0 to T with at most
-// max_rows rows per sequence are reported as -1 - b.
+// idx[cu[b] .. cu[b + 1]); offsets that do not rise from 0, stay within the capacity T and
+// give each sequence at most max_rows rows are reported as -1 - b.
 __global__ __launch_bounds__(256) void check_index_lists(const int32_t* idx, const int32_t* cu, int n,
                                                          int T, int S, int32_t* report) {
   const int b = blockIdx.x;
@@ -114,8 +114,7 @@ __global__ __launch_bounds__(256) void check_index_lists(const int32_t* idx, con
   if (cu) {
     r0 = cu[b];
     cnt = cu[b + 1] - r0;
-    const bool bad_cu = (b == 0 && r0 != 0) || r0 < 0 || cnt < 0 || cnt > n || cu[b + 1] > T ||
-                        (b == (int)gridDim.x - 1 && cu[b + 1] != T);
+    const bool bad_cu = (b == 0 && r0 != 0) || r0 < 0 || cnt < 0 || cnt > n || cu[b + 1] > T;
     if (bad_cu) {
       if (threadIdx.x == 0) atomicMin(&report[0], -1 - b);
       return;
@@ -130,16 +129,16 @@ __global__ __launch_bounds__(256) void check_index_lists(const int32_t* idx, con
 }
 
 // Debug-mode pass over the offsets of a variable-length attention call: sequence b is
-// reported as -1 - b when its row offsets leave [0, T], decrease, give it more than n rows, or
-// miss 0 / T at the ends, or when its key count is outside [1, S].
+// reported as -1 - b when its row offsets leave [0, T] (T: the capacity), decrease, give it
+// more than n rows or do not start at 0, or when its key count is outside [1, S].
 __global__ __launch_bounds__(256) void check_varlen_offsets(const int32_t* cu, const int32_t* lens,
                                                             int B, int n, int T, int S,
                                                             int32_t* report) {
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= B) return;
-  const int r0 = cu[b], r1 = cu[b + 1], len = lens[b];
+  const int r0 = cu[b], r1 = cu[b + 1], len = lens ? lens[b] : S;
   const bool bad = r0 < 0 || r1 < r0 || r1 - r0 > n || r1 > T || (b == 0 && r0 != 0) ||
-                   (b == B - 1 && r1 != T) || len < 1 || len > S;
+                   len < 1 || len > S;
   if (bad) atomicMin(report, -1 - b);
 }
 
@@ -410,7 +409,7 @@ dllm_status attention_call(const dllm_cache* c, const void* q, int32_t act_dtype
   if (!varlen) total = (long long)d.batch * n;
   if (total > (long long)d.batch * n)
     return fail(DLLM_EINVAL, "total rows %lld above B * max rows = %lld", total, (long long)d.batch * n);
-  if (varlen && total > 0 && (!cu || !lens)) return fail(DLLM_EINVAL, "null cu_rows or seq_lens");
+  if (varlen && total > 0 && !cu) return fail(DLLM_EINVAL, "null cu_rows");
   if (varlen && act_dtype == DLLM_F32)
     return fail(DLLM_EUNSUPPORTED, "variable-length batches need bf16 queries");
   if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
@@ -605,6 +604,189 @@ dllm_status dllm_drift_check(const dllm_cache* c, int32_t num_q_heads, int32_t k
   a.gamma = gamma;
   hipStream_t s = (hipStream_t)stream;
   return finish(dllm::launch_drift(a, s), s, "drift");
+}
+
+size_t dllm_similarity_select_workspace_bytes(int32_t batch, int32_t max_seq) {
+  if (batch <= 0 || max_seq <= 0) return 0;
+  return (size_t)batch * max_seq * sizeof(double);
+}
+
+dllm_status dllm_similarity_select(int32_t batch, int32_t max_seq, int32_t hidden_size,
+                                   int32_t act_dtype, const void* hidden_cur,
+                                   const void* hidden_cached, int32_t lo,
+                                   const int32_t* window_start, int32_t window, int32_t k,
+                                   int32_t* idx_out, double* sim_out, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  if (batch <= 0 || max_seq <= 0) return fail(DLLM_EINVAL, "batch and max_seq must be positive");
+  if (max_seq > dllm::kSelectMaxSeq)
+    return fail(DLLM_EUNSUPPORTED, "similarity selection supports S <= %d", dllm::kSelectMaxSeq);
+  if (act_dtype != DLLM_BF16 && act_dtype != DLLM_F32)
+    return fail(DLLM_EINVAL, "act_dtype %d: DLLM_BF16 or DLLM_F32", act_dtype);
+  const int epc = act_dtype == DLLM_BF16 ? 8 : 4;
+  if (hidden_size <= 0 || hidden_size % epc)
+    return fail(DLLM_EINVAL, "hidden_size %d must be a positive multiple of %d", hidden_size, epc);
+  if (lo < 0 || lo >= max_seq) return fail(DLLM_EINVAL, "lo=%d outside [0, S=%d)", lo, max_seq);
+  if (window < 0 || k < 0 || (long long)window + k > (long long)max_seq - lo)
+    return fail(DLLM_EINVAL, "window=%d, k=%d: need window + k <= S - lo = %d", window, k, max_seq - lo);
+  if (window > 0 && !window_start) return fail(DLLM_EINVAL, "null window_start with window > 0");
+  if (window + k == 0) {
+    g_err[0] = '\0';
+    return DLLM_OK;
+  }
+  if (!hidden_cur || !hidden_cached || !idx_out) return fail(DLLM_EINVAL, "null input or output");
+  if (!aligned16(hidden_cur) || !aligned16(hidden_cached))
+    return fail(DLLM_EINVAL, "hidden arrays must be 16-byte aligned");
+  double* sim = sim_out;
+  if (!sim) {
+    const size_t need = dllm_similarity_select_workspace_bytes(batch, max_seq);
+    if (ws_bytes < need) return fail(DLLM_ESIZE, "selection workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if (!workspace || ((uintptr_t)workspace & 7u)) return fail(DLLM_EINVAL, "workspace must be an 8-byte aligned device pointer");
+    sim = (double*)workspace;
+  } else if ((uintptr_t)sim_out & 7u) {
+    return fail(DLLM_EINVAL, "sim_out must be 8-byte aligned");
+  }
+  dllm::SelectArgs a;
+  a.cur = hidden_cur;
+  a.cached = hidden_cached;
+  a.sim = sim;
+  a.window_start = window_start;
+  a.idx_out = idx_out;
+  a.B = batch;
+  a.S = max_seq;
+  a.H = hidden_size;
+  a.act = act_dtype;
+  a.lo = lo;
+  a.window = window;
+  a.k = k;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dllm::launch_similarity_select(a, s), s, "similarity select");
+}
+
+size_t dllm_schedule_rows_workspace_bytes(int32_t batch, int32_t max_seq) {
+  if (batch <= 0 || max_seq <= 0) return 0;
+  return round_up((size_t)batch * max_seq * sizeof(int32_t), 256) + (size_t)batch * sizeof(int32_t);
+}
+
+dllm_status dllm_schedule_rows(int32_t batch, int32_t max_seq, const int32_t* idx, int32_t n,
+                               const int32_t* tracked, int32_t m, const uint8_t* full_in,
+                               const uint8_t* decision, uint8_t* full_out, int32_t* rows_out,
+                               int32_t capacity, int32_t* cu_out, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  if (batch <= 0 || max_seq <= 0) return fail(DLLM_EINVAL, "batch and max_seq must be positive");
+  if (max_seq > dllm::kScheduleMaxSeq)
+    return fail(DLLM_EUNSUPPORTED, "the row schedule supports S <= %d", dllm::kScheduleMaxSeq);
+  if (n < 0 || m < 0) return fail(DLLM_EINVAL, "n and m must be >= 0");
+  if (n > 0 && !idx) return fail(DLLM_EINVAL, "null idx with n > 0");
+  if (m > 0 && !tracked) return fail(DLLM_EINVAL, "null tracked with m > 0");
+  if ((long long)capacity < (long long)batch * max_seq)
+    return fail(DLLM_ESIZE, "capacity %d below B * S = %lld", capacity, (long long)batch * max_seq);
+  if (!rows_out || !cu_out) return fail(DLLM_EINVAL, "null rows_out or cu_out");
+  const size_t need = dllm_schedule_rows_workspace_bytes(batch, max_seq);
+  if (ws_bytes < need) return fail(DLLM_ESIZE, "schedule workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (!workspace || ((uintptr_t)workspace & 255u))
+    return fail(DLLM_EINVAL, "workspace must be a 256-byte aligned device pointer");
+  dllm::SchedArgs a;
+  a.idx = idx;
+  a.tracked = m > 0 ? tracked : nullptr;
+  a.full_in = full_in;
+  a.decision = decision;
+  a.full_out = full_out;
+  a.rows = rows_out;
+  a.cu = cu_out;
+  a.temp = (int32_t*)workspace;
+  a.counts = (int32_t*)((char*)workspace + round_up((size_t)batch * max_seq * sizeof(int32_t), 256));
+  a.B = batch;
+  a.S = max_seq;
+  a.n = n;
+  a.m = m;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dllm::launch_schedule_rows(a, s), s, "schedule rows");
+}
+
+dllm_status dllm_copy_rows_varlen(int32_t batch, int32_t max_seq, int32_t row_bytes,
+                                  const void* src, void* dst, const int32_t* rows,
+                                  const int32_t* cu_rows, int32_t capacity, void* stream) {
+  if (batch <= 0 || max_seq <= 0) return fail(DLLM_EINVAL, "batch and max_seq must be positive");
+  if (row_bytes <= 0 || row_bytes % 16) return fail(DLLM_EINVAL, "row_bytes %d: a positive multiple of 16", row_bytes);
+  if (capacity < 0) return fail(DLLM_EINVAL, "capacity < 0");
+  if (capacity == 0) {
+    g_err[0] = '\0';
+    return DLLM_OK;
+  }
+  if (!src || !dst || !rows || !cu_rows) return fail(DLLM_EINVAL, "null pointer argument");
+  if (!aligned16(src) || !aligned16(dst)) return fail(DLLM_EINVAL, "src and dst must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dllm::launch_copy_rows(src, dst, row_bytes, batch, max_seq, rows, cu_rows, capacity, s),
+                s, "copy rows");
+}
+
+namespace {
+// Workspace of one schedule layer: the similarities, the row schedule's scratch, the refresh's
+// partials (capacity B * S rows) and the attention's split states.
+struct StepWs {
+  size_t sim, sched, refresh, attn, total;
+};
+StepWs step_ws(const dllm_cache_desc* d, int32_t H, int32_t Hq) {
+  StepWs w{};
+  const long long cap = (long long)d->batch * d->max_seq;
+  const int N = (Hq + 2 * d->num_kv_heads) * d->head_dim;
+  w.sim = round_up(dllm_similarity_select_workspace_bytes(d->batch, d->max_seq), 256);
+  w.sched = round_up(dllm_schedule_rows_workspace_bytes(d->batch, d->max_seq), 256);
+  w.refresh = round_up(dllm::refresh_workspace_bytes(DLLM_BF16, (int)cap, N, H), 256);
+  w.attn = round_up(attention_ws_bytes(d, Hq, d->max_seq, cap), 256);
+  w.total = w.sim + w.sched + w.refresh + w.attn + 256;
+  return w;
+}
+}  // namespace
+
+size_t dllm_layer_step_workspace_bytes(const dllm_cache_desc* d, int32_t hidden_size,
+                                       int32_t num_q_heads) {
+  if (check_desc(d) != DLLM_OK || hidden_size <= 0 || num_q_heads <= 0 ||
+      num_q_heads % d->num_kv_heads || (long long)d->batch * d->max_seq > 0x7fffffffLL)
+    return 0;
+  return step_ws(d, hidden_size, num_q_heads).total;
+}
+
+dllm_status dllm_elastic_layer_step(const dllm_cache* c, const dllm_layer_step* a,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  dllm_status st = check_cache(c);
+  if (st) return st;
+  if (!a) return fail(DLLM_EINVAL, "null step arguments");
+  const dllm_cache_desc& d = c->desc;
+  if (d.kv_dtype != DLLM_BF16) return fail(DLLM_EUNSUPPORTED, "the layer step needs a bf16 cache");
+  if ((long long)d.batch * d.max_seq > 0x7fffffffLL) return fail(DLLM_EINVAL, "B * S too large");
+  const size_t need = dllm_layer_step_workspace_bytes(&d, a->hidden_size, a->num_q_heads);
+  if (!need) return fail(DLLM_EINVAL, "invalid hidden_size or num_q_heads");
+  if (ws_bytes < need) return fail(DLLM_ESIZE, "layer step workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (!workspace) return fail(DLLM_EINVAL, "null workspace");
+  if (!a->full || !a->decision) return fail(DLLM_EINVAL, "null full or decision");
+  const StepWs w = step_ws(&d, a->hidden_size, a->num_q_heads);
+  char* base = (char*)round_up((uintptr_t)workspace, 256);
+  char* ws_sim = base;
+  char* ws_sched = ws_sim + w.sim;
+  char* ws_ref = ws_sched + w.sched;
+  char* ws_att = ws_ref + w.refresh;
+  const int B = d.batch, S = d.max_seq, Hq = a->num_q_heads;
+  const int cap = B * S;
+  st = dllm_similarity_select(B, S, a->hidden_size, DLLM_BF16, a->hidden_cur, a->hidden_feat,
+                              a->lo, a->window_start, a->window, a->k_select, a->step_rows,
+                              nullptr, ws_sim, w.sim, stream);
+  if (st) return st;
+  st = dllm_schedule_rows(B, S, a->step_rows, a->window + a->k_select, a->track_idx,
+                          Hq * a->k_track, a->full, a->decision, a->full, a->rows, cap,
+                          a->cu_rows, ws_sched, w.sched, stream);
+  if (st) return st;
+  st = refresh_call(c, a->hidden_cur, a->hidden_size, DLLM_BF16, a->rows, a->cu_rows, S, cap,
+                    a->w_qkv, Hq, a->rope_base, a->q, ws_ref, w.refresh, stream);
+  if (st) return st;
+  st = attention_call(c, a->q, DLLM_BF16, Hq, S, a->softmax_scale, a->out, a->lse, a->attn_mass,
+                      ws_att, w.attn, false, stream, a->cu_rows, nullptr, cap);
+  if (st) return st;
+  st = dllm_drift_check(c, Hq, a->k_track, a->gamma, a->track_idx, a->track_buf, a->attn_mass,
+                        a->sigma, a->decision, stream);
+  if (st) return st;
+  return dllm_copy_rows_varlen(B, S, a->hidden_size * 2, a->hidden_cur, a->hidden_feat, a->rows,
+                               a->cu_rows, cap, stream);
 }
 
 dllm_status dllm_fp8_e4m3_roundtrip(const float* x, int64_t n, float scale, uint8_t* codes,

@@ -104,6 +104,7 @@ __global__ __launch_bounds__(64) void attn_merge(AttnArgs a, int splits) {
   const int G = a.Hq / a.Hkv;
   const size_t nrows_all = (size_t)a.T * a.Hq;
   const size_t pr0 = blockIdx.x;  // q0 * Hq + g * rows + r (q0: the sequence's first row)
+  if (pr0 >= (size_t)live_rows(a.cu, a.B, a.T) * a.Hq) return;   // past the rows present
   const int b = seq_of_row(a.cu, a.B, a.n, (int)(pr0 / a.Hq));
   const int nb = seq_rows(a.cu, a.n, b), q0 = seq_row0(a.cu, a.n, b);
   const int rows = nb * G;

@@ -189,6 +189,11 @@ __device__ __forceinline__ int seq_rows(const int32_t* cu, int n, int b) {
   return cu ? cu[b + 1] - cu[b] : n;
 }
 __device__ __forceinline__ int seq_keys(const int32_t* lens, int S, int b) { return lens ? lens[b] : S; }
+// Packed rows actually present: cu[B] (a device-side schedule may fill fewer rows than the
+// packed arrays hold), never more than the capacity cap; cap without offsets.
+__device__ __forceinline__ int live_rows(const int32_t* cu, int B, int cap) {
+  return cu ? min(cu[B], cap) : cap;
+}
 // The sequence that packed row m belongs to (the last b with cu[b] <= m, so sequences without
 // rows are passed over).
 __device__ __forceinline__ int seq_of_row(const int32_t* cu, int B, int n, int m) {

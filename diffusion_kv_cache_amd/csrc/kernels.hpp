@@ -27,7 +27,8 @@ struct RefreshArgs {
   int kind;              // cache dtype
   double rope_base;
   float* ws;             // split-K partials [8][M][N] (small-M path only)
-  const int32_t* cu;     // [B + 1] row offsets of a variable-length batch, or null (n rows each)
+  const int32_t* cu;     // [B + 1] row offsets of a variable-length batch, or null (n rows each);
+                         // with cu, M is the capacity and cu[B] (read on the device) the rows
 };
 
 // Rows (B * n) up to which a bf16 refresh takes the split-K path.
@@ -57,7 +58,8 @@ struct AttnArgs {
   float scale;           // softmax scale
   // Variable-length batches: query rows of sequence b are [cu[b], cu[b + 1]) of q and out
   // (n is then the largest count), its keys the first lens[b] cache rows; null: n rows and S
-  // keys each.  T: all query rows (B * n without cu).
+  // keys each.  T: all query rows (B * n without cu), or with cu the capacity of the packed
+  // arrays (the rows present, cu[B], are read on the device).
   const int32_t* cu;
   const int32_t* lens;
   int T;
@@ -115,5 +117,38 @@ hipError_t launch_drift(const DriftArgs& a, hipStream_t s);
 
 hipError_t launch_fp8_roundtrip(const float* x, int64_t n, float scale, uint8_t* codes,
                                 float* decoded, hipStream_t s);
+
+// Feature-similarity row choice (window + k least similar response rows per sequence).
+struct SelectArgs {
+  const void* cur;             // [B, S, H] act dtype
+  const void* cached;          // [B, S, H]
+  double* sim;                 // [B, S]: rows >= lo written
+  const int32_t* window_start; // [B] (window > 0)
+  int32_t* idx_out;            // [B, window + k]
+  int B, S, H, act, lo, window, k;
+};
+hipError_t launch_similarity_select(const SelectArgs& a, hipStream_t s);
+// Largest S of the selection (one workgroup of 1024 threads holds a sequence, 8 rows each).
+constexpr int kSelectMaxSeq = 8192;
+
+// Per-layer rows of the Elastic-Cache schedule, packed with offsets.
+struct SchedArgs {
+  const int32_t* idx;          // [B, n] step rows
+  const int32_t* tracked;      // [B, m] or null (-1: empty)
+  const uint8_t* full_in;      // [B] or null
+  const uint8_t* decision;     // [B] or null
+  uint8_t* full_out;           // [B] or null
+  int32_t* rows;               // packed rows (capacity >= B * S)
+  int32_t* cu;                 // [B + 1]
+  int32_t* temp;               // [B, S] workspace
+  int32_t* counts;             // [B] workspace
+  int B, S, n, m;
+};
+hipError_t launch_schedule_rows(const SchedArgs& a, hipStream_t s);
+// Largest S of the row schedule (one byte of LDS per row, 32 rows per thread).
+constexpr int kScheduleMaxSeq = 32768;
+
+hipError_t launch_copy_rows(const void* src, void* dst, int row_bytes, int B, int S,
+                            const int32_t* rows, const int32_t* cu, int cap, hipStream_t s);
 
 }  // namespace dllm

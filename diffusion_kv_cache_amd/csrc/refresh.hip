@@ -165,6 +165,8 @@ __device__ __forceinline__ void tile_epilogue(const RefreshArgs& a,
 // ------------------------------------------------------------------------------------------
 template <typename T, int KIND, int TM, int D, int BKC>
 __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
+  a.M = live_rows(a.cu, a.B, a.M);
+  if ((int)blockIdx.y * TM >= a.M) return;       // row tiles past the packed rows present
   constexpr bool BF = sizeof(T) == 2;
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int BK = BKC * EPC;              // elements of K per stage
@@ -331,6 +333,8 @@ __global__ __launch_bounds__(256) void refresh_tiled(RefreshArgs a) {
 // ------------------------------------------------------------------------------------------
 template <int KIND, int TM, int D, int BKC, int NST, int WM, bool SB>
 __global__ __launch_bounds__(128 * WM) void refresh_gemm(RefreshArgs a) {
+  a.M = live_rows(a.cu, a.B, a.M);
+  if ((int)blockIdx.y * TM >= a.M) return;       // row tiles past the packed rows present
   constexpr int NW = 2 * WM;                 // waves: WM along the rows x 2 column groups
   constexpr int EPC = 8;                     // bf16 per 16-byte chunk
   constexpr int BK = BKC * EPC;              // k per stage

@@ -29,6 +29,10 @@ constexpr int kPartLd = 132;   // floats per staged partial row (128 + 4: no ban
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6)))
 void refresh_partial(RefreshArgs a, float* part) {
   extern __shared__ u32x4 As[];                  // [32 rows][cpr chunks], swizzled
+  // Rows present (a variable-length batch may hold fewer than its capacity): they set the
+  // workspace's row stride here and in refresh_reduce alike.
+  a.M = live_rows(a.cu, a.B, a.M);
+  if ((int)blockIdx.z * 32 >= a.M) return;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
   const int N = (a.Hq + 2 * a.Hkv) * a.D;
   const int p = blockIdx.x;                      // partitions fastest: the eight workgroups
@@ -113,6 +117,7 @@ void refresh_partial(RefreshArgs a, float* part) {
 template <int D, int KIND>
 __global__ __launch_bounds__(64) void refresh_reduce(RefreshArgs a, const float* part) {
   constexpr int HALF = D / 2;
+  a.M = live_rows(a.cu, a.B, a.M);
   constexpr int PPL = HALF / 16;                 // pairs per lane: 4 (D = 128) or 2 (D = 64)
   typedef __attribute__((ext_vector_type(PPL))) float fvec;
   const int lane = threadIdx.x, L = lane & 15;

@@ -141,12 +141,15 @@ DLLM_API dllm_status dllm_refresh_qkv_rope_scatter(const dllm_cache *c, const vo
  * that concatenates variable-length sequences to keep the GPU busy).  The refreshed rows of
  * all sequences are packed without padding: sequence b's rows are packed rows
  * [cu_rows[b], cu_rows[b + 1]) of refresh_idx and q_out, with cu_rows[0] = 0 and
- * cu_rows[B] = total_rows; a sequence may have no rows.  Everything else is as in
+ * cu_rows[B] <= total_rows; a sequence may have no rows.  The kernels read cu_rows[B] on the
+ * device, so the offsets may come from an earlier kernel on the same stream (a device-side
+ * schedule, dllm_schedule_rows) and total_rows is only the capacity the launch is sized for;
+ * packed rows past cu_rows[B] are not touched.  Everything else is as in
  * dllm_refresh_qkv_rope_scatter (same arithmetic and reduction order, so a row stores the same
  * bits as in a full refresh):
  *   refresh_idx  device, [total_rows] int32: per sequence sorted, unique, in [0, S)
  *   cu_rows      device, [B + 1] int32 row offsets
- *   total_rows   cu_rows[B] (0 enqueues nothing)
+ *   total_rows   capacity of the packed arrays, >= cu_rows[B] (0 enqueues nothing)
  *   max_rows     the largest rows per sequence, <= S
  *   q_out        device, [total_rows, Hq, D] of act_dtype
  *   workspace    dllm_refresh_workspace_bytes(d, H, act, total_rows / B rounded up, Hq) is
@@ -203,9 +206,11 @@ DLLM_API dllm_status dllm_block_attention(const dllm_cache *c, const void *q, in
  * seq_lens[b] cache rows only:
  *   out[r, h] = sum_{j < seq_lens[b]} softmax_j(<q[r, h], K[b, g, j]> * softmax_scale) V[b, g, j]
  * for every packed row r of sequence b.
- *   q, out       device, [total_rows, Hq, D] bf16
- *   cu_rows      device, [B + 1] int32 row offsets (cu_rows[0] = 0, cu_rows[B] = total_rows)
- *   seq_lens     device, [B] int32, each in [1, S]
+ *   q, out       device, [total_rows, Hq, D] bf16 (rows past cu_rows[B] are not touched)
+ *   cu_rows      device, [B + 1] int32 row offsets (cu_rows[0] = 0, cu_rows[B] <= total_rows,
+ *                read on the device as in dllm_refresh_qkv_rope_scatter_varlen)
+ *   total_rows   capacity of the packed arrays
+ *   seq_lens     device, [B] int32, each in [1, S], or NULL: every sequence attends over all S
  *   max_rows     the largest rows per sequence (<= S)
  *   lse          device, [total_rows * Hq] fp32 or NULL: sequence b's block at
  *                cu_rows[b] * Hq, laid out [Hq][rows of b]
@@ -305,6 +310,115 @@ DLLM_API dllm_status dllm_facache_attention(const dllm_cache *c, void *q_cache,
 DLLM_API dllm_status dllm_drift_check(const dllm_cache *c, int32_t num_q_heads, int32_t k, float gamma,
                              int32_t *track_idx, void *track_buf, const float *attn_mass,
                              float *sigma_out, uint8_t *refresh_out, void *stream);
+
+/* ---- The layer schedule: which rows each layer refreshes, decided on the device ---- */
+
+/* Rows each sequence refreshes at this step, chosen by feature similarity (dLLM-Cache record,
+ * abstract: partial response updates guided by feature similarity) on top of a window of live
+ * rows (Elastic-Cache card, core idea):
+ *   sim[b, j]    = <x, y> / (|x| |y|) for x = hidden_cur[b, j], y = hidden_cached[b, j], in fp64
+ *                  (both rows zero -> 1, exactly one zero -> 0), for the response rows j >= lo
+ *   idx_out[b]   = the window rows [window_start[b], window_start[b] + window) together with
+ *                  the k rows of [lo, S) outside the window of lowest sim (ties: lower row
+ *                  first), ascending
+ *   batch, max_seq  B and S; S <= 8192
+ *   hidden_size  H, a multiple of 8 (bf16) or 4 (fp32)
+ *   act_dtype    DLLM_BF16 or DLLM_F32: dtype of hidden_cur and hidden_cached
+ *   hidden_cur, hidden_cached  device, [B, S, H]: this step's input features and the features
+ *                the rows' cache entries were last computed from
+ *   lo           first response row, 0 <= lo < S
+ *   window_start device, [B] int32, each in [0, S - window]; may be NULL when window = 0
+ *   window, k    >= 0 with window + k <= S - lo
+ *   idx_out      device, [B, window + k] int32
+ *   sim_out      device, [B, S] fp64, or NULL (the workspace then holds it); rows below lo are
+ *                not written
+ *   workspace    ws_bytes >= dllm_similarity_select_workspace_bytes(B, S) when sim_out is
+ *                NULL, else unused
+ * Deterministic.  Errors: DLLM_EINVAL, DLLM_EUNSUPPORTED (S above 8192), DLLM_ESIZE,
+ * DLLM_ELAUNCH. */
+DLLM_API size_t dllm_similarity_select_workspace_bytes(int32_t batch, int32_t max_seq);
+DLLM_API dllm_status dllm_similarity_select(int32_t batch, int32_t max_seq, int32_t hidden_size,
+                                            int32_t act_dtype, const void *hidden_cur,
+                                            const void *hidden_cached, int32_t lo,
+                                            const int32_t *window_start, int32_t window, int32_t k,
+                                            int32_t *idx_out, double *sim_out, void *workspace,
+                                            size_t ws_bytes, void *stream);
+
+/* Rows one layer refreshes under the Elastic-Cache schedule (card, core idea: when the drift
+ * test fires at layer l, layers l + 1 .. L are recomputed; the tracked tokens are recomputed
+ * with the step rows so the test compares fresh rows):
+ *   full_out[b] = full_in[b] | decision[b] (either may be NULL: 0)
+ *   sequence b's rows: all S rows if full_out[b], else the union of idx[b, 0..n) and the
+ *   entries of tracked[b, 0..m) in [0, S) (-1 marks an empty slot), ascending; packed in
+ *   sequence order into rows_out with offsets cu_out [B + 1], ready for
+ *   dllm_refresh_qkv_rope_scatter_varlen and dllm_block_attention_varlen on the same stream
+ *   (capacity B * S, max_rows S).  Everything stays on the device.
+ *   idx          device, [B, n] int32 (entries outside [0, S) are skipped), n >= 0
+ *   tracked      device, [B, m] int32 or NULL (dllm_drift_check's track_idx, m = Hq * k)
+ *   full_in, decision, full_out  device, [B] uint8 (full_out may alias full_in; the drift
+ *                check's refresh_out is a decision)
+ *   rows_out     device, [capacity] int32, capacity >= B * S
+ *   cu_out       device, [B + 1] int32
+ *   workspace    ws_bytes >= dllm_schedule_rows_workspace_bytes(B, S); S <= 32768
+ * Errors: DLLM_EINVAL, DLLM_EUNSUPPORTED (S above 32768), DLLM_ESIZE, DLLM_ELAUNCH. */
+DLLM_API size_t dllm_schedule_rows_workspace_bytes(int32_t batch, int32_t max_seq);
+DLLM_API dllm_status dllm_schedule_rows(int32_t batch, int32_t max_seq, const int32_t *idx,
+                                        int32_t n, const int32_t *tracked, int32_t m,
+                                        const uint8_t *full_in, const uint8_t *decision,
+                                        uint8_t *full_out, int32_t *rows_out, int32_t capacity,
+                                        int32_t *cu_out, void *workspace, size_t ws_bytes,
+                                        void *stream);
+
+/* dst[b, rows[r]] = src[b, rows[r]] for the packed rows r < cu_rows[B] of a variable-length
+ * batch (read on the device): after a layer's refresh, the refreshed rows' cached features
+ * become the current ones.  src, dst: device [B, S, row_bytes / elem] arrays, row_bytes a
+ * positive multiple of 16; rows, cu_rows as in dllm_refresh_qkv_rope_scatter_varlen, capacity
+ * >= cu_rows[B]. */
+DLLM_API dllm_status dllm_copy_rows_varlen(int32_t batch, int32_t max_seq, int32_t row_bytes,
+                                           const void *src, void *dst, const int32_t *rows,
+                                           const int32_t *cu_rows, int32_t capacity,
+                                           void *stream);
+
+/* One layer of one denoising step under the Elastic-Cache schedule with the dLLM-Cache
+ * partial refresh, enqueued on `stream` with no host synchronisation (the decisions stay on
+ * the device).  In order:
+ *   1. step_rows = dllm_similarity_select(hidden_cur, hidden_feat, lo, window_start, window,
+ *      k_select)
+ *   2. full |= decision; rows / cu_rows = dllm_schedule_rows(step_rows, track_idx, full):
+ *      every row of a sequence flagged at an earlier layer, else its step rows with its
+ *      tracked rows
+ *   3. dllm_refresh_qkv_rope_scatter_varlen of those rows from hidden_cur into the cache; q
+ *   4. dllm_block_attention_varlen of q over each sequence's whole cache, with mass
+ *   5. dllm_drift_check (sigma, decision = this layer's drift test; tracking update)
+ *   6. dllm_copy_rows_varlen: the refreshed rows' features in hidden_feat become hidden_cur's
+ * Call it for layers 1 .. L in order with the same `full` and `decision` arrays, both zeroed
+ * before the first layer of a step.  Packed arrays have capacity B * S rows (rows past
+ * cu_rows[B] are not written).  bf16 activations and a bf16 cache; S <= 8192.
+ * Errors: as the six calls; a failing stage leaves the earlier ones enqueued. */
+typedef struct dllm_layer_step {
+  const void *hidden_cur;       /* [B, S, H] bf16: this step's input states of the layer */
+  void *hidden_feat;            /* [B, S, H] bf16, in/out: features the cache rows came from */
+  const void *w_qkv;            /* [(Hq + 2 Hkv) * D, H] bf16 */
+  const int32_t *window_start;  /* [B], each in [0, S - window] (NULL if window = 0) */
+  int32_t *track_idx;           /* [B, Hq, k_track], in/out (dllm_drift_check) */
+  void *track_buf;              /* [B, Hq, k_track, 2, D] bf16, in/out */
+  uint8_t *full;                /* [B], in/out: sequences that refresh every row */
+  uint8_t *decision;            /* [B], in: the previous layer's drift decision; out: this one's */
+  int32_t *step_rows;           /* [B, window + k_select] out */
+  int32_t *rows;                /* [B * S] out: packed refreshed rows */
+  int32_t *cu_rows;             /* [B + 1] out */
+  void *q;                      /* [B * S, Hq, D] bf16 out */
+  void *out;                    /* [B * S, Hq, D] bf16 out */
+  float *lse;                   /* [B * S * Hq] out, or NULL */
+  float *attn_mass;             /* [B, Hq, S] out */
+  float *sigma;                 /* [B, Hq] out */
+  int32_t hidden_size, num_q_heads, lo, window, k_select, k_track;
+  float rope_base, softmax_scale, gamma;
+} dllm_layer_step;
+DLLM_API size_t dllm_layer_step_workspace_bytes(const dllm_cache_desc *d, int32_t hidden_size,
+                                                int32_t num_q_heads);
+DLLM_API dllm_status dllm_elastic_layer_step(const dllm_cache *c, const dllm_layer_step *a,
+                                             void *workspace, size_t ws_bytes, void *stream);
 
 /* FP8 codec of the cache, exposed so the conversion can be checked element by element:
  * codes[i] = e4m3(x[i] / scale) (nearest even, saturating to +-448, NaN -> NaN) and

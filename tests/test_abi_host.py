@@ -158,3 +158,34 @@ def test_options_switch_round_trips():
         assert dkv.dllm_set_options(0) == dkv.DLLM_OPT_WIDE_OFFSETS
     finally:
         dkv.dllm_set_options(prev)
+
+
+def test_schedule_calls_reject_bad_arguments_on_host():
+    lib = dkv.lib
+    F = ctypes.c_void_p(1 << 40)                     # never dereferenced
+    EINVAL, ESIZE, EUNS = dkv.DLLM_EINVAL, dkv.DLLM_ESIZE, dkv.DLLM_EUNSUPPORTED
+    sel = lib.dllm_similarity_select
+    # B, S, H, act, cur, cached, lo, window_start, window, k, idx_out, sim_out, ws, ws_bytes, s
+    assert sel(2, 9000, 64, dkv.DLLM_BF16, F, F, 0, F, 4, 4, F, F, F, 1 << 30, None) == EUNS
+    assert sel(2, 100, 60, dkv.DLLM_BF16, F, F, 0, F, 4, 4, F, F, F, 1 << 30, None) == EINVAL
+    assert sel(2, 100, 64, dkv.DLLM_BF16, F, F, 50, F, 20, 31, F, F, F, 1 << 30, None) == EINVAL
+    assert sel(2, 100, 64, dkv.DLLM_BF16, F, F, 100, F, 0, 0, F, F, F, 1 << 30, None) == EINVAL
+    assert sel(2, 100, 64, dkv.DLLM_BF16, F, F, 0, None, 4, 4, F, F, F, 1 << 30, None) == EINVAL
+    assert sel(2, 100, 64, dkv.DLLM_BF16, F, F, 0, F, 4, 4, F, None, F, 100, None) == ESIZE
+    assert sel(2, 100, 64, dkv.DLLM_BF16, F, F, 0, F, 0, 0, F, None, None, 0, None) == dkv.DLLM_OK
+    assert lib.dllm_similarity_select_workspace_bytes(2, 100) == 2 * 100 * 8
+    sch = lib.dllm_schedule_rows
+    need = lib.dllm_schedule_rows_workspace_bytes(3, 50)
+    assert need >= 3 * 50 * 4 + 3 * 4
+    # B, S, idx, n, tracked, m, full_in, decision, full_out, rows, cap, cu, ws, ws_bytes, s
+    assert sch(3, 50, F, 4, F, 8, F, F, F, F, 149, F, F, need, None) == ESIZE
+    assert sch(3, 50, F, 4, F, 8, F, F, F, F, 150, F, F, need - 1, None) == ESIZE
+    assert sch(3, 50, None, 4, F, 8, F, F, F, F, 150, F, F, need, None) == EINVAL
+    assert sch(3, 50, F, 4, None, 8, F, F, F, F, 150, F, F, need, None) == EINVAL
+    assert sch(3, 40000, F, 4, F, 8, F, F, F, F, 3 * 40000, F, F, 1 << 30, None) == EUNS
+    assert sch(3, 50, F, 4, F, 8, F, F, F, F, 150, F, ctypes.c_void_p((1 << 40) + 8), need,
+               None) == EINVAL                       # workspace not 256-byte aligned
+    cp = lib.dllm_copy_rows_varlen
+    assert cp(2, 10, 24, F, F, F, F, 20, None) == EINVAL
+    assert cp(2, 10, 32, None, F, F, F, 20, None) == EINVAL
+    assert cp(2, 10, 32, F, F, F, F, 0, None) == dkv.DLLM_OK
