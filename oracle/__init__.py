@@ -507,3 +507,57 @@ def schedule_layer(st: LayerState, h_cur: np.ndarray, full, lo: int, window_star
     full_next = np.asarray(full, bool) | decision.astype(bool)
     return dict(R=R, sim=sim, rows=rows, cu=cu, q=q, out=out, lse=lse, mass=mass, sigma=sigma,
                 decision=decision, T_prev=T_prev, full_next=full_next)
+
+
+# ------------------------------------------------------------------------------------------
+# Per-group FP8 linear layer (LaCache Technical Summary, Methodology 2)
+# ------------------------------------------------------------------------------------------
+
+FP8_GROUP = 128
+
+
+def _e4m3_of_fp32_quotient(x32: np.ndarray, scale32: np.ndarray) -> np.ndarray:
+    """Codes e4m3(fp32(x / scale)): the quotient rounded to fp32 first (IEEE division), the
+    precision the kernel forms it in, since it decides the code."""
+    q = (x32 / scale32).astype(np.float32)
+    return e4m3_encode(q.astype(np.float64))
+
+
+def fp8_quantize_groups(x: np.ndarray):
+    """O15: activations [M, K] -> (codes uint8 [M, K], scales fp32 [M, K / 128]): one scale
+    per 1 x 128 group (LaCache Methodology 2, granularity): scale = fp32(amax) / 448 in fp32
+    (a zero group: 1), code = e4m3(x / scale)."""
+    x32 = _c(x, np.float32)
+    M, K = x32.shape
+    assert K % FP8_GROUP == 0
+    g = x32.reshape(M, K // FP8_GROUP, FP8_GROUP)
+    amax = np.abs(g).max(axis=-1)
+    scale = np.where(amax == 0, np.float32(1.0), amax / np.float32(448.0)).astype(np.float32)
+    codes = _e4m3_of_fp32_quotient(g, scale[..., None]).reshape(M, K)
+    return codes, scale
+
+
+def fp8_quantize_blocks(w: np.ndarray):
+    """O16: weights [N, K] -> (codes uint8 [N, K], scales fp32 [N / 128, K / 128]): one scale
+    per 128 x 128 block (LaCache Methodology 2, granularity), same rule as O15 over the
+    block."""
+    w32 = _c(w, np.float32)
+    N, K = w32.shape
+    assert N % FP8_GROUP == 0 and K % FP8_GROUP == 0
+    blk = w32.reshape(N // FP8_GROUP, FP8_GROUP, K // FP8_GROUP, FP8_GROUP)
+    amax = np.abs(blk).max(axis=(1, 3))
+    scale = np.where(amax == 0, np.float32(1.0), amax / np.float32(448.0)).astype(np.float32)
+    codes = _e4m3_of_fp32_quotient(blk, scale[:, None, :, None]).reshape(N, K)
+    return codes, scale
+
+
+def fp8_linear(x_codes, x_scales, w_codes, w_scales) -> np.ndarray:
+    """O17: y = dequant(x) dequant(w)^T in fp64, with dequant(x)[m, k] =
+    decode(x_codes[m, k]) * x_scales[m, k / 128] and dequant(w)[n, k] =
+    decode(w_codes[n, k]) * w_scales[n / 128, k / 128]: the linear layer the per-group FP8
+    GEMM computes (LaCache Methodology 2).  [M, K] x [N, K] -> [M, N]."""
+    xd = e4m3_decode(x_codes) * np.repeat(np.asarray(x_scales, np.float64), FP8_GROUP, axis=1)
+    ws = np.repeat(np.repeat(np.asarray(w_scales, np.float64), FP8_GROUP, axis=0), FP8_GROUP,
+                   axis=1)
+    wd = e4m3_decode(w_codes) * ws
+    return xd @ wd.T

@@ -662,3 +662,72 @@ def test_layer_schedule_threshold_extremes():
                                      st.window_start, 4, 6, gamma)
         sizes = np.diff(rec1["cu"])
         assert (sizes == wl.seq).all() == bool(expect)
+
+
+# ---------------------------------------------------------------- per-group FP8 linear --
+
+def test_fp8_group_codes_are_torch_casts_of_the_fp32_quotient():
+    """Each code is the nearest-even e4m3 of the fp32 quotient x / scale (torch's
+    float8_e4m3fn cast as the independent encoder); the group's largest magnitude maps to 448
+    and a zero group keeps scale 1 with zero codes."""
+    r = rng(60)
+    x = synth.round_to_bf16(r.standard_normal((5, 512)).astype(np.float32) *
+                            np.float32(3.0))
+    x[2, 128:256] = 0.0
+    codes, scales = oracle.fp8_quantize_groups(x)
+    assert scales.shape == (5, 4) and scales.dtype == np.float32
+    g = x.reshape(5, 4, 128)
+    amax = np.abs(g).max(-1)
+    np.testing.assert_array_equal(scales[amax > 0], (amax / np.float32(448))[amax > 0])
+    assert scales[2, 1] == 1.0 and not codes[2, 128:256].any()
+    q = torch.from_numpy(g / scales[..., None]).clamp(-448, 448)
+    ref = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(5, 512)
+    np.testing.assert_array_equal(codes, ref)
+    dec = oracle.e4m3_decode(codes).reshape(5, 4, 128)
+    big = np.abs(g).argmax(-1)
+    for m in range(5):
+        for kb in range(4):
+            if amax[m, kb] > 0:
+                assert abs(dec[m, kb, big[m, kb]]) == 448.0
+
+
+def test_fp8_block_scales_sit_on_their_128x128_block():
+    """A single large weight raises the scale of its own 128 x 128 block only (rows = output
+    features, columns = input features; a transposed or mis-strided block map fails)."""
+    r = rng(61)
+    w = r.standard_normal((256, 384)).astype(np.float32) * np.float32(0.02)
+    base_codes, base = oracle.fp8_quantize_blocks(w)
+    w2 = w.copy()
+    w2[130, 300] = 5.0                                  # block (1, 2)
+    codes2, s2 = oracle.fp8_quantize_blocks(w2)
+    changed = s2 != base
+    assert changed.sum() == 1 and changed[1, 2]
+    assert s2[1, 2] == np.float32(5.0) / np.float32(448)
+    assert oracle.e4m3_decode(codes2[130:131, 300:301])[0, 0] == 448.0
+    np.testing.assert_array_equal(codes2[:128], base_codes[:128])
+    np.testing.assert_array_equal(codes2[128:, :256], base_codes[128:, :256])
+
+
+def test_fp8_linear_is_an_integer_matmul_with_group_and_block_scales():
+    """Codes of small integers with unit scales make the layer an exact integer matmul
+    (numpy int64); doubling one activation group's scale adds exactly that group's share, and
+    doubling one weight block's scale that block's share (scale placement, no transposition)."""
+    r = rng(62)
+    M, N, K = 3, 256, 384
+    xi = r.integers(-8, 9, size=(M, K))
+    wi = r.integers(-8, 9, size=(N, K))
+    xc = oracle.e4m3_encode(xi.astype(np.float64))
+    wc = oracle.e4m3_encode(wi.astype(np.float64))
+    sx = np.ones((M, K // 128), np.float32)
+    sw = np.ones((N // 128, K // 128), np.float32)
+    y = oracle.fp8_linear(xc, sx, wc, sw)
+    np.testing.assert_array_equal(y, (xi @ wi.T).astype(np.float64))
+    sx2 = sx.copy(); sx2[1, 2] = 2.0
+    part = xi[1, 256:384] @ wi[:, 256:384].T
+    d = oracle.fp8_linear(xc, sx2, wc, sw) - y
+    np.testing.assert_array_equal(d[1], part)
+    assert not d[[0, 2]].any()
+    sw2 = sw.copy(); sw2[1, 0] = 2.0
+    d2 = oracle.fp8_linear(xc, sx, wc, sw2) - y
+    np.testing.assert_array_equal(d2[:, 128:256], xi[:, :128] @ wi[128:256, :128].T)
+    assert not d2[:, :128].any()
