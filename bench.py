@@ -362,6 +362,143 @@ def measure_facache(args, wl):
             "reuse_speedup_vs_plain": round(us["plain_all_rows"] / us["reuse"], 3)}
 
 
+def measure_schedule(args):
+    """One denoising step over L synthetic layers of the GQA workload's shape under the
+    Elastic-Cache layer schedule with the similarity-chosen partial refresh: per layer, one
+    call (similarity choice -> row schedule -> variable-length refresh -> attention with mass
+    -> drift test -> feature copy), every decision on the device.  Each sequence's states move
+    from a planted layer on, so the drift fires there and the later layers of that sequence
+    refresh every row.  Beside it, the same layers with every row recomputed (refresh and
+    attention of all S rows), the step that caching replaces."""
+    import torch
+
+    import diffusion_kv_cache_amd as dkv
+
+    dev = torch.device("cuda:0")
+    base = synth.WORKLOADS["c4"]
+    L = args.schedule_layers
+    wl = dataclasses.replace(base, name="schedule", seed=2001)
+    triggers = [1, L, 2, L, 3, L, L, 1][:wl.batch]
+    B, S, H, Hq, Hkv, D = wl.batch, wl.seq, wl.hidden, wl.q_heads, wl.kv_heads, wl.head_dim
+    window, k_sel, k_track = wl.window, wl.subset, wl.track_k
+    log(f"[bench] schedule: {L} layers of the {base.name} shape, triggers {triggers}")
+    t0 = time.time()
+    st = synth.layer_stack(wl, L, triggers, window)
+    log(f"[bench] schedule inputs generated in {time.time() - t0:.1f}s")
+    bf = torch.bfloat16
+    cap = B * S
+    scale = 1.0 / math.sqrt(D)
+    all_rows = torch.arange(S, dtype=torch.int32, device=dev).repeat(B, 1)
+    rows0 = torch.from_numpy(np.stack([np.arange(w0, w0 + window) for w0 in st.window_start])
+                             .astype(np.int32)).to(dev)
+    ws_d = torch.from_numpy(st.window_start).to(dev)
+    q_all = torch.empty((B, S, Hq, D), dtype=bf, device=dev)
+    out_all = torch.empty_like(q_all)
+    lse_all = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    layers = []
+    for l in range(L):
+        ly = {"cache": dkv.Cache(B, Hkv, S, D, dkv.DLLM_BF16),
+              "w": torch.from_numpy(st.w[l]).to(dev).to(bf),
+              "hcur": torch.from_numpy(st.hidden_cur[l]).to(dev).to(bf)}
+        hp = torch.from_numpy(st.hidden_prev[l]).to(dev).to(bf)
+        dkv.dllm_refresh_qkv_rope_scatter(ly["cache"], hp, all_rows, ly["w"], Hq, wl.rope_base,
+                                          q_all)
+        q0 = torch.empty((B, window, Hq, D), dtype=bf, device=dev)
+        dkv.dllm_refresh_qkv_rope_scatter(ly["cache"], hp, rows0, ly["w"], Hq, wl.rope_base, q0)
+        mass0 = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+        dkv.dllm_block_attention(ly["cache"], q0, Hq, scale, torch.empty_like(q0),
+                                 torch.empty((B, Hq, window), dtype=torch.float32, device=dev),
+                                 mass0)
+        ly["T"] = torch.full((B, Hq, k_track), -1, dtype=torch.int32, device=dev)
+        ly["buf"] = torch.zeros((B, Hq, k_track, 2, D), dtype=bf, device=dev)
+        dkv.dllm_drift_check(ly["cache"], Hq, k_track, wl.gamma, ly["T"], ly["buf"], mass0,
+                             torch.empty((B, Hq), dtype=torch.float32, device=dev),
+                             torch.empty((B,), dtype=torch.uint8, device=dev))
+        ly["feat"] = hp
+        ly["snap"] = {k_: v.clone() for k_, v in (("k", ly["cache"].k), ("v", ly["cache"].v),
+                                                   ("T", ly["T"]), ("buf", ly["buf"]),
+                                                   ("feat", ly["feat"]))}
+        layers.append(ly)
+    torch.cuda.synchronize()
+    full = torch.zeros((B,), dtype=torch.uint8, device=dev)
+    decision = torch.zeros((B,), dtype=torch.uint8, device=dev)
+    o = dict(step_rows=torch.empty((B, window + k_sel), dtype=torch.int32, device=dev),
+             rows=torch.empty((cap,), dtype=torch.int32, device=dev),
+             q=torch.empty((cap, Hq, D), dtype=bf, device=dev),
+             out=torch.empty((cap, Hq, D), dtype=bf, device=dev),
+             lse=None, attn_mass=torch.empty((B, Hq, S), dtype=torch.float32, device=dev),
+             sigma=torch.empty((B, Hq), dtype=torch.float32, device=dev))
+    ws = torch.empty(dkv.dllm_layer_step_workspace_bytes(layers[0]["cache"], H, Hq),
+                     dtype=torch.uint8, device=dev)
+    cus = torch.empty((L, B + 1), dtype=torch.int32, device=dev)
+
+    def restore():
+        for ly in layers:
+            ly["cache"].k.copy_(ly["snap"]["k"])
+            ly["cache"].v.copy_(ly["snap"]["v"])
+            ly["T"].copy_(ly["snap"]["T"])
+            ly["buf"].copy_(ly["snap"]["buf"])
+            ly["feat"].copy_(ly["snap"]["feat"])
+        full.zero_()
+        decision.zero_()
+
+    def step():
+        for l, ly in enumerate(layers):
+            dkv.dllm_elastic_layer_step(
+                ly["cache"], hidden_cur=ly["hcur"], hidden_feat=ly["feat"], w_qkv=ly["w"],
+                window_start=ws_d, track_idx=ly["T"], track_buf=ly["buf"], full=full,
+                decision=decision, num_q_heads=Hq, lo=wl.prompt, window=window,
+                k_select=k_sel, k_track=k_track, rope_base=wl.rope_base, softmax_scale=scale,
+                gamma=wl.gamma, workspace=ws, cu_rows=cus[l], **o)
+
+    def full_recompute():
+        for ly in layers:
+            dkv.dllm_refresh_qkv_rope_scatter(ly["cache"], ly["hcur"], all_rows, ly["w"], Hq,
+                                              wl.rope_base, q_all)
+            dkv.dllm_block_attention(ly["cache"], q_all, Hq, scale, out_all, lse_all, None)
+
+    reps = max(3, min(args.steps, 10))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for r in range(reps + 1):
+        restore()
+        torch.cuda.synchronize()
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        if r:
+            times.append(e0.elapsed_time(e1) * 1e3)
+    rows_per_layer = [int(x) for x in cus[:, -1].cpu().tolist()]
+    full_flags = full.cpu().tolist()
+    us = float(np.median(times))
+    full_recompute()
+    torch.cuda.synchronize()
+    ftimes = []
+    for _ in range(reps):
+        e0.record()
+        full_recompute()
+        e1.record()
+        torch.cuda.synchronize()
+        ftimes.append(e0.elapsed_time(e1) * 1e3)
+    fus = float(np.median(ftimes))
+    restore()
+    log(f"[bench] schedule: {us:.1f} us/step over {L} layers, rows per layer {rows_per_layer}; "
+        f"every row recomputed: {fus:.1f} us")
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": f"{L} synthetic layers of the {base.name} shape ({base.description}); "
+                        f"per step window {window} + {k_sel} least-similar response rows + "
+                        f"tracked rows, every row after a drift; states move from layers "
+                        f"{triggers}",
+            "layers": L, "us_per_step": round(us, 1), "refreshed_rows_per_layer": rows_per_layer,
+            "refreshed_tokens_per_s": round(sum(rows_per_layer) / (us * 1e-6), 1),
+            "full_after_step": full_flags,
+            "every_row_recomputed_us": round(fus, 1),
+            "speedup_vs_every_row": round(fus / us, 3), "repeats": reps}
+
+
 def run(args):
     import torch
 
@@ -395,6 +532,8 @@ def run(args):
         result["configs"] = others
     if not args.no_facache and wl.cache == "bf16":
         result["facache"] = measure_facache(args, wl)
+    if args.schedule_layers > 0:
+        result["layer_schedule"] = measure_schedule(args)
     if args.copy_calibration:
         # A plain device copy of known size, so HBM byte counters read under a profiler can be
         # scaled by what they report for a copy (reads = writes = the buffer size).
@@ -484,6 +623,8 @@ def main():
     ap.add_argument("--no-facache", action="store_true",
                     help="skip the FACache measurement (every row's attention with cached "
                          "statistics of the invariant rows)")
+    ap.add_argument("--schedule-layers", type=int, default=4,
+                    help="layers of the Elastic-Cache schedule section (0: skip it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
