@@ -30,7 +30,9 @@ EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatte
            "dllm_attention_varlen_workspace_bytes", "dllm_block_attention_varlen",
            "dllm_similarity_select_workspace_bytes", "dllm_similarity_select",
            "dllm_schedule_rows_workspace_bytes", "dllm_schedule_rows", "dllm_copy_rows_varlen",
-           "dllm_layer_step_workspace_bytes", "dllm_elastic_layer_step", "dllm_last_error")
+           "dllm_layer_step_workspace_bytes", "dllm_elastic_layer_step",
+           "dllm_fp8_quantize_weight", "dllm_fp8_quantize_activations",
+           "dllm_fp8_linear_workspace_bytes", "dllm_fp8_linear", "dllm_last_error")
 DLLM_OPT_DEBUG, DLLM_OPT_WIDE_OFFSETS = 1, 2
 DLLM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -120,6 +122,14 @@ def _load():
     lib.dllm_elastic_layer_step.restype = i32
     lib.dllm_elastic_layer_step.argtypes = [ctypes.POINTER(CCache), ctypes.POINTER(LayerStep), P,
                                             ctypes.c_size_t, P]
+    lib.dllm_fp8_quantize_weight.restype = i32
+    lib.dllm_fp8_quantize_weight.argtypes = [P, i32, i32, P, P, P]
+    lib.dllm_fp8_quantize_activations.restype = i32
+    lib.dllm_fp8_quantize_activations.argtypes = [P, i32, i32, P, P, i32, P]
+    lib.dllm_fp8_linear_workspace_bytes.restype = ctypes.c_size_t
+    lib.dllm_fp8_linear_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.dllm_fp8_linear.restype = i32
+    lib.dllm_fp8_linear.argtypes = [P, i32, i32, P, P, i32, P, P, ctypes.c_size_t, P]
     lib.dllm_drift_check.restype = i32
     lib.dllm_drift_check.argtypes = [ctypes.POINTER(CCache), i32, i32, ctypes.c_float, P, P, P, P,
                                      P, P]
@@ -539,6 +549,49 @@ def dllm_elastic_layer_step(cache: Cache, *, hidden_cur, hidden_feat, w_qkv, win
     a.rope_base, a.softmax_scale, a.gamma = rope_base, softmax_scale, gamma
     _check(lib.dllm_elastic_layer_step(ctypes.byref(cache.c), ctypes.byref(a), _ptr(workspace),
                                        workspace.numel(), _stream(stream)))
+
+
+def dllm_fp8_quantize_weight(w: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                             stream=None):
+    """w [N, K] bf16 -> codes [N, K] uint8, scales [N / 128, K / 128] fp32."""
+    N, K = w.shape
+    _expect(w, "w", (N, K), torch.bfloat16)
+    _expect(codes, "codes", (N, K), torch.uint8)
+    _expect(scales, "scales", (N // 128, K // 128), torch.float32)
+    _check(lib.dllm_fp8_quantize_weight(_ptr(w), N, K, _ptr(codes), _ptr(scales),
+                                        _stream(stream)))
+
+
+def dllm_fp8_quantize_activations(x: torch.Tensor, codes: torch.Tensor, scales_t: torch.Tensor,
+                                  stream=None):
+    """x [M, K] bf16 -> codes [M, K] uint8, scales_t [K / 128, pitch] fp32 (pitch >= M)."""
+    M, K = x.shape
+    _expect(x, "x", (M, K), torch.bfloat16)
+    _expect(codes, "codes", (M, K), torch.uint8)
+    pitch = scales_t.shape[-1]
+    _expect(scales_t, "scales_t", (K // 128, pitch), torch.float32)
+    _check(lib.dllm_fp8_quantize_activations(_ptr(x), M, K, _ptr(codes), _ptr(scales_t), pitch,
+                                             _stream(stream)))
+
+
+def dllm_fp8_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib.dllm_fp8_linear_workspace_bytes(M, N, K)
+
+
+def dllm_fp8_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+                    y: torch.Tensor, workspace=None, stream=None):
+    """x [M, K] bf16, w_codes [N, K] uint8, w_scales [N / 128, K / 128] fp32, y [M, N] bf16."""
+    M, K = x.shape
+    N = w_codes.shape[0]
+    _expect(x, "x", (M, K), torch.bfloat16)
+    _expect(w_codes, "w_codes", (N, K), torch.uint8)
+    _expect(w_scales, "w_scales", (N // 128, K // 128), torch.float32)
+    _expect(y, "y", (M, N), torch.bfloat16)
+    if workspace is None:
+        need = dllm_fp8_linear_workspace_bytes(M, N, K)
+        workspace = _scratch(max(1, need), x.device, stream)
+    _check(lib.dllm_fp8_linear(_ptr(x), M, K, _ptr(w_codes), _ptr(w_scales), N, _ptr(y),
+                               _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def dllm_fp8_e4m3_roundtrip(x: torch.Tensor, scale: float, codes: torch.Tensor,

@@ -789,6 +789,91 @@ dllm_status dllm_elastic_layer_step(const dllm_cache* c, const dllm_layer_step* 
                                a->cu_rows, cap, stream);
 }
 
+dllm_status dllm_fp8_quantize_weight(const void* w, int32_t N, int32_t K, uint8_t* codes,
+                                     float* scales, void* stream) {
+  if (N <= 0 || K <= 0 || N % 128 || K % 128)
+    return fail(DLLM_EINVAL, "N=%d, K=%d: positive multiples of 128", N, K);
+  if (!w || !codes || !scales) return fail(DLLM_EINVAL, "null pointer argument");
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales))
+    return fail(DLLM_EINVAL, "w, codes and scales must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dllm::launch_fp8_quant_blocks(w, N, K, codes, scales, s), s, "fp8 weight quantisation");
+}
+
+dllm_status dllm_fp8_quantize_activations(const void* x, int32_t M, int32_t K, uint8_t* codes,
+                                          float* scales_t, int32_t pitch, void* stream) {
+  if (M < 0 || K <= 0 || K % 128) return fail(DLLM_EINVAL, "M=%d, K=%d: M >= 0, K a positive multiple of 128", M, K);
+  if (pitch < M) return fail(DLLM_EINVAL, "pitch %d below M %d", pitch, M);
+  if (pitch == 0) {
+    g_err[0] = '\0';
+    return DLLM_OK;
+  }
+  if ((M > 0 && (!x || !codes)) || !scales_t) return fail(DLLM_EINVAL, "null pointer argument");
+  if ((M > 0 && (!aligned16(x) || !aligned16(codes))) || ((uintptr_t)scales_t & 3u))
+    return fail(DLLM_EINVAL, "x and codes must be 16-byte aligned, scales_t 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dllm::launch_fp8_quant_groups(x, M, K, pitch, codes, scales_t, s), s,
+                "fp8 activation quantisation");
+}
+
+namespace {
+struct Fp8Ws {
+  size_t codes, scales, part, total;
+};
+Fp8Ws fp8_ws(const dllm::Fp8Plan& p) {
+  Fp8Ws w{};
+  w.codes = round_up(p.codes_bytes, 256);
+  w.scales = round_up(p.scales_bytes, 256);
+  w.part = round_up(p.part_bytes, 256);
+  w.total = w.codes + w.scales + w.part + 256;
+  return w;
+}
+bool fp8_shape_ok(int32_t M, int32_t N, int32_t K) {
+  return M >= 0 && N > 0 && K > 0 && N % 128 == 0 && K % 128 == 0 &&
+         (long long)M * K < (1LL << 32) && (long long)N * K < (1LL << 32);
+}
+}  // namespace
+
+size_t dllm_fp8_linear_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (!fp8_shape_ok(M, N, K) || M == 0) return 0;
+  return fp8_ws(dllm::plan_fp8_linear(M, N, K)).total;
+}
+
+dllm_status dllm_fp8_linear(const void* x, int32_t M, int32_t K, const uint8_t* w_codes,
+                            const float* w_scales, int32_t N, void* y, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  if (!fp8_shape_ok(M, N, K))
+    return fail(DLLM_EINVAL, "M=%d, N=%d, K=%d: N, K positive multiples of 128, M * K and N * K below 2^32", M, N, K);
+  if (M == 0) {
+    g_err[0] = '\0';
+    return DLLM_OK;
+  }
+  if (!x || !w_codes || !w_scales || !y) return fail(DLLM_EINVAL, "null pointer argument");
+  if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || ((uintptr_t)y & 7u))
+    return fail(DLLM_EINVAL, "x, w_codes, w_scales must be 16-byte aligned, y 8-byte aligned");
+  const dllm::Fp8Plan p = dllm::plan_fp8_linear(M, N, K);
+  const Fp8Ws w = fp8_ws(p);
+  if (ws_bytes < w.total) return fail(DLLM_ESIZE, "fp8 linear workspace needs %zu bytes, got %zu", w.total, ws_bytes);
+  if (!workspace) return fail(DLLM_EINVAL, "null workspace");
+  char* base = (char*)round_up((uintptr_t)workspace, 256);
+  dllm::Fp8GemmArgs a;
+  a.xq = (const uint8_t*)base;
+  a.sxT = (const float*)(base + w.codes);
+  a.wq = w_codes;
+  a.sw = w_scales;
+  a.y = y;
+  a.part = p.splits > 1 ? (float*)(base + w.codes + w.scales) : nullptr;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.Mp = p.Mp;
+  a.kb_per_split = p.kb_per_split;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dllm::launch_fp8_quant_groups(x, M, K, p.Mp, (uint8_t*)base, (float*)(base + w.codes), s);
+  if (e == hipSuccess) e = dllm::launch_fp8_gemm(a, p, s);
+  return finish(e, s, "fp8 linear");
+}
+
 dllm_status dllm_fp8_e4m3_roundtrip(const float* x, int64_t n, float scale, uint8_t* codes,
                                     float* decoded, void* stream) {
   if (n < 0) return fail(DLLM_EINVAL, "n < 0");

@@ -151,4 +151,28 @@ constexpr int kScheduleMaxSeq = 32768;
 hipError_t launch_copy_rows(const void* src, void* dst, int row_bytes, int B, int S,
                             const int32_t* rows, const int32_t* cu, int cap, hipStream_t s);
 
+// Per-group FP8 linear layer: y [M, N] bf16 = dequant(x) dequant(w)^T.
+struct Fp8GemmArgs {
+  const uint8_t* xq;     // [M, K] activation codes
+  const float* sxT;      // [K / 128, Mp] activation scales, group-major (rows >= M: 0)
+  const uint8_t* wq;     // [N, K] weight codes
+  const float* sw;       // [N / 128, K / 128] weight block scales
+  void* y;               // [M, N] bf16
+  float* part;           // [splits, M, N] fp32 split-K partials, or null (one split)
+  int M, N, K, Mp;
+  int kb_per_split;      // 128-groups of k per split
+};
+struct Fp8Plan {
+  bool small;            // M <= 64: 64 x 64 tiles, deep ring
+  int Mp;                // M rounded up to 256 (the scale array's row pitch)
+  int splits, kb_per_split;
+  size_t part_bytes, codes_bytes, scales_bytes;
+};
+Fp8Plan plan_fp8_linear(int M, int N, int K);
+hipError_t launch_fp8_quant_groups(const void* x, int M, int K, int Mp, uint8_t* q, float* sT,
+                                   hipStream_t s);
+hipError_t launch_fp8_quant_blocks(const void* w, int N, int K, uint8_t* q, float* sc,
+                                   hipStream_t s);
+hipError_t launch_fp8_gemm(const Fp8GemmArgs& a, const Fp8Plan& p, hipStream_t s);
+
 }  // namespace dllm

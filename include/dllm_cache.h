@@ -420,6 +420,41 @@ DLLM_API size_t dllm_layer_step_workspace_bytes(const dllm_cache_desc *d, int32_
 DLLM_API dllm_status dllm_elastic_layer_step(const dllm_cache *c, const dllm_layer_step *a,
                                              void *workspace, size_t ws_bytes, void *stream);
 
+/* ---- Per-group FP8 linear layer (LaCache Technical Summary, Methodology 2: FP8 for the
+ * FFN linear layers, one scale per 1 x 128 activation group and per 128 x 128 weight block) */
+
+/* Weights [N, K] bf16 (device) -> codes [N, K] uint8 (e4m3) and scales [N / 128, K / 128]
+ * fp32: per 128 x 128 block, scale = amax / 448 in fp32 (an all-zero block: 1) and code =
+ * e4m3(w / scale), the quotient formed in fp32 (nearest even, saturating).  N and K multiples
+ * of 128; all pointers 16-byte aligned.  Done once per weight matrix. */
+DLLM_API dllm_status dllm_fp8_quantize_weight(const void *w, int32_t N, int32_t K,
+                                              uint8_t *codes, float *scales, void *stream);
+
+/* Activations [M, K] bf16 -> codes [M, K] uint8 and scales_t [K / 128, pitch] fp32 (group-
+ * major: the scale of row m, group kb at scales_t[kb * pitch + m]; rows M .. pitch - 1 get 0),
+ * one scale per row and 128-column group, same rule as the weights.  pitch >= M; K a multiple
+ * of 128. */
+DLLM_API dllm_status dllm_fp8_quantize_activations(const void *x, int32_t M, int32_t K,
+                                                   uint8_t *codes, float *scales_t,
+                                                   int32_t pitch, void *stream);
+
+/* y [M, N] bf16 = dequant(x) dequant(w)^T: the activations x [M, K] bf16 are quantised in
+ * 1 x 128 groups (as dllm_fp8_quantize_activations, into the workspace), then multiplied
+ * with the FP8 weights on the FP8 matrix cores: for each 128-group kb the exact e4m3 product
+ * is summed in fp32 and scaled by x_scale[m, kb] * w_scale[n / 128, kb], groups added in
+ * ascending order in fp32 (for small M the groups are split into contiguous ranges whose fp32
+ * sums are added in range order), and the result rounded to bf16.
+ *   x            device, [M, K] bf16; M >= 0 (0 enqueues nothing), K a multiple of 128
+ *   w_codes, w_scales  from dllm_fp8_quantize_weight, N a multiple of 128
+ *   y            device, [M, N] bf16
+ *   workspace    ws_bytes >= dllm_fp8_linear_workspace_bytes(M, N, K)
+ * M * K and N * K below 2^32.  Deterministic.
+ * Errors: DLLM_EINVAL, DLLM_ESIZE, DLLM_ELAUNCH. */
+DLLM_API size_t dllm_fp8_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
+DLLM_API dllm_status dllm_fp8_linear(const void *x, int32_t M, int32_t K, const uint8_t *w_codes,
+                                     const float *w_scales, int32_t N, void *y, void *workspace,
+                                     size_t ws_bytes, void *stream);
+
 /* FP8 codec of the cache, exposed so the conversion can be checked element by element:
  * codes[i] = e4m3(x[i] / scale) (nearest even, saturating to +-448, NaN -> NaN) and
  * decoded[i] = decode(codes[i]) * scale.  x, codes, decoded: device arrays of n elements;
