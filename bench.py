@@ -33,8 +33,8 @@ import numpy as np  # noqa: E402
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
-RIDGE = {"bf16": 2500e12 / 8000e9, "f32": 157.3e12 / 8000e9}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}
+RIDGE = {"bf16": 2500e12 / 8000e9, "f32": 157.3e12 / 8000e9, "fp8": 5000e12 / 8000e9}
 MALL_BYTES = 256 << 20
 METRIC = "refreshed tokens/sec per layer step (QKV+RoPE+cache write+attn); % MFMA/HBM peak"
 
@@ -499,6 +499,58 @@ def measure_schedule(args):
             "speedup_vs_every_row": round(fus / us, 3), "repeats": reps}
 
 
+def measure_fp8_linear(args):
+    """The per-group FP8 linear layer (FFN Gate-Up and FF-Out, LaCache Methodology 2) on the
+    refreshed rows of the LLaDA-8B-shaped (hidden 4096, FFN 12288) and Dream-7B-shaped
+    (hidden 3584, FFN 18944) steps, beside torch's bf16 matmul of the same shape."""
+    import torch
+
+    import diffusion_kv_cache_amd as dkv
+
+    dev = torch.device("cuda:0")
+    shapes = [("c2 rows, LLaDA gate-up", 32, 2 * 12288, 4096),
+              ("c2 rows, LLaDA ff-out", 32, 4096, 12288),
+              ("c3 rows, LLaDA gate-up", 1024, 2 * 12288, 4096),
+              ("c3 rows, LLaDA ff-out", 1024, 4096, 12288),
+              ("c4 rows, Dream gate-up", 2304, 2 * 18944, 3584),
+              ("c4 rows, Dream ff-out", 2304, 3584, 18944)]
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    for name, M, N, K in shapes:
+        inst = max(2, math.ceil(3 * MALL_BYTES / (N * K)))
+        x = (torch.randn((M, K), generator=g, device=dev)).to(torch.bfloat16)
+        ws = []
+        for _ in range(inst):
+            w = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+            wc = torch.empty((N, K), dtype=torch.uint8, device=dev)
+            sc = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+            dkv.dllm_fp8_quantize_weight(w, wc, sc)
+            ws.append((wc, sc, w if inst * N * K * 2 < (8 << 30) else None))
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(dkv.dllm_fp8_linear_workspace_bytes(M, N, K), dtype=torch.uint8,
+                          device=dev)
+        fp8 = lambda t: dkv.dllm_fp8_linear(x, t[0], t[1], y, wsp)       # noqa: E731
+        bf16 = lambda t: torch.matmul(x, t[2].t(), out=y)               # noqa: E731
+        for _ in range(3):
+            fp8(ws[0])
+            bf16(ws[0])
+        torch.cuda.synchronize()
+        count = max(10, args.steps)
+        us8 = burst_us(torch, fp8, count, ws)
+        us16 = burst_us(torch, bf16, count, ws)
+        w8 = dict(bytes=M * K * 2 + N * K + (N // 128) * (K // 128) * 4 + M * N * 2,
+                  flops=2 * M * N * K)
+        out[name] = {"M": M, "N": N, "K": K, "fp8_us": round(us8, 2),
+                     "bf16_matmul_us": round(us16, 2), "speedup_vs_bf16": round(us16 / us8, 3),
+                     "roofline": roofline_entry("fp8_linear", w8, us8, "fp8")}
+        log(f"[bench] fp8 linear {name} (M={M} N={N} K={K}): {us8:.1f} us, bf16 matmul "
+            f"{us16:.1f} us; {out[name]['roofline']['achieved']} {out[name]['roofline']['unit']}")
+        del ws, x, y, wsp
+        torch.cuda.empty_cache()
+    return out
+
+
 def run(args):
     import torch
 
@@ -534,6 +586,8 @@ def run(args):
         result["facache"] = measure_facache(args, wl)
     if args.schedule_layers > 0:
         result["layer_schedule"] = measure_schedule(args)
+    if not args.no_fp8_linear:
+        result["fp8_linear"] = measure_fp8_linear(args)
     if args.copy_calibration:
         # A plain device copy of known size, so HBM byte counters read under a profiler can be
         # scaled by what they report for a copy (reads = writes = the buffer size).
@@ -625,6 +679,8 @@ def main():
                          "statistics of the invariant rows)")
     ap.add_argument("--schedule-layers", type=int, default=4,
                     help="layers of the Elastic-Cache schedule section (0: skip it)")
+    ap.add_argument("--no-fp8-linear", action="store_true",
+                    help="skip the per-group FP8 linear layer section")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",

@@ -31,7 +31,8 @@ FLAGS = [
 EXTRA = {"attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
          "attention_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
          "attention_facache.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-         "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+         "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "fp8_linear.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def build(verbose: bool = False) -> str:

@@ -829,7 +829,7 @@ Fp8Ws fp8_ws(const dllm::Fp8Plan& p) {
   return w;
 }
 bool fp8_shape_ok(int32_t M, int32_t N, int32_t K) {
-  return M >= 0 && N > 0 && K > 0 && N % 128 == 0 && K % 128 == 0 &&
+  return M >= 0 && N > 0 && K > 0 && N % 128 == 0 && K % 128 == 0 && K / 128 <= dllm::kFp8MaxGroups &&
          (long long)M * K < (1LL << 32) && (long long)N * K < (1LL << 32);
 }
 }  // namespace
@@ -843,7 +843,7 @@ dllm_status dllm_fp8_linear(const void* x, int32_t M, int32_t K, const uint8_t* 
                             const float* w_scales, int32_t N, void* y, void* workspace,
                             size_t ws_bytes, void* stream) {
   if (!fp8_shape_ok(M, N, K))
-    return fail(DLLM_EINVAL, "M=%d, N=%d, K=%d: N, K positive multiples of 128, M * K and N * K below 2^32", M, N, K);
+    return fail(DLLM_EINVAL, "M=%d, N=%d, K=%d: N, K positive multiples of 128, K <= 65536, M * K and N * K below 2^32", M, N, K);
   if (M == 0) {
     g_err[0] = '\0';
     return DLLM_OK;
@@ -868,6 +868,7 @@ dllm_status dllm_fp8_linear(const void* x, int32_t M, int32_t K, const uint8_t* 
   a.K = K;
   a.Mp = p.Mp;
   a.kb_per_split = p.kb_per_split;
+  a.splits = p.splits;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dllm::launch_fp8_quant_groups(x, M, K, p.Mp, (uint8_t*)base, (float*)(base + w.codes), s);
   if (e == hipSuccess) e = dllm::launch_fp8_gemm(a, p, s);

@@ -118,8 +118,7 @@ __global__ __launch_bounds__(256) void fp8_quant_blocks(const bf16_t* w, int N, 
 // GEMM: workgroup tile TM x TN, WM x WN waves of (TM / WM) x (TN / WN).  Each stage is one
 // 128-group of k: the A rows (codes), the B rows (codes) and the stage's row scales move
 // global -> LDS by DMA through an NST-stage ring; chunk j of a 128-byte row r sits at slot
-// j ^ (r % 8).  The grid is 1-D, column tiles fastest, so the workgroups on one XCD share the
-// A row tile and each weight column tile is fetched by one XCD.
+// j ^ (r % 8).
 // ------------------------------------------------------------------------------------------
 template <int TM, int TN, int WM, int WN, int NST>
 __global__ __launch_bounds__(64 * WM * WN) void fp8_gemm(Fp8GemmArgs a) {
@@ -133,15 +132,17 @@ __global__ __launch_bounds__(64 * WM * WN) void fp8_gemm(Fp8GemmArgs a) {
   constexpr int NI = (IA + IB) / NW;             // A / B blocks per wave and stage
   constexpr int PEND = NI + 1;                   // + the scale block (every wave issues it)
   __shared__ __attribute__((aligned(16))) char smem[NST * STAGE];
+  __shared__ float s_sw[kFp8MaxGroups];          // this column block's weight scales
 
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int l16 = lane & 15, lg = lane >> 4;
   const int wm = wave / WN, wn = wave % WN;
+  // All row tiles (and k ranges) of one column tile run on one XCD, back to back: the weight
+  // tile is fetched into that L2 once and the concurrent column tiles share the row tiles.
   const int nN = (a.N + TN - 1) / TN, nM = (a.M + TM - 1) / TM;
-  int id = blockIdx.x;
-  const int nt = id % nN;
-  id /= nN;
-  const int mt = id % nM, split = id / nM;
+  int nt, unit;
+  xcd_group_unit(blockIdx.x, nN, nM * a.splits, nt, unit);
+  const int mt = unit % nM, split = unit / nM;
   const int n0 = nt * TN, m0 = mt * TM;
   const int KB = a.K / kGroup;
   const int kb0 = split * a.kb_per_split;
@@ -181,7 +182,12 @@ __global__ __launch_bounds__(64 * WM * WN) void fp8_gemm(Fp8GemmArgs a) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) tot[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const float* swp = a.sw + (size_t)(n0 / kGroup) * KB;
+  // The weight scales of the block's groups go to LDS first (ordinary loads, complete before
+  // the ring starts), so the loop reads them without waiting on the memory counter that the
+  // ring's transfers also count.
+  const float* swp = a.sw + (size_t)(n0 / kGroup) * KB + kb0;
+  for (int i = t; i < stages; i += 64 * NW) s_sw[i] = swp[i];
+  __syncthreads();
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < stages) issue(kb0 + s, s);
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fp8_gemm(Fp8GemmArgs a) {
       const char* A = smem + u * STAGE;
       const char* Bt = A + A_BYTES;
       const float* Sx = (const float*)(Bt + B_BYTES);
-      const float swv = swp[kb0 + s];
+      const float swv = s_sw[s];
       i32x8 af[RT], bfr[CT];
       f32x4 sr[RT];
 #pragma unroll
@@ -217,14 +223,19 @@ __global__ __launch_bounds__(64 * WM * WN) void fp8_gemm(Fp8GemmArgs a) {
         bfr[ct] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
+      // Every product of the group first (independent MFMAs back to back, each into its own
+      // registers), then the scaled adds: no add waits on the MFMA issued just before it.
+      f32x4 p[RT][CT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const f32x4 p = mfma_fp8(af[rt], bfr[ct]);
+        for (int ct = 0; ct < CT; ++ct) p[rt][ct] = mfma_fp8(af[rt], bfr[ct]);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) tot[rt][ct][v] = fmaf(p[v], sr[rt][v], tot[rt][ct][v]);
-        }
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) tot[rt][ct][v] = fmaf(p[rt][ct][v], sr[rt][v], tot[rt][ct][v]);
     }
   }
 
@@ -269,8 +280,8 @@ hipError_t launch_cfg(const Fp8GemmArgs& a, int splits, hipStream_t s) {
 
 Fp8Plan plan_fp8_linear(int M, int N, int K) {
   Fp8Plan p{};
-  p.small = M <= 64;
-  const int TM = p.small ? 64 : 128, TN = p.small ? 64 : 128;
+  p.tile = M <= 64 ? 0 : M <= 256 ? 1 : 2;
+  const int TM = p.tile == 0 ? 64 : p.tile == 1 ? 128 : 256, TN = p.tile == 0 ? 64 : 128;
   p.Mp = (M + 255) / 256 * 256;
   const int KB = K / kGroup;
   const long long tiles = (long long)((N + TN - 1) / TN) * ((M + TM - 1) / TM);
@@ -298,8 +309,9 @@ hipError_t launch_fp8_quant_blocks(const void* w, int N, int K, uint8_t* q, floa
 }
 
 hipError_t launch_fp8_gemm(const Fp8GemmArgs& a, const Fp8Plan& p, hipStream_t s) {
-  hipError_t e = p.small ? launch_cfg<64, 64, 2, 2, 6>(a, p.splits, s)
-                         : launch_cfg<128, 128, 2, 2, 4>(a, p.splits, s);
+  hipError_t e = p.tile == 0 ? launch_cfg<64, 64, 2, 2, 6>(a, p.splits, s)
+                 : p.tile == 1 ? launch_cfg<128, 128, 2, 2, 4>(a, p.splits, s)
+                               : launch_cfg<256, 128, 4, 2, 3>(a, p.splits, s);
   if (e != hipSuccess || p.splits == 1) return e;
   const long long MN = (long long)a.M * a.N;
   fp8_splitk_reduce<<<(unsigned)((MN / 4 + 255) / 256), 256, 0, s>>>(a.part, p.splits, MN, (bf16_t*)a.y);

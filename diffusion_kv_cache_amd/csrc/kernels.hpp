@@ -161,14 +161,17 @@ struct Fp8GemmArgs {
   float* part;           // [splits, M, N] fp32 split-K partials, or null (one split)
   int M, N, K, Mp;
   int kb_per_split;      // 128-groups of k per split
+  int splits;
 };
 struct Fp8Plan {
-  bool small;            // M <= 64: 64 x 64 tiles, deep ring
+  int tile;              // 0: 64 x 64 tiles, deep ring (M <= 64); 1: 128 x 128; 2: 256 x 128
   int Mp;                // M rounded up to 256 (the scale array's row pitch)
   int splits, kb_per_split;
   size_t part_bytes, codes_bytes, scales_bytes;
 };
 Fp8Plan plan_fp8_linear(int M, int N, int K);
+// Largest K / 128 of the FP8 linear layer (its weight scales of one column block sit in LDS).
+constexpr int kFp8MaxGroups = 512;
 hipError_t launch_fp8_quant_groups(const void* x, int M, int K, int Mp, uint8_t* q, float* sT,
                                    hipStream_t s);
 hipError_t launch_fp8_quant_blocks(const void* w, int N, int K, uint8_t* q, float* sc,

@@ -448,7 +448,7 @@ DLLM_API dllm_status dllm_fp8_quantize_activations(const void *x, int32_t M, int
  *   w_codes, w_scales  from dllm_fp8_quantize_weight, N a multiple of 128
  *   y            device, [M, N] bf16
  *   workspace    ws_bytes >= dllm_fp8_linear_workspace_bytes(M, N, K)
- * M * K and N * K below 2^32.  Deterministic.
+ * K <= 65536; M * K and N * K below 2^32.  Deterministic.
  * Errors: DLLM_EINVAL, DLLM_ESIZE, DLLM_ELAUNCH. */
 DLLM_API size_t dllm_fp8_linear_workspace_bytes(int32_t M, int32_t N, int32_t K);
 DLLM_API dllm_status dllm_fp8_linear(const void *x, int32_t M, int32_t K, const uint8_t *w_codes,
