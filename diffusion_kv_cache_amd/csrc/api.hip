@@ -223,7 +223,7 @@ dllm_status refresh_call(const dllm_cache* c, const void* hidden, int32_t hidden
   const long long M = total;
   if (M > (1LL << 30)) return fail(DLLM_EINVAL, "too many rows");
   const int N = (num_q_heads + 2 * d.num_kv_heads) * d.head_dim;
-  const size_t need = dllm::refresh_workspace_bytes(act_dtype, d.kv_dtype, (int)M, N, hidden_size);
+  const size_t need = dllm::refresh_workspace_bytes(act_dtype, (int)M, N, hidden_size);
   if (ws_bytes < need) return fail(DLLM_ESIZE, "refresh workspace needs %zu bytes, got %zu", need, ws_bytes);
   if (need && (!workspace || !aligned16(workspace)))
     return fail(DLLM_EINVAL, "refresh workspace must be a 16-byte aligned device pointer");
@@ -355,7 +355,7 @@ size_t dllm_refresh_workspace_bytes(const dllm_cache_desc* d, int32_t hidden_siz
   const long long M = (long long)d->batch * n;
   if (M > (1LL << 30)) return 0;
   const int N = (num_q_heads + 2 * d->num_kv_heads) * d->head_dim;
-  return dllm::refresh_workspace_bytes(act_dtype, d->kv_dtype, (int)M, N, hidden_size);
+  return dllm::refresh_workspace_bytes(act_dtype, (int)M, N, hidden_size);
 }
 
 }  // extern "C"
@@ -732,7 +732,7 @@ StepWs step_ws(const dllm_cache_desc* d, int32_t H, int32_t Hq) {
   const int N = (Hq + 2 * d->num_kv_heads) * d->head_dim;
   w.sim = round_up(dllm_similarity_select_workspace_bytes(d->batch, d->max_seq), 256);
   w.sched = round_up(dllm_schedule_rows_workspace_bytes(d->batch, d->max_seq), 256);
-  w.refresh = round_up(dllm::refresh_workspace_bytes(DLLM_BF16, d->kv_dtype, (int)cap, N, H), 256);
+  w.refresh = round_up(dllm::refresh_workspace_bytes(DLLM_BF16, (int)cap, N, H), 256);
   w.attn = round_up(attention_ws_bytes(d, Hq, d->max_seq, cap), 256);
   w.total = w.sim + w.sched + w.refresh + w.attn + 256;
   return w;

@@ -36,15 +36,12 @@ constexpr int kSplitKMaxRows = 64;
 // Largest hidden size of the split-K path (its LDS slice is 32 x H/8 bf16).
 constexpr int kSplitKMaxHidden = 16384;
 bool refresh_uses_splitk(int act, int M, int H);
-// Workspace of a refresh: the split-K partials of a small step on an FP8 cache (a bf16
-// cache keeps them in LDS, refresh_wavesplit), else 0.
-size_t refresh_workspace_bytes(int act, int kind, int M, int N, int H);
+size_t refresh_workspace_bytes(int act, int M, int N, int H);
 size_t splitk_workspace_bytes(int M, int N);
 
 // Picks the path and tile shape for (M, N, dtypes) and launches the refresh.
 hipError_t launch_refresh(const RefreshArgs& a, hipStream_t s);
 hipError_t launch_refresh_splitk(const RefreshArgs& a, float* part, hipStream_t s);
-hipError_t launch_refresh_wavesplit(const RefreshArgs& a, hipStream_t s);
 
 struct AttnArgs {
   const void* q;         // [B, n, Hq, D] act dtype

@@ -534,13 +534,12 @@ bool refresh_uses_splitk(int act, int M, int H) {
   return act == DLLM_BF16 && M <= kSplitKMaxRows && H <= kSplitKMaxHidden;
 }
 
-size_t refresh_workspace_bytes(int act, int kind, int M, int N, int H) {
-  return (refresh_uses_splitk(act, M, H) && kind == kCacheFP8) ? splitk_workspace_bytes(M, N) : 0;
+size_t refresh_workspace_bytes(int act, int M, int N, int H) {
+  return refresh_uses_splitk(act, M, H) ? splitk_workspace_bytes(M, N) : 0;
 }
 
 hipError_t launch_refresh(const RefreshArgs& a, hipStream_t s) {
-  if (refresh_uses_splitk(a.act, a.M, a.H))
-    return a.kind == kCacheFP8 ? launch_refresh_splitk(a, a.ws, s) : launch_refresh_wavesplit(a, s);
+  if (refresh_uses_splitk(a.act, a.M, a.H)) return launch_refresh_splitk(a, a.ws, s);
   if (a.D == 128) return launch_d<128>(a, s);
   return launch_d<64>(a, s);
 }

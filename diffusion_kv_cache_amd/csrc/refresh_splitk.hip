@@ -203,136 +203,6 @@ __global__ __launch_bounds__(64) void refresh_reduce(RefreshArgs a, const float*
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// Small steps with a bf16 cache: the eight K-partitions inside one workgroup.  Workgroup
-// (32 rows) x (32 columns: rotary pairs i .. i + 15 of one head, both halves (i, i + D/2)),
-// eight waves; wave p streams partition p of its 32 W rows and its 32 gathered hidden rows
-// straight from memory through a register ring (the weights are read once; the hidden rows
-// stay in L2) and chains its MFMAs in ascending k -- the partition sum Pp.  The eight partial
-// tiles meet in LDS, where ((0 + P0) + P1) + ... + P7 is formed as in every other path, then
-// rotated and written as Q / K / V rows: no partials in HBM and no second launch.
-// ------------------------------------------------------------------------------------------
-constexpr int kRing = 4;                         // k-steps in flight per wave
-constexpr int kRedLd = 36;                       // floats per staged partial row (32 + 4)
-
-template <int D>
-__global__ __launch_bounds__(512) void refresh_wavesplit(RefreshArgs a) {
-  __shared__ float red[kKSplit][32 * kRedLd];
-  __shared__ int s_pos[32], s_hrow[32];
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
-  a.M = live_rows(a.cu, a.B, a.M);
-  const int heads = a.Hq + 2 * a.Hkv;
-  constexpr int TPH = D / 32;                    // column tiles per head
-  int ctile, rtile;
-  xcd_group_unit(blockIdx.x, heads * TPH, (a.M + 31) / 32, ctile, rtile);
-  const int m0 = rtile * 32;
-  if (m0 >= a.M) return;                         // uniform: rows present (variable-length)
-  const int j = ctile / TPH, pb = ctile % TPH;
-  const int col_lo = j * D + pb * 16;            // pairs pb*16 .. +15 of head j
-  if (t < 32) {
-    const int m = min(m0 + t, a.M - 1);
-    const int pos = a.idx[m];
-    s_pos[t] = pos;
-    s_hrow[t] = seq_of_row(a.cu, a.B, a.n, m) * a.S + pos;
-  }
-  __syncthreads();
-  // This thread's rotary pair in the epilogue; its frequency (fp64) is formed while the
-  // first transfers are in flight.
-  const int r_ep = t >> 4, c_ep = t & 15;
-  float t_hi = 0.f, t_lo = 0.f;
-  // This wave's K-partition, rotated by workgroup: the workgroups of an XCD read the shared
-  // hidden rows at eight different offsets at any moment instead of all at one.
-  const int p = (wave + (int)blockIdx.x) & (kKSplit - 1);
-  const int Lp = a.H / kKSplit, steps = Lp / 32;
-  const int kb = p * Lp + lg * 8;
-  const bf16_t* ar0 = (const bf16_t*)a.hidden + (size_t)s_hrow[l16] * a.H + kb;
-  const bf16_t* ar1 = (const bf16_t*)a.hidden + (size_t)s_hrow[16 + l16] * a.H + kb;
-  const bf16_t* wr0 = (const bf16_t*)a.w + (size_t)(col_lo + l16) * a.H + kb;
-  const bf16_t* wr1 = (const bf16_t*)a.w + (size_t)(col_lo + D / 2 + l16) * a.H + kb;
-  u32x4 ra[kRing][2], rw[kRing][2];
-#pragma unroll
-  for (int u = 0; u < kRing; ++u) {
-    const int st = min(u, steps - 1) * 32;
-    rw[u][0] = *(const u32x4*)(wr0 + st);
-    rw[u][1] = *(const u32x4*)(wr1 + st);
-    ra[u][0] = *(const u32x4*)(ar0 + st);
-    ra[u][1] = *(const u32x4*)(ar1 + st);
-  }
-  if (j < a.Hq + a.Hkv) rope_turns(pb * 16 + c_ep, D, a.rope_base, t_hi, t_lo);
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Slot u holds step s0 + u; after its MFMAs it is refilled with step s0 + u + kRing (the
-  // last round refills nothing: no branch around a load anywhere).
-  int s0 = 0;
-  for (; s0 + kRing < steps; s0 += kRing) {
-#pragma unroll
-    for (int u = 0; u < kRing; ++u) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          acc[rt][ct] = mfma_bf16(as_bf16x8(ra[u][rt]), as_bf16x8(rw[u][ct]), acc[rt][ct]);
-      const int st = min(s0 + u + kRing, steps - 1) * 32;
-      rw[u][0] = *(const u32x4*)(wr0 + st);
-      rw[u][1] = *(const u32x4*)(wr1 + st);
-      ra[u][0] = *(const u32x4*)(ar0 + st);
-      ra[u][1] = *(const u32x4*)(ar1 + st);
-      // the refill goes out right behind the slot's MFMAs (kept in program order), so
-      // kRing - 1 steps stay in flight at every point of the loop
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kRing; ++u)
-    if (s0 + u < steps)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          acc[rt][ct] = mfma_bf16(as_bf16x8(ra[u][rt]), as_bf16x8(rw[u][ct]), acc[rt][ct]);
-
-  // Partition p's 32 x 32 tile to LDS: row rt*16 + 4 lg + v, column ct*16 + l16.
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[p][(rt * 16 + lg * 4 + v) * kRedLd + ct * 16 + l16] = acc[rt][ct][v];
-  __syncthreads();
-
-  // One rotary pair (row r, pair c) per thread: ((0 + P0) + P1) + ... + P7 for both halves.
-  const int r = r_ep, c = c_ep;
-  float x = 0.f, y = 0.f;
-#pragma unroll
-  for (int q = 0; q < kKSplit; ++q) {
-    x = x + red[q][r * kRedLd + c];
-    y = y + red[q][r * kRedLd + 16 + c];
-  }
-  const int m = m0 + r;
-  if (m >= a.M) return;                          // no barrier follows
-  const int pos = s_pos[r];
-  const int i = pb * 16 + c;                     // pair index within the head
-  if (j < a.Hq + a.Hkv) {
-    float sn, cs;
-    rope_sincos(pos, t_hi, t_lo, sn, cs);
-    rope_rotate(x, y, sn, cs);
-  }
-  bf16_t* dst;
-  if (j < a.Hq) {
-    dst = (bf16_t*)a.q_out + ((size_t)m * a.Hq + j) * D;
-  } else {
-    const bool is_k = j < a.Hq + a.Hkv;
-    const int g = is_k ? j - a.Hq : j - a.Hq - a.Hkv;
-    const int b = seq_of_row(a.cu, a.B, a.n, m);
-    dst = (bf16_t*)(is_k ? a.kc : a.vc) + (((size_t)b * a.Hkv + g) * a.S + pos) * D;
-  }
-  dst[i] = f32_to_bf16(x);
-  dst[i + D / 2] = f32_to_bf16(y);
-}
-
 template <int D>
 hipError_t launch_reduce(const RefreshArgs& a, const float* part, hipStream_t s) {
   const long long items = (long long)a.M * (a.Hq + 2 * a.Hkv);
@@ -345,14 +215,6 @@ hipError_t launch_reduce(const RefreshArgs& a, const float* part, hipStream_t s)
 }  // namespace
 
 size_t splitk_workspace_bytes(int M, int N) { return (size_t)kKSplit * M * N * sizeof(float); }
-
-hipError_t launch_refresh_wavesplit(const RefreshArgs& a, hipStream_t s) {
-  const int heads = a.Hq + 2 * a.Hkv;
-  const unsigned grid = (unsigned)(heads * (a.D / 32) * ((a.M + 31) / 32));
-  if (a.D == 128) refresh_wavesplit<128><<<grid, 512, 0, s>>>(a);
-  else refresh_wavesplit<64><<<grid, 512, 0, s>>>(a);
-  return hipGetLastError();
-}
 
 hipError_t launch_refresh_splitk(const RefreshArgs& a, float* part, hipStream_t s) {
   const int N = (a.Hq + 2 * a.Hkv) * a.D;

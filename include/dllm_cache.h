@@ -119,10 +119,8 @@ DLLM_API dllm_status dllm_cache_alloc(const dllm_cache_desc *d, void *base, size
  *                and K head of row s is rotated by s * theta_i (rotate-half convention)
  *   q_out        device, [B, n, Hq, D] of act_dtype: rotated queries of the refreshed rows
  *   workspace    device scratch of ws_bytes >= dllm_refresh_workspace_bytes(...) (may be NULL
- *                when that is 0): small steps on an FP8 cache split the projection over K
- *                across workgroups and keep the eight partial sums here (on a bf16 cache the
- *                eight partitions of a tile run in one workgroup and meet in LDS); contents
- *                need no initialisation
+ *                when that is 0): small steps split the projection over K across workgroups
+ *                and keep the eight partial sums here; contents need no initialisation
  * Writes exactly the K/V rows (b, :, refresh_idx[b, i], :) (and their scales) and q_out;
  * every other cache row is left untouched.  Each output element is the fp32 sum of eight
  * fixed, equal K-partitions of H, each accumulated in ascending order and added in
@@ -168,8 +166,8 @@ DLLM_API dllm_status dllm_refresh_qkv_rope_scatter_varlen(const dllm_cache *c, c
                                                           void *stream);
 
 /* Workspace bytes the refresh call needs for n rows per sequence (0 when the step runs as a
- * single kernel; 8 * B * n * (Hq + 2 Hkv) * D * 4 for the split-K path of small bf16 steps
- * on an FP8 cache, B * n <= 64).  Returns 0 also for invalid arguments. */
+ * single fused kernel; 8 * B * n * (Hq + 2 Hkv) * D * 4 for the split-K path of small
+ * bf16 steps, B * n <= 64).  Returns 0 also for invalid arguments. */
 DLLM_API size_t dllm_refresh_workspace_bytes(const dllm_cache_desc *d, int32_t hidden_size,
                                              int32_t act_dtype, int32_t n,
                                              int32_t num_q_heads);

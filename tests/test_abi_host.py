@@ -104,19 +104,16 @@ def test_refresh_rejects_bad_arguments_on_host():
     assert _refresh(c, n=0) == dkv.DLLM_OK                         # nothing to do, no launch
     assert dkv.lib.dllm_refresh_qkv_rope_scatter(None, ADDR, 256, 1, ADDR, 4, ADDR, 4, 1e4, ADDR,
                                                  None, 0, None) == dkv.DLLM_EINVAL
-    # small bf16 steps on an FP8 cache split K over workgroups and need 8 fp32 partials per
-    # output; on a bf16 cache the partials stay in LDS
+    # small bf16 steps split K over workgroups and need 8 fp32 partials per output
     L = dkv.lib
-    c8 = _fake_cache(dt=dkv.DLLM_FP8_E4M3)
-    need = L.dllm_refresh_workspace_bytes(ctypes.byref(c8.desc), 256, dkv.DLLM_BF16, 4, 4)
+    need = L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_BF16, 4, 4)
     assert need == 8 * (2 * 4) * ((4 + 2 * 4) * 128) * 4
-    assert _refresh(c8, ws_bytes=need - 1) == dkv.DLLM_ESIZE
-    assert _refresh(c8, ws=None, ws_bytes=need) == dkv.DLLM_EINVAL
-    assert L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_BF16, 4, 4) == 0
+    assert _refresh(c, ws_bytes=need - 1) == dkv.DLLM_ESIZE
+    assert _refresh(c, ws=None, ws_bytes=need) == dkv.DLLM_EINVAL
     # large steps and fp32 run as one fused kernel: no workspace
-    assert L.dllm_refresh_workspace_bytes(ctypes.byref(c8.desc), 256, dkv.DLLM_BF16, 64, 4) == 0
+    assert L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_BF16, 64, 4) == 0
     assert L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_F32, 4, 4) == 0
-    assert L.dllm_refresh_workspace_bytes(ctypes.byref(c8.desc), 256, dkv.DLLM_BF16, 4, 5) == 0
+    assert L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_BF16, 4, 5) == 0
 
 
 def test_attention_and_drift_reject_bad_arguments_on_host():
