@@ -812,7 +812,7 @@ dllm_status dllm_fp8_quantize_activations(const void* x, int32_t M, int32_t K, u
   if ((M > 0 && (!aligned16(x) || !aligned16(codes))) || ((uintptr_t)scales_t & 3u))
     return fail(DLLM_EINVAL, "x and codes must be 16-byte aligned, scales_t 4-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  return finish(dllm::launch_fp8_quant_groups(x, M, K, pitch, codes, scales_t, s), s,
+  return finish(dllm::launch_fp8_quant_groups(x, M, K, pitch, codes, scales_t, true, s), s,
                 "fp8 activation quantisation");
 }
 
@@ -870,7 +870,7 @@ dllm_status dllm_fp8_linear(const void* x, int32_t M, int32_t K, const uint8_t* 
   a.kb_per_split = p.kb_per_split;
   a.splits = p.splits;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dllm::launch_fp8_quant_groups(x, M, K, p.Mp, (uint8_t*)base, (float*)(base + w.codes), s);
+  hipError_t e = dllm::launch_fp8_quant_groups(x, M, K, p.Mp, (uint8_t*)base, (float*)(base + w.codes), false, s);
   if (e == hipSuccess) e = dllm::launch_fp8_gemm(a, p, s);
   return finish(e, s, "fp8 linear");
 }

@@ -296,8 +296,10 @@ Fp8Plan plan_fp8_linear(int M, int N, int K) {
 }
 
 hipError_t launch_fp8_quant_groups(const void* x, int M, int K, int Mp, uint8_t* q, float* sT,
-                                   hipStream_t s) {
-  const long long groups = (long long)Mp * (K / kGroup);
+                                   bool zero_pad, hipStream_t s) {
+  // Without zero_pad the scales of rows M .. Mp - 1 are left as they are: the GEMM reads them
+  // only for rows it never stores.
+  const long long groups = (long long)(zero_pad ? Mp : M) * (K / kGroup);
   fp8_quant_groups<<<(unsigned)((groups + 15) / 16), 256, 0, s>>>((const bf16_t*)x, M, K, Mp, q, sT);
   return hipGetLastError();
 }

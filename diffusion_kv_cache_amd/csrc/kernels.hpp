@@ -173,7 +173,7 @@ Fp8Plan plan_fp8_linear(int M, int N, int K);
 // Largest K / 128 of the FP8 linear layer (its weight scales of one column block sit in LDS).
 constexpr int kFp8MaxGroups = 512;
 hipError_t launch_fp8_quant_groups(const void* x, int M, int K, int Mp, uint8_t* q, float* sT,
-                                   hipStream_t s);
+                                   bool zero_pad, hipStream_t s);
 hipError_t launch_fp8_quant_blocks(const void* w, int N, int K, uint8_t* q, float* sc,
                                    hipStream_t s);
 hipError_t launch_fp8_gemm(const Fp8GemmArgs& a, const Fp8Plan& p, hipStream_t s);
