@@ -551,6 +551,107 @@ def measure_fp8_linear(args):
     return out
 
 
+def measure_unfused_and_hbm_paths(args):
+    """The fused refresh beside its unfused form (gather + GEMM, then the rotary kernel, then
+    the row scatter: the four-kernel pipeline the fused call replaces, Flash-dLLM news summary,
+    memory paragraph) on the c2, c3 and c4 shapes; the row scatter's own HBM rate (c3); and the
+    drift check batched over 28 layers of the GQA shape in one launch (28 x 8 sequences)."""
+    import torch
+
+    import diffusion_kv_cache_amd as dkv
+
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    ab = {}
+    scatter = None
+    for name in ("c2", "c3", "c4"):
+        wl = synth.WORKLOADS[name]
+        inp = synth.make_inputs(wl)
+        B, n, S, H, Hq, Hkv, D = (wl.batch, wl.n_refresh, wl.seq, wl.hidden, wl.q_heads,
+                                  wl.kv_heads, wl.head_dim)
+        M, N = B * n, wl.n_cols
+        h = torch.from_numpy(inp.hidden_cur()).to(dev).to(bf)
+        idx = torch.from_numpy(inp.idx).to(dev)
+        bidx = torch.arange(B, device=dev)[:, None]
+        pos = idx.reshape(-1).contiguous()
+        L = max(3, math.ceil(3 * MALL_BYTES / (N * H * 2 + 2 * B * Hkv * S * D * 2)))
+        layers = []
+        for _ in range(L):
+            c = dkv.Cache(B, Hkv, S, D, dkv.DLLM_BF16)
+            w = torch.from_numpy(inp.w).to(dev).to(bf)
+            layers.append((c, w))
+        q = torch.empty((B, n, Hq, D), dtype=bf, device=dev)
+        rws_bytes = dkv.dllm_refresh_workspace_bytes(layers[0][0], H, dkv.DLLM_BF16, n, Hq)
+        rws = torch.empty(rws_bytes, dtype=torch.uint8, device=dev) if rws_bytes else None
+        y = torch.empty((M, N), dtype=bf, device=dev)
+
+        def fused(ly):
+            dkv.dllm_refresh_qkv_rope_scatter(ly[0], h, idx, ly[1], Hq, wl.rope_base, q, rws)
+
+        def unfused(ly):
+            x = h[bidx, idx.long()].reshape(M, H)
+            torch.matmul(x, ly[1].t(), out=y)
+            dkv.dllm_rope_rows(y, Hq + Hkv, D, pos, wl.rope_base)
+            dkv.dllm_scatter_kv_rows(ly[0], y, Hq * D, (Hq + Hkv) * D, idx)
+
+        def scat(ly):
+            dkv.dllm_scatter_kv_rows(ly[0], y, Hq * D, (Hq + Hkv) * D, idx)
+
+        for fn in (fused, unfused):
+            for r in range(3):
+                fn(layers[r % L])
+        torch.cuda.synchronize()
+        count = max(10, args.steps)
+        uf, uu = burst_us(torch, fused, count, layers), burst_us(torch, unfused, count, layers)
+        ab[name] = {"rows": M, "fused_us": round(uf, 2), "unfused_us": round(uu, 2),
+                    "fused_speedup": round(uu / uf, 3)}
+        log(f"[bench] {name} refresh: fused {uf:.1f} us, unfused (gather + GEMM + rope + "
+            f"scatter) {uu:.1f} us")
+        if name == "c3":
+            us = burst_us(torch, scat, count, layers)
+            byts = 2 * M * Hkv * D * 2 * 2 + M * 4           # K, V rows read from y and written
+            scatter = {"workload": "c3 rows (1024 rows x 2 x 32 heads x 128, bf16)",
+                       "us": round(us, 2), "algorithmic_bytes": byts,
+                       "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1),
+                       "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            log(f"[bench] row scatter (c3): {us:.1f} us, {scatter['achieved_GBs']} GB/s")
+        del layers, h, y
+        torch.cuda.empty_cache()
+
+    # the drift check batched over 28 layers of the GQA shape: 28 x 8 sequences in one launch
+    wl = synth.WORKLOADS["c4"]
+    Lyr = 28
+    Bb, Hq, Hkv, S, D, k = wl.batch * Lyr, wl.q_heads, wl.kv_heads, wl.seq, wl.head_dim, wl.track_k
+    c = dkv.Cache(Bb, Hkv, S, D, dkv.DLLM_BF16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    c.k.copy_(torch.randn(c.k.shape, generator=g, device=dev).to(bf))
+    c.v.copy_(torch.randn(c.v.shape, generator=g, device=dev).to(bf))
+    masses = [torch.rand((Bb, Hq, S), generator=g, device=dev) for _ in range(3)]
+    T = torch.full((Bb, Hq, k), -1, dtype=torch.int32, device=dev)
+    buf = torch.zeros((Bb, Hq, k, 2, D), dtype=bf, device=dev)
+    sig = torch.empty((Bb, Hq), dtype=torch.float32, device=dev)
+    dec = torch.empty((Bb,), dtype=torch.uint8, device=dev)
+    dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[0], sig, dec)
+    torch.cuda.synchronize()
+    it = [0]
+
+    def drift(_):
+        it[0] += 1
+        dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[it[0] % 3], sig, dec)
+
+    us = burst_us(torch, drift, max(10, args.steps), [None])
+    byts = Bb * Hq * (3 * k * 2 * D * 2 + S * 4 + k * 8)
+    drift_b = {"workload": f"{Lyr} layers x B=8 of the GQA shape (28 query heads, S=2048, k=32) "
+                           "in one launch", "us": round(us, 2), "algorithmic_bytes": byts,
+               "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1),
+               "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"[bench] drift batched over {Lyr} layers: {us:.1f} us, {drift_b['achieved_GBs']} GB/s")
+    del c, masses, T, buf
+    torch.cuda.empty_cache()
+    return ab, {"row_scatter": scatter, "drift_batched": drift_b}
+
+
 def run(args):
     import torch
 
@@ -588,6 +689,8 @@ def run(args):
         result["layer_schedule"] = measure_schedule(args)
     if not args.no_fp8_linear:
         result["fp8_linear"] = measure_fp8_linear(args)
+    if not args.no_unfused:
+        result["unfused_refresh"], result["hbm_paths"] = measure_unfused_and_hbm_paths(args)
     if args.copy_calibration:
         # A plain device copy of known size, so HBM byte counters read under a profiler can be
         # scaled by what they report for a copy (reads = writes = the buffer size).
@@ -681,6 +784,8 @@ def main():
                     help="layers of the Elastic-Cache schedule section (0: skip it)")
     ap.add_argument("--no-fp8-linear", action="store_true",
                     help="skip the per-group FP8 linear layer section")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the unfused-refresh comparison and the HBM-path section")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",

@@ -32,7 +32,8 @@ EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatte
            "dllm_schedule_rows_workspace_bytes", "dllm_schedule_rows", "dllm_copy_rows_varlen",
            "dllm_layer_step_workspace_bytes", "dllm_elastic_layer_step",
            "dllm_fp8_quantize_weight", "dllm_fp8_quantize_activations",
-           "dllm_fp8_linear_workspace_bytes", "dllm_fp8_linear", "dllm_last_error")
+           "dllm_fp8_linear_workspace_bytes", "dllm_fp8_linear", "dllm_rope_rows",
+           "dllm_scatter_kv_rows", "dllm_last_error")
 DLLM_OPT_DEBUG, DLLM_OPT_WIDE_OFFSETS = 1, 2
 DLLM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -130,6 +131,10 @@ def _load():
     lib.dllm_fp8_linear_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dllm_fp8_linear.restype = i32
     lib.dllm_fp8_linear.argtypes = [P, i32, i32, P, P, i32, P, P, ctypes.c_size_t, P]
+    lib.dllm_rope_rows.restype = i32
+    lib.dllm_rope_rows.argtypes = [P, i32, i32, i32, i32, P, ctypes.c_float, P]
+    lib.dllm_scatter_kv_rows.restype = i32
+    lib.dllm_scatter_kv_rows.argtypes = [ctypes.POINTER(CCache), P, i32, i32, i32, P, i32, P]
     lib.dllm_drift_check.restype = i32
     lib.dllm_drift_check.argtypes = [ctypes.POINTER(CCache), i32, i32, ctypes.c_float, P, P, P, P,
                                      P, P]
@@ -592,6 +597,27 @@ def dllm_fp8_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tens
         workspace = _scratch(max(1, need), x.device, stream)
     _check(lib.dllm_fp8_linear(_ptr(x), M, K, _ptr(w_codes), _ptr(w_scales), N, _ptr(y),
                                _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dllm_rope_rows(y: torch.Tensor, heads: int, head_dim: int, pos: torch.Tensor,
+                   rope_base: float, stream=None):
+    """y [M, ld] bf16 (rotated in place), pos [M] int32."""
+    M, ld = y.shape
+    _expect(y, "y", (M, ld), torch.bfloat16)
+    _expect(pos, "pos", (M,), torch.int32)
+    _check(lib.dllm_rope_rows(_ptr(y), M, ld, heads, head_dim, _ptr(pos), float(rope_base),
+                              _stream(stream)))
+
+
+def dllm_scatter_kv_rows(cache: Cache, y: torch.Tensor, k_col: int, v_col: int,
+                         refresh_idx: torch.Tensor, stream=None):
+    """y [B * n, ld] bf16, refresh_idx [B, n] int32."""
+    d = cache.desc
+    n = refresh_idx.shape[1]
+    _expect(refresh_idx, "refresh_idx", (d.batch, n), torch.int32)
+    _expect(y, "y", (d.batch * n, y.shape[1]), torch.bfloat16)
+    _check(lib.dllm_scatter_kv_rows(ctypes.byref(cache.c), _ptr(y), y.shape[1], k_col, v_col,
+                                    _ptr(refresh_idx), n, _stream(stream)))
 
 
 def dllm_fp8_e4m3_roundtrip(x: torch.Tensor, scale: float, codes: torch.Tensor,

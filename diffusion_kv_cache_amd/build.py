@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdllm_cache.so")
 SOURCES = ["api.hip", "refresh.hip", "refresh_splitk.hip", "attention.hip", "attention_fwd.hip",
-           "attention_fused.hip", "attention_facache.hip", "drift.hip", "schedule.hip", "fp8_linear.hip"]
+           "attention_fused.hip", "attention_facache.hip", "drift.hip", "schedule.hip", "fp8_linear.hip", "unfused.hip"]
 ARCH = os.environ.get("DLLM_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -186,6 +186,33 @@ dllm_status finish(hipError_t e, hipStream_t s, const char* what) {
   return DLLM_OK;
 }
 
+// Debug mode: a device pass over the index lists (and the row offsets cu, if given); the
+// report comes back to the host and the stream is synchronised.
+dllm_status debug_check_lists(const int32_t* refresh_idx, const int32_t* cu, int n, int T,
+                              const dllm_cache_desc& d, hipStream_t s) {
+  DeviceSymbols* sym = nullptr;
+  dllm_status st = device_symbols(&sym);
+  if (st) return st;
+  hipError_t e = hipMemsetAsync(sym->debug_report, 0x7f, sizeof(int32_t), s);
+  if (e == hipSuccess) {
+    check_index_lists<<<d.batch, 256, 0, s>>>(refresh_idx, cu, n, T, d.max_seq, sym->debug_report);
+    e = hipGetLastError();
+  }
+  int32_t flat = 0, val = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&flat, sym->debug_report, sizeof flat, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && flat >= 0 && flat != 0x7f7f7f7f)
+    e = hipMemcpy(&val, refresh_idx + flat, sizeof val, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(DLLM_ELAUNCH, "debug index check: %s", hipGetErrorString(e));
+  if (flat < 0) return fail(DLLM_EINVAL, "row offsets broken at sequence %d", -1 - flat);
+  if (flat != 0x7f7f7f7f) {
+    if (val < 0 || val >= d.max_seq)
+      return fail(DLLM_EINVAL, "refresh_idx[%d] = %d outside [0, %d)", flat, val, d.max_seq);
+    return fail(DLLM_EINVAL, "refresh_idx not strictly increasing at packed row %d (value %d)", flat, val);
+  }
+  return DLLM_OK;
+}
+
 // Body of both refresh calls.  cu: row offsets [B + 1] of a variable-length batch (n is then
 // the largest rows per sequence and total all rows), or null (n rows per sequence).
 dllm_status refresh_call(const dllm_cache* c, const void* hidden, int32_t hidden_size,
@@ -230,28 +257,8 @@ dllm_status refresh_call(const dllm_cache* c, const void* hidden, int32_t hidden
   hipStream_t s = (hipStream_t)stream;
 
   if (debug_mode()) {
-    // Device pass over the lists (and the row offsets); the report comes back to the host and
-    // the stream is synchronised (debug mode only).
-    DeviceSymbols* sym = nullptr;
-    st = device_symbols(&sym);
+    st = debug_check_lists(refresh_idx, cu, n, (int)M, d, s);
     if (st) return st;
-    hipError_t e = hipMemsetAsync(sym->debug_report, 0x7f, sizeof(int32_t), s);
-    if (e == hipSuccess) {
-      check_index_lists<<<d.batch, 256, 0, s>>>(refresh_idx, cu, n, (int)M, d.max_seq, sym->debug_report);
-      e = hipGetLastError();
-    }
-    int32_t flat = 0, val = 0;
-    if (e == hipSuccess) e = hipMemcpyAsync(&flat, sym->debug_report, sizeof flat, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e == hipSuccess && flat >= 0 && flat != 0x7f7f7f7f)
-      e = hipMemcpy(&val, refresh_idx + flat, sizeof val, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return fail(DLLM_ELAUNCH, "debug index check: %s", hipGetErrorString(e));
-    if (flat < 0) return fail(DLLM_EINVAL, "row offsets broken at sequence %d", -1 - flat);
-    if (flat != 0x7f7f7f7f) {
-      if (val < 0 || val >= d.max_seq)
-        return fail(DLLM_EINVAL, "refresh_idx[%d] = %d outside [0, %d)", flat, val, d.max_seq);
-      return fail(DLLM_EINVAL, "refresh_idx not strictly increasing at packed row %d (value %d)", flat, val);
-    }
   }
 
   dllm::RefreshArgs a;
@@ -873,6 +880,50 @@ dllm_status dllm_fp8_linear(const void* x, int32_t M, int32_t K, const uint8_t* 
   hipError_t e = dllm::launch_fp8_quant_groups(x, M, K, p.Mp, (uint8_t*)base, (float*)(base + w.codes), false, s);
   if (e == hipSuccess) e = dllm::launch_fp8_gemm(a, p, s);
   return finish(e, s, "fp8 linear");
+}
+
+dllm_status dllm_rope_rows(void* y, int32_t M, int32_t ld, int32_t heads, int32_t head_dim,
+                           const int32_t* pos, float rope_base, void* stream) {
+  if (M < 0 || heads <= 0 || (head_dim != 64 && head_dim != 128))
+    return fail(DLLM_EINVAL, "M=%d, heads=%d, head_dim=%d: M >= 0, heads >= 1, head_dim 64 or 128", M, heads, head_dim);
+  if ((long long)ld < (long long)heads * head_dim) return fail(DLLM_EINVAL, "ld %d below heads * head_dim", ld);
+  if (!(rope_base > 0.f)) return fail(DLLM_EINVAL, "rope_base must be positive");
+  if (M == 0) {
+    g_err[0] = '\0';
+    return DLLM_OK;
+  }
+  if (!y || !pos) return fail(DLLM_EINVAL, "null y or pos");
+  if ((uintptr_t)y & 1u) return fail(DLLM_EINVAL, "y must be 2-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dllm::launch_rope_rows(y, M, ld, heads, head_dim, pos, (double)rope_base, s), s,
+                "rope rows");
+}
+
+dllm_status dllm_scatter_kv_rows(const dllm_cache* c, const void* y, int32_t ld, int32_t k_col,
+                                 int32_t v_col, const int32_t* refresh_idx, int32_t n,
+                                 void* stream) {
+  dllm_status st = check_cache(c);
+  if (st) return st;
+  const dllm_cache_desc& d = c->desc;
+  if (d.kv_dtype != DLLM_BF16) return fail(DLLM_EUNSUPPORTED, "the row scatter takes a bf16 cache");
+  if (n < 0 || n > d.max_seq) return fail(DLLM_EINVAL, "n=%d outside [0, S=%d]", n, d.max_seq);
+  const long long span = (long long)d.num_kv_heads * d.head_dim;
+  if (ld % 8 || k_col % 8 || v_col % 8 || k_col < 0 || v_col < 0 || k_col + span > ld || v_col + span > ld)
+    return fail(DLLM_EINVAL, "ld %d, k_col %d, v_col %d: multiples of 8 with Hkv * D columns inside ld", ld, k_col, v_col);
+  if (n == 0) {
+    g_err[0] = '\0';
+    return DLLM_OK;
+  }
+  if (!y || !refresh_idx) return fail(DLLM_EINVAL, "null y or refresh_idx");
+  if (!aligned16(y)) return fail(DLLM_EINVAL, "y must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (debug_mode()) {
+    st = debug_check_lists(refresh_idx, nullptr, n, d.batch * n, d, s);
+    if (st) return st;
+  }
+  return finish(dllm::launch_scatter_kv_rows(y, ld, k_col, v_col, c->k, c->v, d.batch, n,
+                                             d.num_kv_heads, d.max_seq, d.head_dim, refresh_idx, s),
+                s, "row scatter");
 }
 
 dllm_status dllm_fp8_e4m3_roundtrip(const float* x, int64_t n, float scale, uint8_t* codes,

@@ -178,4 +178,11 @@ hipError_t launch_fp8_quant_blocks(const void* w, int N, int K, uint8_t* q, floa
                                    hipStream_t s);
 hipError_t launch_fp8_gemm(const Fp8GemmArgs& a, const Fp8Plan& p, hipStream_t s);
 
+// The unfused refresh, for comparison: rotary embedding of rows in place, K/V row scatter.
+hipError_t launch_rope_rows(void* y, int M, int ld, int heads, int D, const int32_t* pos,
+                            double base, hipStream_t s);
+hipError_t launch_scatter_kv_rows(const void* y, int ld, int k_col, int v_col, void* kc, void* vc,
+                                  int B, int n, int Hkv, int S, int D, const int32_t* idx,
+                                  hipStream_t s);
+
 }  // namespace dllm

@@ -1,0 +1,74 @@
+// The unfused form of the refresh, for comparison with the fused kernels (Flash-dLLM news
+// summary, memory paragraph: the projection, the rotary embedding and the cache write as
+// separate kernels, each a round trip through HBM).  With the gather and the projection done
+// by any GEMM into y [M, ld] (columns Q heads | K heads | V heads):
+//   rope_rows        rotates the Q and K head columns of y in place at each row's position;
+//   scatter_kv_rows  copies each row's K and V head columns into the flat cache at
+//                    (b, g, position), 16-byte chunks, every other cache row untouched.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dllm {
+namespace {
+
+// One thread per rotary pair (row m, head j, pair i): (x_i, x_{i + D/2}) of y[m, j*D ...].
+__global__ __launch_bounds__(256) void rope_rows(bf16_t* y, int M, int ld, int heads, int D,
+                                                 const int32_t* pos, double base) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int half = D / 2;
+  const long long total = (long long)M * heads * half;
+  if (t >= total) return;
+  const int i = (int)(t % half);
+  const long long rh = t / half;
+  const int j = (int)(rh % heads), m = (int)(rh / heads);
+  bf16_t* row = y + (size_t)m * ld + (size_t)j * D;
+  float x = bf16_to_f32(row[i]), z = bf16_to_f32(row[i + half]);
+  float hi, lo, s, c;
+  rope_turns(i, D, base, hi, lo);
+  rope_sincos(pos[m], hi, lo, s, c);
+  rope_rotate(x, z, s, c);
+  row[i] = f32_to_bf16(x);
+  row[i + half] = f32_to_bf16(z);
+}
+
+// One thread per 16-byte chunk of a K or V row: chunk c of (row m, KV head g, part).
+__global__ __launch_bounds__(256) void scatter_kv_rows(const bf16_t* y, int ld, int k_col, int v_col,
+                                                       bf16_t* kc, bf16_t* vc, int n, int Hkv,
+                                                       int S, int D, const int32_t* idx, int M) {
+  const int cpr = D / 8;                         // chunks per row
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long total = (long long)M * Hkv * 2 * cpr;
+  if (t >= total) return;
+  const int c = (int)(t % cpr);
+  long long r = t / cpr;
+  const int part = (int)(r % 2);
+  r /= 2;
+  const int g = (int)(r % Hkv), m = (int)(r / Hkv);
+  const int b = m / n, p = idx[m];
+  const u32x4 v = *(const u32x4*)(y + (size_t)m * ld + (part ? v_col : k_col) + (size_t)g * D + c * 8);
+  bf16_t* dst = (part ? vc : kc) + (((size_t)b * Hkv + g) * S + p) * D + c * 8;
+  *(u32x4*)dst = v;
+}
+
+}  // namespace
+
+hipError_t launch_rope_rows(void* y, int M, int ld, int heads, int D, const int32_t* pos,
+                            double base, hipStream_t s) {
+  const long long total = (long long)M * heads * (D / 2);
+  if (total == 0) return hipSuccess;
+  rope_rows<<<(unsigned)((total + 255) / 256), 256, 0, s>>>((bf16_t*)y, M, ld, heads, D, pos, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_kv_rows(const void* y, int ld, int k_col, int v_col, void* kc, void* vc,
+                                  int B, int n, int Hkv, int S, int D, const int32_t* idx,
+                                  hipStream_t s) {
+  const int M = B * n;
+  const long long total = (long long)M * Hkv * 2 * (D / 8);
+  if (total == 0) return hipSuccess;
+  scatter_kv_rows<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
+      (const bf16_t*)y, ld, k_col, v_col, (bf16_t*)kc, (bf16_t*)vc, n, Hkv, S, D, idx, M);
+  return hipGetLastError();
+}
+
+}  // namespace dllm

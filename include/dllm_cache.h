@@ -455,6 +455,26 @@ DLLM_API dllm_status dllm_fp8_linear(const void *x, int32_t M, int32_t K, const 
                                      const float *w_scales, int32_t N, void *y, void *workspace,
                                      size_t ws_bytes, void *stream);
 
+/* ---- The unfused refresh, for comparison with the fused call (Flash-dLLM news summary,
+ * memory paragraph: projection, rotary embedding and cache write as separate kernels, each a
+ * round trip through HBM).  With y = gathered hidden rows x W_qkv^T computed by any GEMM
+ * ([B * n, ld] bf16, row m = b * n + i; columns Q heads | K heads | V heads):
+ *   dllm_rope_rows        rotates, in place, the pairs (i, i + D/2) of the first `heads` head
+ *                         columns of every row m at position pos[m] (the same rotation as the
+ *                         fused call: theta_i = rope_base^(-2i/D), rotate-half); bf16
+ *   dllm_scatter_kv_rows  copies, for every row m = b * n + i and KV head g, the D values at
+ *                         columns k_col + g * D and v_col + g * D into the cache rows
+ *                         (b, g, refresh_idx[b, i]) of K and V; every other cache row is left
+ *                         as it is.  bf16 cache; ld, k_col, v_col multiples of 8; y 16-byte
+ *                         aligned; debug mode checks refresh_idx as the refresh call does.
+ * Errors: DLLM_EINVAL, DLLM_EUNSUPPORTED, DLLM_ELAUNCH. */
+DLLM_API dllm_status dllm_rope_rows(void *y, int32_t M, int32_t ld, int32_t heads,
+                                    int32_t head_dim, const int32_t *pos, float rope_base,
+                                    void *stream);
+DLLM_API dllm_status dllm_scatter_kv_rows(const dllm_cache *c, const void *y, int32_t ld,
+                                          int32_t k_col, int32_t v_col,
+                                          const int32_t *refresh_idx, int32_t n, void *stream);
+
 /* FP8 codec of the cache, exposed so the conversion can be checked element by element:
  * codes[i] = e4m3(x[i] / scale) (nearest even, saturating to +-448, NaN -> NaN) and
  * decoded[i] = decode(codes[i]) * scale.  x, codes, decoded: device arrays of n elements;
