@@ -647,9 +647,31 @@ def measure_unfused_and_hbm_paths(args):
                "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1),
                "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     log(f"[bench] drift batched over {Lyr} layers: {us:.1f} us, {drift_b['achieved_GBs']} GB/s")
+    # attainable rates beside the datasheet peaks: a device copy, and a loop of independent
+    # MFMAs on register operands
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    cp_us = burst_us(torch, lambda _: dst.copy_(src), 10, [None])
+    del src, dst
+    wgs, iters = 256 * 8, 2048
+    out = torch.empty(wgs * 4, dtype=torch.float32, device=dev)
+    attain = {"copy_GBs": round(2 * nb / (cp_us * 1e-6) / 1e9, 1)}
+    for kind, name, tile, flops in ((dkv.DLLM_BF16, "bf16_16x16x32", 16, 2 * 16 * 16 * 32 * 8),
+                                    (dkv.DLLM_BF16, "bf16_32x32x16", 32, 2 * 32 * 32 * 16 * 4),
+                                    (dkv.DLLM_FP8_E4M3, "fp8_16x16x128", 16, 2 * 16 * 16 * 128 * 8),
+                                    (dkv.DLLM_FP8_E4M3, "fp8_32x32x64", 32, 2 * 32 * 32 * 64 * 4)):
+        dkv.dllm_mfma_rate_probe(kind, tile, wgs, 16, out)
+        us = burst_us(torch, lambda _: dkv.dllm_mfma_rate_probe(kind, tile, wgs, iters, out), 5,
+                      [None])
+        tf = wgs * 4 * iters * flops / (us * 1e-6) / 1e12
+        attain[f"mfma_{name}_TFLOPs"] = round(tf, 1)
+        attain[f"mfma_{name}_frac_of_peak"] = round(tf / MFMA_PEAK_TFLOPS[name[:4].rstrip("_")], 4)
+    log("[bench] attainable: copy {} GB/s; ".format(attain["copy_GBs"]) +
+        ", ".join(f"{k[5:-7]} {v} TFLOP/s" for k, v in attain.items() if k.endswith("TFLOPs")))
     del c, masses, T, buf
     torch.cuda.empty_cache()
-    return ab, {"row_scatter": scatter, "drift_batched": drift_b}
+    return ab, {"row_scatter": scatter, "drift_batched": drift_b, "attainable": attain}
 
 
 def run(args):

@@ -33,7 +33,7 @@ EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatte
            "dllm_layer_step_workspace_bytes", "dllm_elastic_layer_step",
            "dllm_fp8_quantize_weight", "dllm_fp8_quantize_activations",
            "dllm_fp8_linear_workspace_bytes", "dllm_fp8_linear", "dllm_rope_rows",
-           "dllm_scatter_kv_rows", "dllm_last_error")
+           "dllm_scatter_kv_rows", "dllm_mfma_rate_probe", "dllm_last_error")
 DLLM_OPT_DEBUG, DLLM_OPT_WIDE_OFFSETS = 1, 2
 DLLM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -135,6 +135,8 @@ def _load():
     lib.dllm_rope_rows.argtypes = [P, i32, i32, i32, i32, P, ctypes.c_float, P]
     lib.dllm_scatter_kv_rows.restype = i32
     lib.dllm_scatter_kv_rows.argtypes = [ctypes.POINTER(CCache), P, i32, i32, i32, P, i32, P]
+    lib.dllm_mfma_rate_probe.restype = i32
+    lib.dllm_mfma_rate_probe.argtypes = [i32, i32, i32, i32, P, P]
     lib.dllm_drift_check.restype = i32
     lib.dllm_drift_check.argtypes = [ctypes.POINTER(CCache), i32, i32, ctypes.c_float, P, P, P, P,
                                      P, P]
@@ -618,6 +620,13 @@ def dllm_scatter_kv_rows(cache: Cache, y: torch.Tensor, k_col: int, v_col: int,
     _expect(y, "y", (d.batch * n, y.shape[1]), torch.bfloat16)
     _check(lib.dllm_scatter_kv_rows(ctypes.byref(cache.c), _ptr(y), y.shape[1], k_col, v_col,
                                     _ptr(refresh_idx), n, _stream(stream)))
+
+
+def dllm_mfma_rate_probe(kind: int, tile: int, workgroups: int, iters: int, out: torch.Tensor,
+                         stream=None):
+    """out [workgroups * 4] fp32; tile 16 or 32."""
+    _expect(out, "out", (workgroups * 4,), torch.float32)
+    _check(lib.dllm_mfma_rate_probe(kind, tile, workgroups, iters, _ptr(out), _stream(stream)))
 
 
 def dllm_fp8_e4m3_roundtrip(x: torch.Tensor, scale: float, codes: torch.Tensor,

@@ -926,6 +926,16 @@ dllm_status dllm_scatter_kv_rows(const dllm_cache* c, const void* y, int32_t ld,
                 s, "row scatter");
 }
 
+dllm_status dllm_mfma_rate_probe(int32_t kind, int32_t tile, int32_t workgroups, int32_t iters,
+                                 float* out, void* stream) {
+  if (kind != DLLM_BF16 && kind != DLLM_FP8_E4M3) return fail(DLLM_EINVAL, "kind: DLLM_BF16 or DLLM_FP8_E4M3");
+  if (tile != 16 && tile != 32) return fail(DLLM_EINVAL, "tile: 16 or 32");
+  if (workgroups <= 0 || iters <= 0) return fail(DLLM_EINVAL, "workgroups and iters must be positive");
+  if (!out) return fail(DLLM_EINVAL, "null out");
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dllm::launch_mfma_probe(kind, tile == 32, workgroups, iters, out, s), s, "mfma probe");
+}
+
 dllm_status dllm_fp8_e4m3_roundtrip(const float* x, int64_t n, float scale, uint8_t* codes,
                                     float* decoded, void* stream) {
   if (n < 0) return fail(DLLM_EINVAL, "n < 0");

@@ -185,4 +185,7 @@ hipError_t launch_scatter_kv_rows(const void* y, int ld, int k_col, int v_col, v
                                   int B, int n, int Hkv, int S, int D, const int32_t* idx,
                                   hipStream_t s);
 
+// Attainable matrix-core rate (a loop of independent MFMAs on register operands).
+hipError_t launch_mfma_probe(int kind, int big, int workgroups, int iters, float* out, hipStream_t s);
+
 }  // namespace dllm

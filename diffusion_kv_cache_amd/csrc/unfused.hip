@@ -5,6 +5,7 @@
 //   rope_rows        rotates the Q and K head columns of y in place at each row's position;
 //   scatter_kv_rows  copies each row's K and V head columns into the flat cache at
 //                    (b, g, position), 16-byte chunks, every other cache row untouched.
+// Also the attainable matrix-core rate microbenchmark of the roofline report (mfma_probe).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -68,6 +69,84 @@ hipError_t launch_scatter_kv_rows(const void* y, int ld, int k_col, int v_col, v
   if (total == 0) return hipSuccess;
   scatter_kv_rows<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(
       (const bf16_t*)y, ld, k_col, v_col, (bf16_t*)kc, (bf16_t*)vc, n, Hkv, S, D, idx, M);
+  return hipGetLastError();
+}
+
+}  // namespace dllm
+
+// ------------------------------------------------------------------------------------------
+// Attainable matrix-core rate: every wave chains `iters` rounds of independent MFMAs on
+// register operands (no memory traffic in the loop): eight 16 x 16 chains (bf16 K = 32, FP8
+// K = 128) or four 32 x 32 chains (bf16 K = 16, FP8 K = 64); one value per wave is stored so
+// the work is kept.
+// ------------------------------------------------------------------------------------------
+namespace dllm {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) int i32x8_probe;
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_probe;
+
+// BIG: 32 x 32 output tiles (bf16 K = 16, FP8 K = 64) instead of 16 x 16 (K = 32, 128).
+template <int KIND, bool BIG>
+__global__ __launch_bounds__(256) void mfma_probe(int iters, float* out) {
+  const int t = threadIdx.x;
+  const uint32_t s = 0x3c003c00u ^ (uint32_t)(t & 7);
+  float sum = 0.f;
+  if constexpr (KIND == kCacheFP8) {
+    const i32x8_probe a = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                           0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    if constexpr (BIG) {
+      f32x16_probe acc[4] = {};
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, acc[c], 0, 0, 0, 0x7f7f7f7f,
+                                                                  0, 0x7f7f7f7f);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sum += acc[c][0];
+    } else {
+      f32x4 acc[8] = {};
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, a, acc[c], 0, 0, 0, 0x7f7f7f7f,
+                                                                   0, 0x7f7f7f7f);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sum += acc[c][0];
+    }
+  } else {
+    const u32x4 av = {s, s, s, s};
+    const bf16x8 a = as_bf16x8(av);
+    if constexpr (BIG) {
+      f32x16_probe acc[4] = {};
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, acc[c], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sum += acc[c][0];
+    } else {
+      f32x4 acc[8] = {};
+      for (int it = 0; it < iters; ++it)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = mfma_bf16(a, a, acc[c]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sum += acc[c][0];
+    }
+  }
+  if ((t & 63) == 0) out[blockIdx.x * 4 + (t >> 6)] = sum;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_probe(int kind, int big, int workgroups, int iters, float* out, hipStream_t s) {
+  if (kind == kCacheFP8) {
+    if (big) mfma_probe<kCacheFP8, true><<<workgroups, 256, 0, s>>>(iters, out);
+    else mfma_probe<kCacheFP8, false><<<workgroups, 256, 0, s>>>(iters, out);
+  } else {
+    if (big) mfma_probe<kCacheBF16, true><<<workgroups, 256, 0, s>>>(iters, out);
+    else mfma_probe<kCacheBF16, false><<<workgroups, 256, 0, s>>>(iters, out);
+  }
   return hipGetLastError();
 }
 

@@ -475,6 +475,16 @@ DLLM_API dllm_status dllm_scatter_kv_rows(const dllm_cache *c, const void *y, in
                                           int32_t k_col, int32_t v_col,
                                           const int32_t *refresh_idx, int32_t n, void *stream);
 
+/* Attainable matrix-core rate, a microbenchmark for the roofline report: `workgroups`
+ * workgroups of four waves, each wave chaining `iters` rounds of independent MFMAs on
+ * register operands, no memory traffic in the loop.  tile 16: eight 16x16 chains
+ * (DLLM_BF16: 16x16x32; DLLM_FP8_E4M3: 16x16x128 e4m3), 2 * 16 * 16 * K * 8 flops per wave and
+ * round; tile 32: four 32x32 chains (32x32x16 bf16, 32x32x64 e4m3), 2 * 32 * 32 * K * 4.
+ * out: device, [workgroups * 4] fp32 (one value per wave, meaningless, written so the work is
+ * kept).  Errors: DLLM_EINVAL, DLLM_ELAUNCH. */
+DLLM_API dllm_status dllm_mfma_rate_probe(int32_t kind, int32_t tile, int32_t workgroups,
+                                          int32_t iters, float *out, void *stream);
+
 /* FP8 codec of the cache, exposed so the conversion can be checked element by element:
  * codes[i] = e4m3(x[i] / scale) (nearest even, saturating to +-448, NaN -> NaN) and
  * decoded[i] = decode(codes[i]) * scale.  x, codes, decoded: device arrays of n elements;

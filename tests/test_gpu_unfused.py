@@ -90,3 +90,16 @@ def test_unfused_scatter_debug_mode_rejects_a_bad_list():
         assert "outside" in str(e.value)
     finally:
         dkv.dllm_set_options(prev)
+
+
+def test_mfma_rate_probe_runs_and_writes_every_wave():
+    for kind in (dkv.DLLM_BF16, dkv.DLLM_FP8_E4M3):
+        for tile in (16, 32):
+            out = torch.full((8 * 4,), 12345.0, dtype=torch.float32, device="cuda")
+            dkv.dllm_mfma_rate_probe(kind, tile, 8, 4, out)
+            torch.cuda.synchronize()
+            assert not torch.eq(out, 12345.0).any()
+    with pytest.raises(dkv.DllmError):
+        dkv.dllm_mfma_rate_probe(dkv.DLLM_F32, 16, 8, 4, out)
+    with pytest.raises(dkv.DllmError):
+        dkv.dllm_mfma_rate_probe(dkv.DLLM_BF16, 8, 8, 4, out)
