@@ -168,6 +168,7 @@ def measure(args, wl):
                      dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(D)
     track = layers[0].track
+    dws = dkv.drift_workspace(B, dev) if track else None  # decision in the drift launch
 
     # Previous step (untimed, on H_prev): the tracking sets come from its attention mass.
     for ly in layers:
@@ -175,7 +176,8 @@ def measure(args, wl):
             dkv.dllm_refresh_qkv_rope_scatter(ly.cache, h_prev, idx_t, ly.w, Hq, wl.rope_base, q,
                                               rws)
             dkv.dllm_block_attention(ly.cache, q, Hq, scale, out, lse, mass, ws)
-            dkv.dllm_drift_check(ly.cache, Hq, k, wl.gamma, ly.T, ly.buf, mass, sigma, refresh)
+            dkv.dllm_drift_check(ly.cache, Hq, k, wl.gamma, ly.T, ly.buf, mass, sigma, refresh,
+                                 dws)
     torch.cuda.synchronize()
 
     names = ["refresh", "attention"] + (["drift"] if track else [])
@@ -185,7 +187,7 @@ def measure(args, wl):
         "attention": lambda ly: dkv.dllm_block_attention(ly.cache, q, Hq, scale, out, lse,
                                                          mass if track else None, ws),
         "drift": lambda ly: dkv.dllm_drift_check(ly.cache, Hq, k, wl.gamma, ly.T, ly.buf, mass,
-                                                 sigma, refresh),
+                                                 sigma, refresh, dws),
     }
 
     def step(ly):
@@ -632,13 +634,14 @@ def measure_unfused_and_hbm_paths(args):
     buf = torch.zeros((Bb, Hq, k, 2, D), dtype=bf, device=dev)
     sig = torch.empty((Bb, Hq), dtype=torch.float32, device=dev)
     dec = torch.empty((Bb,), dtype=torch.uint8, device=dev)
-    dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[0], sig, dec)
+    dws = dkv.drift_workspace(Bb, dev)
+    dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[0], sig, dec, dws)
     torch.cuda.synchronize()
     it = [0]
 
     def drift(_):
         it[0] += 1
-        dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[it[0] % 3], sig, dec)
+        dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[it[0] % 3], sig, dec, dws)
 
     us = burst_us(torch, drift, max(10, args.steps), [None])
     byts = Bb * Hq * (3 * k * 2 * D * 2 + S * 4 + k * 8)

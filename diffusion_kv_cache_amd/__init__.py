@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "DLLM_OK", 1: "DLLM_EINVAL", 2: "DLLM_ESIZE", 3: "DLLM_EUNSUP
                 4: "DLLM_ELAUNCH"}
 EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatter",
            "dllm_refresh_workspace_bytes", "dllm_attention_workspace_bytes",
-           "dllm_block_attention", "dllm_drift_check", "dllm_fp8_e4m3_roundtrip",
+           "dllm_block_attention", "dllm_drift_workspace_bytes", "dllm_drift_check",
+           "dllm_fp8_e4m3_roundtrip",
            "dllm_set_options", "dllm_block_attention_noalloc", "dllm_facache_state_bytes",
            "dllm_facache_attention", "dllm_refresh_qkv_rope_scatter_varlen",
            "dllm_attention_varlen_workspace_bytes", "dllm_block_attention_varlen",
@@ -138,8 +139,10 @@ def _load():
     lib.dllm_mfma_rate_probe.restype = i32
     lib.dllm_mfma_rate_probe.argtypes = [i32, i32, i32, i32, P, P]
     lib.dllm_drift_check.restype = i32
+    lib.dllm_drift_workspace_bytes.restype = ctypes.c_size_t
+    lib.dllm_drift_workspace_bytes.argtypes = [i32]
     lib.dllm_drift_check.argtypes = [ctypes.POINTER(CCache), i32, i32, ctypes.c_float, P, P, P, P,
-                                     P, P]
+                                     P, P, ctypes.c_size_t, P]
     lib.dllm_fp8_e4m3_roundtrip.restype = i32
     lib.dllm_fp8_e4m3_roundtrip.argtypes = [P, i64, ctypes.c_float, P, P, P]
     lib.dllm_set_options.restype = i32
@@ -414,11 +417,19 @@ def dllm_facache_attention(cache: Cache, q_cache: torch.Tensor, q_block: torch.T
         _stream(stream)))
 
 
+def drift_workspace(batch: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for dllm_drift_check's decision in the same launch (every call
+    leaves it zero; calls that share it must not overlap)."""
+    n = int(lib.dllm_drift_workspace_bytes(batch))
+    return torch.zeros(max(n, 8) // 8, dtype=torch.int64, device=device)
+
+
 def dllm_drift_check(cache: Cache, num_q_heads: int, k: int, gamma: float,
                      track_idx: torch.Tensor, track_buf: torch.Tensor, attn_mass, sigma_out,
-                     refresh_out, stream=None):
+                     refresh_out, workspace=None, stream=None):
     """track_idx [B,Hq,k] int32 (in/out), track_buf [B,Hq,k,2,D] cache dtype (in/out),
-    attn_mass [B,Hq,S] fp32 or None, sigma_out [B,Hq] fp32, refresh_out [B] uint8."""
+    attn_mass [B,Hq,S] fp32 or None, sigma_out [B,Hq] fp32, refresh_out [B] uint8,
+    workspace from drift_workspace(B) or None (the decision by a second kernel)."""
     d = cache.desc
     B, Hq = d.batch, num_q_heads
     _expect(track_idx, "track_idx", (B, Hq, k), torch.int32)
@@ -427,9 +438,15 @@ def dllm_drift_check(cache: Cache, num_q_heads: int, k: int, gamma: float,
         _expect(attn_mass, "attn_mass", (B, Hq, d.max_seq), torch.float32)
     _expect(sigma_out, "sigma_out", (B, Hq), torch.float32)
     _expect(refresh_out, "refresh_out", (B,), torch.uint8)
+    ws_bytes = 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise DllmError(DLLM_EINVAL, "workspace: contiguous device tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.dllm_drift_check(
         ctypes.byref(cache.c), num_q_heads, k, float(gamma), _ptr(track_idx), _ptr(track_buf),
-        _ptr(attn_mass), _ptr(sigma_out), _ptr(refresh_out), _stream(stream)))
+        _ptr(attn_mass), _ptr(sigma_out), _ptr(refresh_out), _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def dllm_similarity_select(hidden_cur: torch.Tensor, hidden_cached: torch.Tensor, lo: int,

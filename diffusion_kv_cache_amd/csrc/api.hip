@@ -576,9 +576,15 @@ dllm_status dllm_facache_attention(const dllm_cache* c, void* q_cache, const voi
   return finish(dllm::launch_facache(a, s), s, "facache attention");
 }
 
+size_t dllm_drift_workspace_bytes(int32_t batch) {
+  if (batch <= 0) return 0;
+  return (size_t)batch * dllm::kDriftArriveStride * sizeof(unsigned long long);
+}
+
 dllm_status dllm_drift_check(const dllm_cache* c, int32_t num_q_heads, int32_t k, float gamma,
                              int32_t* track_idx, void* track_buf, const float* attn_mass,
-                             float* sigma_out, uint8_t* refresh_out, void* stream) {
+                             float* sigma_out, uint8_t* refresh_out, void* workspace,
+                             size_t ws_bytes, void* stream) {
   dllm_status st = check_cache(c);
   if (st) return st;
   const dllm_cache_desc& d = c->desc;
@@ -593,6 +599,13 @@ dllm_status dllm_drift_check(const dllm_cache* c, int32_t num_q_heads, int32_t k
   if (!aligned16(track_buf)) return fail(DLLM_EINVAL, "track_buf must be 16-byte aligned");
   if (attn_mass && d.max_seq > 16384)
     return fail(DLLM_EUNSUPPORTED, "tracking update supports S <= 16384 (S=%d)", d.max_seq);
+  if ((int64_t)d.max_seq * d.head_dim >= ((int64_t)1 << 31))
+    return fail(DLLM_EUNSUPPORTED, "drift check needs S * head_dim < 2^31");
+  if (workspace) {
+    const size_t need = dllm_drift_workspace_bytes(d.batch);
+    if (ws_bytes < need) return fail(DLLM_ESIZE, "drift workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if ((uintptr_t)workspace % 8) return fail(DLLM_EINVAL, "drift workspace must be 8-byte aligned");
+  }
   dllm::DriftArgs a;
   a.kc = c->k;
   a.vc = c->v;
@@ -601,6 +614,7 @@ dllm_status dllm_drift_check(const dllm_cache* c, int32_t num_q_heads, int32_t k
   a.mass = attn_mass;
   a.sigma = sigma_out;
   a.refresh = refresh_out;
+  a.arrive = (unsigned long long*)workspace;
   a.B = d.batch;
   a.Hq = num_q_heads;
   a.Hkv = d.num_kv_heads;
@@ -790,7 +804,7 @@ dllm_status dllm_elastic_layer_step(const dllm_cache* c, const dllm_layer_step* 
                       ws_att, w.attn, false, stream, a->cu_rows, nullptr, cap);
   if (st) return st;
   st = dllm_drift_check(c, Hq, a->k_track, a->gamma, a->track_idx, a->track_buf, a->attn_mass,
-                        a->sigma, a->decision, stream);
+                        a->sigma, a->decision, nullptr, 0, stream);
   if (st) return st;
   return dllm_copy_rows_varlen(B, S, a->hidden_size * 2, a->hidden_cur, a->hidden_feat, a->rows,
                                a->cu_rows, cap, stream);

@@ -7,14 +7,17 @@
 // of the 32 most-attended tokens.
 //
 // drift_track: one workgroup per (b, h).  The K||V rows of the tracked slots are compared in
-// fp64 (16-byte loads, DPP sums over rows of 16 lanes, then the 16 row sums in order).  Then,
-// when this step's mass is given, a radix select over the order-preserving bits of the mass
-// (staged in LDS) finds the k-th largest value in up to four 8-bit passes (it stops as soon as
+// fp64 (16-byte loads, one partial per chunk, DPP sums over rows of 16 lanes, row swaps over
+// the four rows, then the four wave sums in order).  Then, when this step's mass is given, a
+// radix select over the order-preserving bits of the mass (held in registers) finds the k-th
+// largest value in 8-bit passes over the bits below those all keys share (it stops as soon as
 // every key of the boundary digit is taken); values above it are taken, and of the values
-// equal to it the lowest positions, placed by ballot counts so the set comes out in ascending
-// position order; the tracking buffer is refilled from the current cache.  Scans within a
-// wave are DPP moves.
-// drift_decide: one wave per sequence, any head below gamma.
+// equal to it the lowest positions, placed by a prefix count over threads so the set comes out
+// in ascending position order; the tracking buffer is refilled from the current cache.  Scans
+// within a wave are DPP moves.
+// The decision (any head of a sequence below gamma) is taken by the last head of the sequence
+// to finish, through an arrival word in a caller workspace, or else by drift_decide, one wave
+// per sequence.
 #include <math.h>
 
 #include "common.hpp"
@@ -43,6 +46,22 @@ __device__ __forceinline__ double row_sum_f64(double v) {
   return v;
 }
 
+// Sum over the four rows of 16 lanes of a wave (each row holding one value in all its
+// lanes), left in every lane: the gfx950 row swaps pair lane l with l ^ 32, then with l ^ 16;
+// both partners add the same two operands, so every lane ends with the same bits.
+__device__ __forceinline__ double rows_sum_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  v = __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi[0] << 32) | (uint32_t)lo[0]) +
+      __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi[1] << 32) | (uint32_t)lo[1]);
+  const uint64_t w = __builtin_bit_cast(uint64_t, v);
+  const auto lo2 = __builtin_amdgcn_permlane16_swap((uint32_t)w, (uint32_t)w, false, false);
+  const auto hi2 = __builtin_amdgcn_permlane16_swap((uint32_t)(w >> 32), (uint32_t)(w >> 32), false, false);
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi2[0] << 32) | (uint32_t)lo2[0]) +
+         __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi2[1] << 32) | (uint32_t)lo2[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts of 1, 2, 4 and 8
 // lanes inside each row of 16, then the running totals of rows 0 and 2 (lanes 15, 47) into
 // rows 1 and 3, then that of rows 0-1 (lane 31) into rows 2 and 3.  Lanes without a source
@@ -55,6 +74,31 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
+}
+
+// Largest and smallest value over the 64 lanes of a wave, in every lane: DPP moves inside
+// each row of 16 (quad permutes, half-row and row mirrors), then the gfx950 row swaps
+// (v_permlane32_swap pairs lane l with l ^ 32, v_permlane16_swap with l ^ 16; with both
+// operands = v, the two results are v of the lane and of its partner).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+  const auto x = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max((uint32_t)x[0], (uint32_t)x[1]);
+  const auto y = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((uint32_t)y[0], (uint32_t)y[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+  const auto x = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = min((uint32_t)x[0], (uint32_t)x[1]);
+  const auto y = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return min((uint32_t)y[0], (uint32_t)y[1]);
 }
 
 // Order-preserving map of fp32 bits to uint32 (larger float -> larger key).
@@ -78,22 +122,19 @@ __device__ __forceinline__ void chunk_f64(const u32x4& w, double* out) {
   }
 }
 
-// Mass values per thread loaded ahead of everything else (four 16-byte loads): S <= 4096
-// needs one round, longer rows take further rounds after it.
-constexpr int kMassAhead = 4;
-
 // One workgroup per (b, h): the drift of the previous tracked set, then (do_update) the new
 // top-k set and the tracking-buffer refill.  The old set and the buffer are read before any
 // write.  Global loads that do not depend on each other are issued together (old positions,
 // buffer rows, this step's mass), the cache rows of the cosine stay in flight while the
-// top-k runs on LDS, and the rows of the new set are requested as soon as it is known, so
-// they arrive while the cosine is formed.
+// top-k runs, and the rows of the new set are requested as soon as it is known, so they
+// arrive while the cosine is formed.
 // CH: 16-byte chunks of the tracked K||V rows per thread (k * 2 * D / elements per chunk /
 // 256, rounded up to a power of two).  Chunk indices past the end are clamped to the last
 // chunk, so every load is issued unconditionally, back to back.
-template <typename E, int CH>
+// KP: mass values per thread (4, 16 or 64; S <= 256 KP): thread t holds the order keys of
+// positions [t KP, t KP + KP) in registers, so position order is (thread, slot) order.
+template <typename E, int CH, int KP>
 __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
-  extern __shared__ uint32_t keys[];             // [S] order keys of this head's mass
   constexpr int EPC = 16 / (int)sizeof(E);       // elements per 16-byte chunk
   constexpr int kMaxChunks = CH;
   const int h = blockIdx.x, b = blockIdx.y;
@@ -102,20 +143,23 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   const int D = a.D, k = a.k, S = a.S;
   int32_t* T = a.track_idx + ((size_t)b * a.Hq + h) * k;
   E* buf = (E*)a.track_buf + ((size_t)b * a.Hq + h) * k * 2 * D;
-  const E* kc = (const E*)a.kc;
-  const E* vc = (const E*)a.vc;
-  const size_t head_base = ((size_t)b * a.Hkv + g) * S;
+  const size_t head_base = ((size_t)b * a.Hkv + g) * S * D;  // this KV head's rows
+  const E* kh = (const E*)a.kc + head_base;
+  const E* vh = (const E*)a.vc + head_base;
   const int cpr = D / EPC;                       // chunks per K (or V) row (power of 2)
   const int cs = __builtin_ctz(cpr);
   const int nch = k * 2 * cpr;                   // chunks of the tracked rows
 
-  __shared__ double red[3][16];                  // row sums: [quantity][wave * 4 + row]
+  __shared__ double red[3][4];                   // wave sums: [quantity][wave]
   __shared__ int sflag[4];
-  __shared__ int32_t sT[64], sTn[64];            // old and new tracked positions
-  __shared__ uint32_t hist[4][256];              // one digit histogram per radix pass
-  __shared__ uint32_t wcnt[2][4];                // per wave: keys above, keys equal
+  __shared__ int32_t sT[64];                     // old tracked positions
+  __shared__ int32_t sTn[64 + 256];              // new ones, then a discard slot per thread
+  __shared__ __align__(16) uint32_t hist[4][256 + 64];  // per radix pass: 256 digit counts,
+                                                        // then one discard slot per lane
+  __shared__ __align__(16) uint32_t wext[2][4];  // per wave: largest and smallest key
+  __shared__ __align__(16) uint32_t wsum[4];     // per wave: (keys above << 16) + keys equal
 
-  // ---- loads issued together: old positions, buffer rows, the first round of mass ----
+  // ---- loads issued together: old positions, buffer rows, this step's mass ----
   const int told = (t < k) ? T[t] : -1;
   u32x4 ub[kMaxChunks];
 #pragma unroll
@@ -123,79 +167,91 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
     const int c = min(t + 256 * i, nch - 1);
     ub[i] = *(const u32x4*)(buf + (size_t)c * EPC);
   }
+  const int p0 = t * KP;                         // this thread's first position
+  const int nv = do_update ? max(0, min(KP, S - p0)) : 0;  // its positions below S
   const float* mass = a.mass + ((size_t)b * a.Hq + h) * S;
-  const bool vec_mass = do_update && (S % 4 == 0) && (((uintptr_t)a.mass & 15) == 0);
-  float4 mr[kMassAhead];
+  const bool vec_mass = (S % 4 == 0) && (((uintptr_t)a.mass & 15) == 0);
+  float mv[KP];
   if (vec_mass) {
 #pragma unroll
-    for (int u = 0; u < kMassAhead; ++u) {
-      const int q = t + 256 * u;
-      if (q < S / 4) mr[u] = ((const float4*)mass)[q];
+    for (int u = 0; u < KP / 4; ++u) {
+      float4 m4 = {0.f, 0.f, 0.f, 0.f};
+      if (4 * u < nv) m4 = *(const float4*)(mass + p0 + 4 * u);
+      mv[4 * u] = m4.x;
+      mv[4 * u + 1] = m4.y;
+      mv[4 * u + 2] = m4.z;
+      mv[4 * u + 3] = m4.w;
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KP; ++i) mv[i] = (i < nv) ? mass[p0 + i] : 0.f;
   }
 #pragma unroll
-  for (int p = 0; p < 4; ++p) hist[p][t] = 0;
+  for (int p = 0; p < 4; ++p) hist[p][t] = 0;   // (discard slots are never read)
   if (t < k) sT[t] = told;
-  if (vec_mass) {
+  uint32_t key[KP];
+  uint32_t kmax = 0u, kmin = 0xffffffffu;        // range of the keys (none: empty range)
 #pragma unroll
-    for (int u = 0; u < kMassAhead; ++u) {
-      const int q = t + 256 * u;
-      if (q < S / 4) {
-        keys[4 * q] = order_key(mr[u].x);
-        keys[4 * q + 1] = order_key(mr[u].y);
-        keys[4 * q + 2] = order_key(mr[u].z);
-        keys[4 * q + 3] = order_key(mr[u].w);
-      }
+  for (int i = 0; i < KP; ++i) {
+    key[i] = order_key(mv[i]);
+    if (i < nv) {
+      kmax = max(kmax, key[i]);
+      kmin = min(kmin, key[i]);
     }
+  }
+  kmax = wave_max_u32(kmax);
+  kmin = wave_min_u32(kmin);
+  if (lane == 0) {
+    wext[0][wave] = kmax;
+    wext[1][wave] = kmin;
   }
   __syncthreads();
 
   // ---- cache rows of the old set: in flight during the top-k ----
+  // (okc: the chunk exists and its slot holds a position; the others read row 0 and count
+  // as zeros in the cosine)
   u32x4 uc[kMaxChunks];
+  bool okc[kMaxChunks];
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = min(t + 256 * i, nch - 1);
     const int slot = c >> (cs + 1), part = (c >> cs) & 1, d0 = (c & (cpr - 1)) * EPC;
     const int j = sT[slot];
-    const int jc = (j >= 0 && j < S) ? j : 0;    // empty slots read row 0, unused below
-    uc[i] = *(const u32x4*)((part ? vc : kc) + (head_base + jc) * D + d0);
+    okc[i] = t + 256 * i < nch && j >= 0 && j < S;
+    uc[i] = *(const u32x4*)((part ? vh : kh) + ((okc[i] ? j : 0) * D + d0));
   }
 
   if (do_update) {
-    // the rest of the mass (rows longer than the first round, or not a multiple of 4)
-    if (vec_mass) {
-      for (int q = t + 256 * kMassAhead; q < S / 4; q += 256) {
-        const float4 m4 = ((const float4*)mass)[q];
-        keys[4 * q] = order_key(m4.x);
-        keys[4 * q + 1] = order_key(m4.y);
-        keys[4 * q + 2] = order_key(m4.z);
-        keys[4 * q + 3] = order_key(m4.w);
-      }
-    } else {
-      for (int j = t; j < S; j += 256) keys[j] = order_key(mass[j]);
-    }
-    lds_barrier();
-
-    // ---- top-k of this step's mass: the k-th largest key by four 8-bit radix passes ----
-    // Every wave scans the pass's histogram itself, so a pass costs one barrier.
+    // ---- top-k of this step's mass: the k-th largest key by radix passes ----
+    // Every key lies between the largest and the smallest, so the bits above the highest bit
+    // where those two differ are common to all keys and need no pass; the passes take 8-bit
+    // digits from that bit down (the last one narrower).  Every wave scans the pass's
+    // histogram itself, so a pass costs one barrier.
+    const uint4 x4 = *(const uint4*)wext[0], n4 = *(const uint4*)wext[1];
+    kmax = max(max(x4.x, x4.y), max(x4.z, x4.w));
+    kmin = min(min(n4.x, n4.y), min(n4.z, n4.w));
     const uint32_t want = (uint32_t)min(k, S);
-    uint32_t prefix = 0, pmask = 0, rem = want;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+    const uint32_t diff = kmax ^ kmin;
+    int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest bit not common to all keys
+    // the common bits (all 32 when every key is equal: then the lowest positions are taken)
+    uint32_t pmask = top < 0 ? 0xffffffffu : top >= 31 ? 0u : ~((2u << top) - 1u);
+    uint32_t prefix = kmax & pmask, rem = want;
+    for (int pass = 0; top >= 0; ++pass) {
+      const int w = min(8, top + 1), shift = top + 1 - w;
+      const uint32_t dmask = (1u << w) - 1u;
       uint32_t* hp = hist[pass];
-#pragma unroll 4
-      for (int j = t; j < S; j += 256) {
-        const uint32_t u = keys[j];
-        if ((u & pmask) == prefix) atomicAdd(&hp[(u >> shift) & 255u], 1u);
+      // keys outside the candidate set count into this lane's discard slot (no branch)
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const bool cand = i < nv && (key[i] & pmask) == prefix;
+        atomicAdd(&hp[cand ? (key[i] >> shift) & dmask : 256u + lane], 1u);
       }
       lds_barrier();
-      // lane L owns digits 255-4L .. 252-4L (descending); inclusive scan over lanes
-      uint32_t cnt[4], own = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        cnt[e] = hp[255 - 4 * lane - e];
-        own += cnt[e];
-      }
+      // lane L owns digits 255-4L .. 252-4L (descending, one 16-byte read); inclusive scan
+      // over lanes
+      const uint4 h4 = *(const uint4*)&hp[252 - 4 * lane];
+      const uint32_t cnt[4] = {h4.w, h4.z, h4.y, h4.x};
+      const uint32_t own = (h4.x + h4.y) + (h4.z + h4.w);
       const uint32_t inc = wave_inclusive_scan(own);
       const uint32_t exc = inc - own;
       // the digit holding the rem-th largest candidate, how many of it are taken, and how
@@ -217,65 +273,41 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
       left = __builtin_amdgcn_readlane(left, src);
       size = __builtin_amdgcn_readlane(size, src);
       prefix |= digit << shift;
-      pmask |= 0xffu << shift;
+      pmask |= dmask << shift;
       rem = left;
+      top = shift - 1;
       if (left == size) break;                   // the whole digit is taken: the set is known
     }
 
-    // prefix holds the leading bytes of the k-th largest key (all four unless the passes
-    // stopped early because every key of the last digit is taken); `rem` of the keys whose
-    // leading bytes equal it are taken, lowest positions first.  Wave w walks the positions
-    // [w Q, w Q + Q) 64 at a time: ballots count the keys above and equal, the four waves'
-    // counts are exchanged once, and a second walk places every taken key at its slot in
-    // ascending position order (keys above: #above before it + min(#equal before it, rem);
-    // equal keys: #above before + #equal before, if that is below rem).  Q is a multiple of
-    // 256 so each round reads four keys per lane before any ballot.
-    const int Q = (S + 1023) / 1024 * 256;       // positions per wave, 256 per round
-    const int jb = wave * Q;
-    uint32_t ngt = 0, neq = 0;
-    for (int c = 0; c < Q; c += 256) {
-      uint32_t u[4];
+    // prefix holds the leading bits of the k-th largest key (all 32 unless the passes stopped
+    // early because every key of the last digit is taken); `rem` of the keys whose leading
+    // bits equal it are taken, lowest positions first.  An exclusive scan over threads of
+    // (keys above << 16) + keys equal gives each thread the counts before its positions; a
+    // key above goes to slot #above before + min(#equal before, rem), an equal key to
+    // #above before + #equal before if that count is below rem.
+    uint32_t own = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = keys[min(jb + c + 64 * e + lane, S - 1)] & pmask;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool in = jb + c + 64 * e + lane < S;
-        ngt += (uint32_t)__builtin_popcountll(__ballot(in && u[e] > prefix));
-        neq += (uint32_t)__builtin_popcountll(__ballot(in && u[e] == prefix));
-      }
+    for (int i = 0; i < KP; ++i) {
+      const uint32_t m = key[i] & pmask;
+      if (i < nv) own += m > prefix ? 0x10000u : (m == prefix ? 1u : 0u);
     }
-    if (lane == 0) {
-      wcnt[0][wave] = ngt;
-      wcnt[1][wave] = neq;
-    }
+    const uint32_t inc = wave_inclusive_scan(own);
+    if (lane == 63) wsum[wave] = inc;
     lds_barrier();
-    uint32_t gb = 0, eb = 0;
-    for (int q = 0; q < wave; ++q) {
-      gb += wcnt[0][q];
-      eb += wcnt[1][q];
-    }
-    for (int c = 0; c < Q; c += 256) {
-      uint32_t u[4];
+    const uint4 ws = *(const uint4*)wsum;        // one LDS read, summed by selects
+    const uint32_t before = inc - own + (wave > 0 ? ws.x : 0u) + (wave > 1 ? ws.y : 0u) +
+                            (wave > 2 ? ws.z : 0u);
+    // (no branches: a key not taken is written to this thread's discard slot)
+    uint32_t ga = before >> 16, ge = before & 0xffffu;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = keys[min(jb + c + 64 * e + lane, S - 1)] & pmask;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = jb + c + 64 * e + lane;
-        const bool in = j < S, above = in && u[e] > prefix, equal = in && u[e] == prefix;
-        const unsigned long long ba = __ballot(above), be = __ballot(equal);
-        const uint32_t ga = gb + __builtin_amdgcn_mbcnt_hi(
-                                     (uint32_t)(ba >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ba, 0u));
-        const uint32_t ge = eb + __builtin_amdgcn_mbcnt_hi(
-                                     (uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
-        if (above) {
-          const uint32_t slot = ga + min(ge, rem);
-          if (slot < (uint32_t)k) sTn[slot] = j;
-        } else if (equal && ge < rem && ga + ge < (uint32_t)k) {
-          sTn[ga + ge] = j;
-        }
-        gb += (uint32_t)__builtin_popcountll(ba);
-        eb += (uint32_t)__builtin_popcountll(be);
-      }
+    for (int i = 0; i < KP; ++i) {
+      const uint32_t m = key[i] & pmask;
+      const bool ab = i < nv && m > prefix, eq = i < nv && m == prefix;
+      const uint32_t slot = ab ? ga + min(ge, rem) : ga + ge;
+      const bool take = (ab || (eq && ge < rem)) && slot < (uint32_t)k;
+      sTn[take ? slot : 64u + t] = p0 + i;
+      ga += ab ? 1u : 0u;
+      ge += eq ? 1u : 0u;
     }
     for (int sl = (int)want + t; sl < k; sl += 256) sTn[sl] = -1;
     lds_barrier();
@@ -284,81 +316,92 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   // ---- rows of the new set: in flight during the cosine (row 0 without an update, so the
   // loads need no branch) ----
   u32x4 un[kMaxChunks];
+  bool emp[kMaxChunks];                          // empty slot of the new set (S < k): zero row
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = min(t + 256 * i, nch - 1);
     const int slot = c >> (cs + 1), part = (c >> cs) & 1, d0 = (c & (cpr - 1)) * EPC;
     const int j = do_update ? sTn[slot] : 0;
-    un[i] = *(const u32x4*)((part ? vc : kc) + (head_base + (j >= 0 ? j : 0)) * D + d0);
+    emp[i] = j < 0;
+    un[i] = *(const u32x4*)((part ? vh : kh) + ((j >= 0 ? j : 0) * D + d0));
   }
 
   // ---- sigma over the previous tracked set (fp64) ----
+  // One partial sum per chunk and quantity (independent chains), added in chunk order (a
+  // chunk without a tracked row adds zeros); then the 16 lanes of a row, the four rows of a
+  // wave and the four waves, each in a fixed order.  When |u| |w| = 0 the rows are equal
+  // exactly when both are all zero (a sum of squares is zero only for zero elements).
   double uw = 0.0, uu = 0.0, ww = 0.0;
-  int neq = 0;
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = t + 256 * i;
-    if (c >= nch) continue;
-    const int j = sT[c >> (cs + 1)];
-    if (j < 0 || j >= S) continue;
     double u[EPC], w[EPC];
     chunk_f64<E>(ub[i], u);
     chunk_f64<E>(uc[i], w);
+    double puw = 0.0, puu = 0.0, pww = 0.0;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      uw += u[e] * w[e];
-      uu += u[e] * u[e];
-      ww += w[e] * w[e];
-      neq |= (u[e] != w[e]);
+      puw += u[e] * w[e];
+      puu += u[e] * u[e];
+      pww += w[e] * w[e];
     }
+    uw += okc[i] ? puw : 0.0;
+    uu += okc[i] ? puu : 0.0;
+    ww += okc[i] ? pww : 0.0;
   }
   const int valid_slot = (t < k) ? (told >= 0 && told < S) : 0;
-  uw = row_sum_f64(uw);
-  uu = row_sum_f64(uu);
-  ww = row_sum_f64(ww);
-  const int wflags = (__any(neq) ? 1 : 0) | (__any(valid_slot) ? 2 : 0);
-  if ((lane & 15) == 0) {
-    red[0][wave * 4 + (lane >> 4)] = uw;
-    red[1][wave * 4 + (lane >> 4)] = uu;
-    red[2][wave * 4 + (lane >> 4)] = ww;
+  uw = rows_sum_f64(row_sum_f64(uw));
+  uu = rows_sum_f64(row_sum_f64(uu));
+  ww = rows_sum_f64(row_sum_f64(ww));
+  const int any_valid = __any(valid_slot) ? 1 : 0;
+  if (lane == 0) {
+    red[0][wave] = uw;
+    red[1][wave] = uu;
+    red[2][wave] = ww;
+    sflag[wave] = any_valid;
   }
-  if (lane == 0) sflag[wave] = wflags;
   lds_barrier();
-  float sig = 1.f;                               // thread 0: this head's sigma
+
+  if (do_update) {
+    // ---- new set out, and the tracking buffer refilled with its K||V rows (issued before
+    // the sigma below, which only thread 0 forms) ----
+    for (int sl = t; sl < k; sl += 256) T[sl] = sTn[sl];
+#pragma unroll
+    for (int i = 0; i < kMaxChunks; ++i) {
+      const int c = t + 256 * i;
+      if (c < nch) *(u32x4*)(buf + (size_t)c * EPC) = emp[i] ? u32x4{0u, 0u, 0u, 0u} : un[i];
+    }
+  }
   if (t == 0) {
     double UW = 0.0, UU = 0.0, WW = 0.0;
     int F = 0;
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < 4; ++q) {
       UW += red[0][q];
       UU += red[1][q];
       WW += red[2][q];
+      F |= sflag[q];
     }
-    for (int q = 0; q < 4; ++q) F |= sflag[q];
     double sigma;
-    if (!(F & 2)) sigma = 1.0;
+    if (!F) sigma = 1.0;
     else {
       const double den = sqrt(UU) * sqrt(WW);
-      sigma = (den == 0.0) ? ((F & 1) ? 0.0 : 1.0) : UW / den;
+      sigma = (den == 0.0) ? ((UU == 0.0 && WW == 0.0) ? 1.0 : 0.0) : UW / den;
     }
     // Report in fp32 on the side of gamma the fp64 value lies on.
     float f = (float)sigma;
     if (sigma < (double)a.gamma && !(f < a.gamma)) f = nextafterf(a.gamma, -INFINITY);
-    sig = f;
-  }
-  if (!do_update) {
-    if (t == 0) a.sigma[(size_t)b * a.Hq + h] = sig;
-    return;
-  }
-
-  // ---- new set out, and the tracking buffer refilled with its K||V rows ----
-  if (t == 0) a.sigma[(size_t)b * a.Hq + h] = sig;
-  for (int sl = t; sl < k; sl += 256) T[sl] = sTn[sl];
-#pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = t + 256 * i;
-    if (c < nch) {
-      const bool empty = sTn[c >> (cs + 1)] < 0;   // empty slot (S < k): zero row
-      *(u32x4*)(buf + (size_t)c * EPC) = empty ? u32x4{0u, 0u, 0u, 0u} : un[i];
+    a.sigma[(size_t)b * a.Hq + h] = f;
+    if (a.arrive) {
+      // The decision in the same launch: every head of sequence b adds 1 + (below gamma) << 32
+      // to the sequence's arrival word (device-scope atomic; the data travels in the word, so
+      // no other memory needs to be visible); the head that brings the count to Hq is the
+      // last, writes refresh[b] from the summed flags and resets the word for the next call.
+      unsigned long long* wd = a.arrive + (size_t)b * kDriftArriveStride;
+      const unsigned long long inc = 1ull | ((unsigned long long)(f < a.gamma ? 1 : 0) << 32);
+      const unsigned long long old = atomicAdd(wd, inc);
+      if ((uint32_t)old == (uint32_t)(a.Hq - 1)) {
+        a.refresh[b] = ((old >> 32) + (inc >> 32)) ? 1 : 0;
+        atomicExch(wd, 0ull);
+      }
     }
   }
 }
@@ -384,33 +427,40 @@ __global__ void fp8_roundtrip(const float* x, int64_t n, float scale, uint8_t* c
   }
 }
 
+// Keys per thread by row length (the update takes S <= 16384).
+template <typename E, int CH>
+void launch_drift_track(const DriftArgs& a, int upd, hipStream_t s) {
+  dim3 grid(a.Hq, a.B);
+  if (a.S <= 1024) drift_track<E, CH, 4><<<grid, 256, 0, s>>>(a, upd);
+  else if (a.S <= 4096) drift_track<E, CH, 16><<<grid, 256, 0, s>>>(a, upd);
+  else drift_track<E, CH, 64><<<grid, 256, 0, s>>>(a, upd);
+}
+
 }  // namespace
 
 hipError_t launch_drift(const DriftArgs& a, hipStream_t s) {
-  dim3 grid(a.Hq, a.B);
   const int upd = a.mass != nullptr;
-  const size_t lds = upd ? (size_t)a.S * sizeof(uint32_t) : 0;
   const int esz = a.kind == kCacheF32 ? 4 : 2;
   const int per = (a.k * 2 * a.D * esz / 16 + 255) / 256;  // chunks per thread, <= 16
   const int ch = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
   if (a.kind == kCacheF32) {
     switch (ch) {
-      case 1: drift_track<float, 1><<<grid, 256, lds, s>>>(a, upd); break;
-      case 2: drift_track<float, 2><<<grid, 256, lds, s>>>(a, upd); break;
-      case 4: drift_track<float, 4><<<grid, 256, lds, s>>>(a, upd); break;
-      case 8: drift_track<float, 8><<<grid, 256, lds, s>>>(a, upd); break;
-      default: drift_track<float, 16><<<grid, 256, lds, s>>>(a, upd); break;
+      case 1: launch_drift_track<float, 1>(a, upd, s); break;
+      case 2: launch_drift_track<float, 2>(a, upd, s); break;
+      case 4: launch_drift_track<float, 4>(a, upd, s); break;
+      case 8: launch_drift_track<float, 8>(a, upd, s); break;
+      default: launch_drift_track<float, 16>(a, upd, s); break;
     }
   } else {
     switch (ch) {
-      case 1: drift_track<bf16_t, 1><<<grid, 256, lds, s>>>(a, upd); break;
-      case 2: drift_track<bf16_t, 2><<<grid, 256, lds, s>>>(a, upd); break;
-      case 4: drift_track<bf16_t, 4><<<grid, 256, lds, s>>>(a, upd); break;
-      default: drift_track<bf16_t, 8><<<grid, 256, lds, s>>>(a, upd); break;
+      case 1: launch_drift_track<bf16_t, 1>(a, upd, s); break;
+      case 2: launch_drift_track<bf16_t, 2>(a, upd, s); break;
+      case 4: launch_drift_track<bf16_t, 4>(a, upd, s); break;
+      default: launch_drift_track<bf16_t, 8>(a, upd, s); break;
     }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.arrive) return e;
   drift_decide<<<a.B, 64, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -109,9 +109,14 @@ struct DriftArgs {
   const float* mass;     // [B, Hq, S] or null
   float* sigma;          // [B, Hq]
   uint8_t* refresh;      // [B]
+  // arrival words, one per sequence at a 128-byte stride (zero on entry, left zero), or null:
+  // the decision is then taken by a second kernel
+  unsigned long long* arrive;
   int B, Hq, Hkv, S, D, k, kind;
   float gamma;
 };
+
+constexpr int kDriftArriveStride = 16;  // 64-bit words between two sequences' arrival words
 
 hipError_t launch_drift(const DriftArgs& a, hipStream_t s);
 

@@ -306,10 +306,20 @@ DLLM_API dllm_status dllm_facache_attention(const dllm_cache *c, void *q_cache,
  *                sigma_out < gamma reproduces the fp64 decision exactly.
  *   refresh_out  device, [B] uint8: 1 iff min over heads of sigma < gamma, i.e. the later
  *                layers of sequence b should be recomputed.
- * Errors: DLLM_EUNSUPPORTED for FP8 caches. */
+ *   workspace    device, >= dllm_drift_workspace_bytes(B) bytes, 8-byte aligned, or NULL.
+ *                With a workspace the decision is taken in the same launch (one arrival
+ *                word per sequence, 128 bytes apart); the words must be zero when the
+ *                workspace is first used (fill it with zeros once after allocating it) and
+ *                every call leaves them zero.  Calls that share a workspace must not overlap
+ *                in time (same stream, or ordered by events).  NULL: a second kernel takes
+ *                the decision (no state).
+ * Errors: DLLM_EINVAL; DLLM_ESIZE (workspace too small); DLLM_EUNSUPPORTED for FP8 caches,
+ * for an update with S above 16384 and for S * head_dim of 2^31 or more. */
+DLLM_API size_t dllm_drift_workspace_bytes(int32_t batch);
 DLLM_API dllm_status dllm_drift_check(const dllm_cache *c, int32_t num_q_heads, int32_t k, float gamma,
                              int32_t *track_idx, void *track_buf, const float *attn_mass,
-                             float *sigma_out, uint8_t *refresh_out, void *stream);
+                             float *sigma_out, uint8_t *refresh_out, void *workspace,
+                             size_t ws_bytes, void *stream);
 
 /* ---- The layer schedule: which rows each layer refreshes, decided on the device ---- */
 

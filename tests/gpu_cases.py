@@ -156,8 +156,12 @@ def run_workload_gpu(wl, inp, snapshot_prefill: bool = True):
     m.dllm_refresh_qkv_rope_scatter(layer.cache, h_cur, idx_t, layer.w, Hq, wl.rope_base, q)
     m.dllm_block_attention(layer.cache, q, Hq, scale, out, lse, mass if track else None)
     if track:
-        m.dllm_drift_check(layer.cache, Hq, k, wl.gamma, T, buf, mass, sigma, refresh)
+        # the step takes the decision in the same launch, as the bench does
+        dws = m.drift_workspace(B)
+        m.dllm_drift_check(layer.cache, Hq, k, wl.gamma, T, buf, mass, sigma, refresh, dws)
     torch.cuda.synchronize()
+    if track:
+        assert not dws.any(), "drift workspace not left zero"
     res.update(layer=layer, q=q.float().cpu().numpy(), out=out.float().cpu().numpy(),
                lse=lse.cpu().numpy())
     if track:

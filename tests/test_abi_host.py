@@ -131,10 +131,17 @@ def test_attention_and_drift_reject_bad_arguments_on_host():
     assert att(q=None) == dkv.DLLM_EINVAL
     assert att(n=0) == dkv.DLLM_OK
     dr = lambda cc, **kw: L.dllm_drift_check(ctypes.byref(cc), kw.get("hq", 4), kw.get("k", 32),
-                                             0.9, ADDR, ADDR, None, ADDR, ADDR, None)
+                                             0.9, ADDR, ADDR, None, ADDR, ADDR, kw.get("w"),
+                                             kw.get("wb", 0), None)
     assert dr(c, k=0) == dkv.DLLM_EINVAL and dr(c, k=65) == dkv.DLLM_EINVAL
     assert dr(c, hq=3) == dkv.DLLM_EINVAL
     assert dr(_fake_cache(dt=dkv.DLLM_FP8_E4M3)) == dkv.DLLM_EUNSUPPORTED
+    # the decision's workspace: one 128-byte line per sequence, 8-byte aligned
+    dws = L.dllm_drift_workspace_bytes(c.desc.batch)
+    assert dws == 128 * c.desc.batch and L.dllm_drift_workspace_bytes(0) == 0
+    assert dr(c, k=0, w=ADDR, wb=dws) == dkv.DLLM_EINVAL
+    assert dr(c, w=ADDR, wb=dws - 1) == dkv.DLLM_ESIZE
+    assert dr(c, w=P((1 << 41) + 4), wb=dws) == dkv.DLLM_EINVAL
     # the allocation-free call validates the same way, and refuses shapes beyond its scratch
     na = lambda cc, **kw: L.dllm_block_attention_noalloc(
         ctypes.byref(cc), kw.get("q", ADDR), 1, kw.get("hq", 4), kw.get("n", 8), 0.088, ADDR,

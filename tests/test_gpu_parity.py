@@ -361,11 +361,14 @@ def _drift_inputs(p, seed):
 
 @pytest.mark.parametrize("name", list(DRIFT_CASES))
 @pytest.mark.parametrize("update", [True, False])
-def test_drift_stagewise(name, update):
+@pytest.mark.parametrize("same_launch", [False, True])
+def test_drift_stagewise(name, update, same_launch):
     """Drift test and tracking update on identical seeded inputs: sigma to fp32 rounding of
-    the fp64 value, decisions and the new tracking set exactly, buffer refilled bitwise."""
+    the fp64 value, decisions and the new tracking set exactly, buffer refilled bitwise.
+    same_launch: the decision taken in the drift kernel through a workspace (left zero, and
+    right again on a second call) instead of by the second kernel."""
     p = DRIFT_CASES[name]
-    say(f"[drift] {name} update={update}")
+    say(f"[drift] {name} update={update} same_launch={same_launch}")
     B, Hq, Hkv, S, D, k = p["B"], p["Hq"], p["Hkv"], p["S"], p["D"], p["k"]
     kc, vc, T, buf, mass = _drift_inputs(p, 40 + len(name))
     tdt = torch.bfloat16 if p["dt"] == "bf16" else torch.float32
@@ -378,9 +381,12 @@ def test_drift_stagewise(name, update):
     sigma = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     refresh = torch.empty((B,), dtype=torch.uint8, device="cuda")
     gamma = float(np.float32(0.9))
+    dws = dkv.drift_workspace(B) if same_launch else None
     dkv.dllm_drift_check(cache, Hq, k, gamma, T_d, buf_d, mass_d if update else None, sigma,
-                         refresh)
+                         refresh, dws)
     torch.cuda.synchronize()
+    if same_launch:
+        assert not dws.any()
 
     s_ref, r_ref = oracle.drift(buf.astype(np.float64), T, kc.astype(np.float64),
                                 vc.astype(np.float64), gamma)
@@ -391,6 +397,16 @@ def test_drift_stagewise(name, update):
     np.testing.assert_array_equal(refresh.cpu().numpy()[decided], r_ref[decided])
     assert (sigma.cpu().numpy() < gamma).any(axis=1).astype(np.uint8).tolist() == \
         refresh.cpu().numpy().tolist()
+    if same_launch:
+        # a second call on the same workspace (inputs now the updated set and buffer)
+        sigma2 = torch.empty_like(sigma)
+        refresh2 = torch.full_like(refresh, 7)
+        dkv.dllm_drift_check(cache, Hq, k, gamma, T_d.clone(), buf_d.clone(), None, sigma2,
+                             refresh2, dws)
+        torch.cuda.synchronize()
+        assert not dws.any()
+        assert (sigma2.cpu().numpy() < gamma).any(axis=1).astype(np.uint8).tolist() == \
+            refresh2.cpu().numpy().tolist()
     if not update:
         assert torch.equal(T_d.cpu(), torch.from_numpy(T))
         return
