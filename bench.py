@@ -620,36 +620,53 @@ def measure_unfused_and_hbm_paths(args):
         del layers, h, y
         torch.cuda.empty_cache()
 
-    # the drift check batched over 28 layers of the GQA shape: 28 x 8 sequences in one launch
+    # the drift check batched over 28 layers of the GQA shape: 28 x 8 sequences in one launch,
+    # on a bf16 cache and on an FP8 cache (codes and one scale per row)
     wl = synth.WORKLOADS["c4"]
     Lyr = 28
     Bb, Hq, Hkv, S, D, k = wl.batch * Lyr, wl.q_heads, wl.kv_heads, wl.seq, wl.head_dim, wl.track_k
-    c = dkv.Cache(Bb, Hkv, S, D, dkv.DLLM_BF16)
-    g = torch.Generator(device=dev)
-    g.manual_seed(5)
-    c.k.copy_(torch.randn(c.k.shape, generator=g, device=dev).to(bf))
-    c.v.copy_(torch.randn(c.v.shape, generator=g, device=dev).to(bf))
-    masses = [torch.rand((Bb, Hq, S), generator=g, device=dev) for _ in range(3)]
-    T = torch.full((Bb, Hq, k), -1, dtype=torch.int32, device=dev)
-    buf = torch.zeros((Bb, Hq, k, 2, D), dtype=bf, device=dev)
-    sig = torch.empty((Bb, Hq), dtype=torch.float32, device=dev)
-    dec = torch.empty((Bb,), dtype=torch.uint8, device=dev)
-    dws = dkv.drift_workspace(Bb, dev)
-    dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[0], sig, dec, dws)
-    torch.cuda.synchronize()
-    it = [0]
+    drift_b = {}
+    for kv, tag in ((dkv.DLLM_BF16, "bf16"), (dkv.DLLM_FP8_E4M3, "fp8")):
+        c = dkv.Cache(Bb, Hkv, S, D, kv)
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        if kv == dkv.DLLM_BF16:
+            c.k.copy_(torch.randn(c.k.shape, generator=g, device=dev).to(bf))
+            c.v.copy_(torch.randn(c.v.shape, generator=g, device=dev).to(bf))
+            buf = torch.zeros((Bb, Hq, k, 2, D), dtype=bf, device=dev)
+            row_bytes = D * 2
+        else:
+            c.k.copy_(torch.randint(0, 0x7f, c.k.shape, generator=g, device=dev, dtype=torch.uint8))
+            c.v.copy_(torch.randint(0, 0x7f, c.v.shape, generator=g, device=dev, dtype=torch.uint8))
+            c.k_scale.fill_(0.01)
+            c.v_scale.fill_(0.02)
+            buf = torch.zeros(dkv.track_buffer_bytes(c, Hq, k),
+                              dtype=torch.uint8, device=dev)
+            row_bytes = D + 4
+        masses = [torch.rand((Bb, Hq, S), generator=g, device=dev) for _ in range(3)]
+        T = torch.full((Bb, Hq, k), -1, dtype=torch.int32, device=dev)
+        sig = torch.empty((Bb, Hq), dtype=torch.float32, device=dev)
+        dec = torch.empty((Bb,), dtype=torch.uint8, device=dev)
+        dws = dkv.drift_workspace(Bb, dev)
+        dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[0], sig, dec, dws)
+        torch.cuda.synchronize()
+        it = [0]
 
-    def drift(_):
-        it[0] += 1
-        dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[it[0] % 3], sig, dec, dws)
+        def drift(_):
+            it[0] += 1
+            dkv.dllm_drift_check(c, Hq, k, wl.gamma, T, buf, masses[it[0] % 3], sig, dec, dws)
 
-    us = burst_us(torch, drift, max(10, args.steps), [None])
-    byts = Bb * Hq * (3 * k * 2 * D * 2 + S * 4 + k * 8)
-    drift_b = {"workload": f"{Lyr} layers x B=8 of the GQA shape (28 query heads, S=2048, k=32) "
-                           "in one launch", "us": round(us, 2), "algorithmic_bytes": byts,
-               "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1),
-               "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"[bench] drift batched over {Lyr} layers: {us:.1f} us, {drift_b['achieved_GBs']} GB/s")
+        us = burst_us(torch, drift, max(10, args.steps), [None])
+        byts = Bb * Hq * (3 * k * 2 * row_bytes + S * 4 + k * 8)
+        drift_b[tag] = {"workload": f"{Lyr} layers x B=8 of the GQA shape (28 query heads, "
+                                   f"S=2048, k=32), {tag} cache, in one launch",
+                        "us": round(us, 2), "algorithmic_bytes": byts,
+                        "achieved_GBs": round(byts / (us * 1e-6) / 1e9, 1),
+                        "frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] drift batched over {Lyr} layers ({tag}): {us:.1f} us, "
+            f"{drift_b[tag]['achieved_GBs']} GB/s")
+        del c, masses, T, buf
+        torch.cuda.empty_cache()
     # attainable rates beside the datasheet peaks: a device copy, and a loop of independent
     # MFMAs on register operands
     nb = 1 << 30
@@ -672,8 +689,6 @@ def measure_unfused_and_hbm_paths(args):
         attain[f"mfma_{name}_frac_of_peak"] = round(tf / MFMA_PEAK_TFLOPS[name[:4].rstrip("_")], 4)
     log("[bench] attainable: copy {} GB/s; ".format(attain["copy_GBs"]) +
         ", ".join(f"{k[5:-7]} {v} TFLOP/s" for k, v in attain.items() if k.endswith("TFLOPs")))
-    del c, masses, T, buf
-    torch.cuda.empty_cache()
     return ab, {"row_scatter": scatter, "drift_batched": drift_b, "attainable": attain}
 
 

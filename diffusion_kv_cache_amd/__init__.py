@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "DLLM_OK", 1: "DLLM_EINVAL", 2: "DLLM_ESIZE", 3: "DLLM_EUNSUP
                 4: "DLLM_ELAUNCH"}
 EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatter",
            "dllm_refresh_workspace_bytes", "dllm_attention_workspace_bytes",
-           "dllm_block_attention", "dllm_drift_workspace_bytes", "dllm_drift_check",
+           "dllm_block_attention", "dllm_track_buffer_bytes", "dllm_drift_workspace_bytes",
+           "dllm_drift_check",
            "dllm_fp8_e4m3_roundtrip",
            "dllm_set_options", "dllm_block_attention_noalloc", "dllm_facache_state_bytes",
            "dllm_facache_attention", "dllm_refresh_qkv_rope_scatter_varlen",
@@ -139,6 +140,8 @@ def _load():
     lib.dllm_mfma_rate_probe.restype = i32
     lib.dllm_mfma_rate_probe.argtypes = [i32, i32, i32, i32, P, P]
     lib.dllm_drift_check.restype = i32
+    lib.dllm_track_buffer_bytes.restype = ctypes.c_size_t
+    lib.dllm_track_buffer_bytes.argtypes = [ctypes.POINTER(CacheDesc), i32, i32]
     lib.dllm_drift_workspace_bytes.restype = ctypes.c_size_t
     lib.dllm_drift_workspace_bytes.argtypes = [i32]
     lib.dllm_drift_check.argtypes = [ctypes.POINTER(CCache), i32, i32, ctypes.c_float, P, P, P, P,
@@ -417,6 +420,11 @@ def dllm_facache_attention(cache: Cache, q_cache: torch.Tensor, q_block: torch.T
         _stream(stream)))
 
 
+def track_buffer_bytes(cache: Cache, num_q_heads: int, k: int) -> int:
+    """Bytes of dllm_drift_check's tracking buffer for this cache (FP8: codes, then scales)."""
+    return int(lib.dllm_track_buffer_bytes(ctypes.byref(cache.desc), num_q_heads, k))
+
+
 def drift_workspace(batch: int, device="cuda") -> torch.Tensor:
     """A zero-filled workspace for dllm_drift_check's decision in the same launch (every call
     leaves it zero; calls that share it must not overlap)."""
@@ -427,13 +435,17 @@ def drift_workspace(batch: int, device="cuda") -> torch.Tensor:
 def dllm_drift_check(cache: Cache, num_q_heads: int, k: int, gamma: float,
                      track_idx: torch.Tensor, track_buf: torch.Tensor, attn_mass, sigma_out,
                      refresh_out, workspace=None, stream=None):
-    """track_idx [B,Hq,k] int32 (in/out), track_buf [B,Hq,k,2,D] cache dtype (in/out),
-    attn_mass [B,Hq,S] fp32 or None, sigma_out [B,Hq] fp32, refresh_out [B] uint8,
+    """track_idx [B,Hq,k] int32 (in/out), track_buf [B,Hq,k,2,D] cache dtype (in/out; FP8
+    caches: flat uint8 of track_buffer_bytes, codes then row scales), attn_mass [B,Hq,S] fp32
+    or None, sigma_out [B,Hq] fp32, refresh_out [B] uint8,
     workspace from drift_workspace(B) or None (the decision by a second kernel)."""
     d = cache.desc
     B, Hq = d.batch, num_q_heads
     _expect(track_idx, "track_idx", (B, Hq, k), torch.int32)
-    _expect(track_buf, "track_buf", (B, Hq, k, 2, d.head_dim), _TORCH_DTYPE[d.kv_dtype])
+    if d.kv_dtype == DLLM_FP8_E4M3:
+        _expect(track_buf, "track_buf", (track_buffer_bytes(cache, Hq, k),), torch.uint8)
+    else:
+        _expect(track_buf, "track_buf", (B, Hq, k, 2, d.head_dim), _TORCH_DTYPE[d.kv_dtype])
     if attn_mass is not None:
         _expect(attn_mass, "attn_mass", (B, Hq, d.max_seq), torch.float32)
     _expect(sigma_out, "sigma_out", (B, Hq), torch.float32)

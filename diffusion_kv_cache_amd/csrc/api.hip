@@ -576,6 +576,17 @@ dllm_status dllm_facache_attention(const dllm_cache* c, void* q_cache, const voi
   return finish(dllm::launch_facache(a, s), s, "facache attention");
 }
 
+size_t dllm_track_buffer_bytes(const dllm_cache_desc* d, int32_t num_q_heads, int32_t k) {
+  if (!d || d->batch <= 0 || d->head_dim <= 0 || num_q_heads <= 0 || k <= 0) return 0;
+  const size_t rows = (size_t)d->batch * num_q_heads * k * 2;
+  switch (d->kv_dtype) {
+    case DLLM_F32: return rows * d->head_dim * 4;
+    case DLLM_BF16: return rows * d->head_dim * 2;
+    case DLLM_FP8_E4M3: return rows * (d->head_dim + sizeof(float));
+    default: return 0;
+  }
+}
+
 size_t dllm_drift_workspace_bytes(int32_t batch) {
   if (batch <= 0) return 0;
   return (size_t)batch * dllm::kDriftArriveStride * sizeof(unsigned long long);
@@ -588,7 +599,6 @@ dllm_status dllm_drift_check(const dllm_cache* c, int32_t num_q_heads, int32_t k
   dllm_status st = check_cache(c);
   if (st) return st;
   const dllm_cache_desc& d = c->desc;
-  if (d.kv_dtype == DLLM_FP8_E4M3) return fail(DLLM_EUNSUPPORTED, "drift check on FP8 caches");
   if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
     return fail(DLLM_EINVAL, "num_q_heads %d is not a positive multiple of Hkv %d", num_q_heads,
                 d.num_kv_heads);
@@ -609,6 +619,8 @@ dllm_status dllm_drift_check(const dllm_cache* c, int32_t num_q_heads, int32_t k
   dllm::DriftArgs a;
   a.kc = c->k;
   a.vc = c->v;
+  a.ks = c->k_scale;
+  a.vs = c->v_scale;
   a.track_idx = track_idx;
   a.track_buf = track_buf;
   a.mass = attn_mass;

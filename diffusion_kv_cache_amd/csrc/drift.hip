@@ -122,6 +122,20 @@ __device__ __forceinline__ void chunk_f64(const u32x4& w, double* out) {
   }
 }
 
+// Sixteen E4M3 codes (one 16-byte chunk) as fp64 values code * scale (exact: a 4-bit
+// significand times a 24-bit one).
+__device__ __forceinline__ void chunk_f64_e4m3(const u32x4& w, double scale, double* out) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t lo, hi;
+    e4m3x4_to_bf16x4(w[e], lo, hi);
+    out[4 * e] = (double)__uint_as_float(lo << 16) * scale;
+    out[4 * e + 1] = (double)__uint_as_float(lo & 0xffff0000u) * scale;
+    out[4 * e + 2] = (double)__uint_as_float(hi << 16) * scale;
+    out[4 * e + 3] = (double)__uint_as_float(hi & 0xffff0000u) * scale;
+  }
+}
+
 // One workgroup per (b, h): the drift of the previous tracked set, then (do_update) the new
 // top-k set and the tracking-buffer refill.  The old set and the buffer are read before any
 // write.  Global loads that do not depend on each other are issued together (old positions,
@@ -133,8 +147,11 @@ __device__ __forceinline__ void chunk_f64(const u32x4& w, double* out) {
 // chunk, so every load is issued unconditionally, back to back.
 // KP: mass values per thread (4, 16 or 64; S <= 256 KP): thread t holds the order keys of
 // positions [t KP, t KP + KP) in registers, so position order is (thread, slot) order.
+// E: float, bf16_t or uint8_t (FP8: E4M3 codes with one fp32 scale per row, the tracking
+// buffer holding the codes and then the scales of its rows).
 template <typename E, int CH, int KP>
 __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
+  constexpr bool F8 = sizeof(E) == 1;
   constexpr int EPC = 16 / (int)sizeof(E);       // elements per 16-byte chunk
   constexpr int kMaxChunks = CH;
   const int h = blockIdx.x, b = blockIdx.y;
@@ -149,6 +166,13 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   const int cpr = D / EPC;                       // chunks per K (or V) row (power of 2)
   const int cs = __builtin_ctz(cpr);
   const int nch = k * 2 * cpr;                   // chunks of the tracked rows
+  // FP8: row scales of this KV head in the cache, and of this head's buffer rows (slot,
+  // part) at index 2 slot + part = chunk >> cs, after the codes of the whole buffer
+  const float* ksh = F8 ? a.ks + head_base / D : nullptr;
+  const float* vsh = F8 ? a.vs + head_base / D : nullptr;
+  float* bsc = F8 ? (float*)((uint8_t*)a.track_buf + (size_t)a.B * a.Hq * k * 2 * D) +
+                        ((size_t)b * a.Hq + h) * k * 2
+                  : nullptr;
 
   __shared__ double red[3][4];                   // wave sums: [quantity][wave]
   __shared__ int sflag[4];
@@ -162,10 +186,12 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   // ---- loads issued together: old positions, buffer rows, this step's mass ----
   const int told = (t < k) ? T[t] : -1;
   u32x4 ub[kMaxChunks];
+  float sb[kMaxChunks];                          // FP8: the buffer row's scale
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = min(t + 256 * i, nch - 1);
     ub[i] = *(const u32x4*)(buf + (size_t)c * EPC);
+    if constexpr (F8) sb[i] = bsc[c >> cs];
   }
   const int p0 = t * KP;                         // this thread's first position
   const int nv = do_update ? max(0, min(KP, S - p0)) : 0;  // its positions below S
@@ -212,13 +238,16 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   // as zeros in the cosine)
   u32x4 uc[kMaxChunks];
   bool okc[kMaxChunks];
+  float sc[kMaxChunks];                          // FP8: the cache row's scale
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = min(t + 256 * i, nch - 1);
     const int slot = c >> (cs + 1), part = (c >> cs) & 1, d0 = (c & (cpr - 1)) * EPC;
     const int j = sT[slot];
     okc[i] = t + 256 * i < nch && j >= 0 && j < S;
-    uc[i] = *(const u32x4*)((part ? vh : kh) + ((okc[i] ? j : 0) * D + d0));
+    const int jr = okc[i] ? j : 0;
+    uc[i] = *(const u32x4*)((part ? vh : kh) + (jr * D + d0));
+    if constexpr (F8) sc[i] = (part ? vsh : ksh)[jr];
   }
 
   if (do_update) {
@@ -317,13 +346,16 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
   // loads need no branch) ----
   u32x4 un[kMaxChunks];
   bool emp[kMaxChunks];                          // empty slot of the new set (S < k): zero row
+  float sn[kMaxChunks];                          // FP8: the new row's scale
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = min(t + 256 * i, nch - 1);
     const int slot = c >> (cs + 1), part = (c >> cs) & 1, d0 = (c & (cpr - 1)) * EPC;
     const int j = do_update ? sTn[slot] : 0;
     emp[i] = j < 0;
-    un[i] = *(const u32x4*)((part ? vh : kh) + ((j >= 0 ? j : 0) * D + d0));
+    const int jr = j >= 0 ? j : 0;
+    un[i] = *(const u32x4*)((part ? vh : kh) + (jr * D + d0));
+    if constexpr (F8) sn[i] = (part ? vsh : ksh)[jr];
   }
 
   // ---- sigma over the previous tracked set (fp64) ----
@@ -335,8 +367,13 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     double u[EPC], w[EPC];
-    chunk_f64<E>(ub[i], u);
-    chunk_f64<E>(uc[i], w);
+    if constexpr (F8) {
+      chunk_f64_e4m3(ub[i], (double)sb[i], u);
+      chunk_f64_e4m3(uc[i], (double)sc[i], w);
+    } else {
+      chunk_f64<E>(ub[i], u);
+      chunk_f64<E>(uc[i], w);
+    }
     double puw = 0.0, puu = 0.0, pww = 0.0;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
@@ -369,6 +406,8 @@ __global__ __launch_bounds__(256) void drift_track(DriftArgs a, int do_update) {
     for (int i = 0; i < kMaxChunks; ++i) {
       const int c = t + 256 * i;
       if (c < nch) *(u32x4*)(buf + (size_t)c * EPC) = emp[i] ? u32x4{0u, 0u, 0u, 0u} : un[i];
+      if constexpr (F8)                          // the row's first chunk carries its scale
+        if (c < nch && (c & (cpr - 1)) == 0) bsc[c >> cs] = emp[i] ? 0.f : sn[i];
     }
   }
   if (t == 0) {
@@ -440,7 +479,7 @@ void launch_drift_track(const DriftArgs& a, int upd, hipStream_t s) {
 
 hipError_t launch_drift(const DriftArgs& a, hipStream_t s) {
   const int upd = a.mass != nullptr;
-  const int esz = a.kind == kCacheF32 ? 4 : 2;
+  const int esz = a.kind == kCacheF32 ? 4 : a.kind == kCacheFP8 ? 1 : 2;
   const int per = (a.k * 2 * a.D * esz / 16 + 255) / 256;  // chunks per thread, <= 16
   const int ch = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 16;
   if (a.kind == kCacheF32) {
@@ -450,6 +489,12 @@ hipError_t launch_drift(const DriftArgs& a, hipStream_t s) {
       case 4: launch_drift_track<float, 4>(a, upd, s); break;
       case 8: launch_drift_track<float, 8>(a, upd, s); break;
       default: launch_drift_track<float, 16>(a, upd, s); break;
+    }
+  } else if (a.kind == kCacheFP8) {
+    switch (ch) {
+      case 1: launch_drift_track<uint8_t, 1>(a, upd, s); break;
+      case 2: launch_drift_track<uint8_t, 2>(a, upd, s); break;
+      default: launch_drift_track<uint8_t, 4>(a, upd, s); break;
     }
   } else {
     switch (ch) {

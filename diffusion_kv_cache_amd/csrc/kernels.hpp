@@ -107,6 +107,8 @@ struct DriftArgs {
   int32_t* track_idx;    // [B, Hq, k]
   void* track_buf;       // [B, Hq, k, 2, D]
   const float* mass;     // [B, Hq, S] or null
+  const float* ks;       // FP8: [B, Hkv, S] row scales of K and V (else null)
+  const float* vs;
   float* sigma;          // [B, Hq]
   uint8_t* refresh;      // [B]
   // arrival words, one per sequence at a 128-byte stride (zero on entry, left zero), or null:

@@ -295,9 +295,12 @@ DLLM_API dllm_status dllm_facache_attention(const dllm_cache *c, void *q_cache,
  *                positions (-1 = empty slot); on exit (if attn_mass != NULL) the k
  *                positions with the largest mass (ties: lower position first), sorted
  *                ascending, -1 padded when S < k
- *   track_buf    device, [B, Hq, k, 2, D] of the cache dtype, in/out: the K and V rows of
- *                the tracked positions as saved when they were chosen; refilled from the
- *                current cache on exit (if attn_mass != NULL)
+ *   track_buf    device, dllm_track_buffer_bytes(desc, Hq, k) bytes, 16-byte aligned,
+ *                in/out: the K and V rows of the tracked positions as saved when they were
+ *                chosen; refilled from the current cache on exit (if attn_mass != NULL).
+ *                bf16 / fp32 caches: [B, Hq, k, 2, D] of the cache dtype.  FP8 caches: the
+ *                codes [B, Hq, k, 2, D] uint8, then the rows' scales [B, Hq, k, 2] fp32; a
+ *                row's values are code * scale (LaCache Methodology 2), compared in fp64.
  *   attn_mass    device, [B, Hq, S] fp32 from dllm_block_attention, or NULL (no update)
  *   sigma_out    device, [B, Hq] fp32: sigma = <u, w> / (|u| |w|), u = the saved K||V rows
  *                of the previous tracked set, w = the same rows in the cache now (computed
@@ -313,8 +316,9 @@ DLLM_API dllm_status dllm_facache_attention(const dllm_cache *c, void *q_cache,
  *                every call leaves them zero.  Calls that share a workspace must not overlap
  *                in time (same stream, or ordered by events).  NULL: a second kernel takes
  *                the decision (no state).
- * Errors: DLLM_EINVAL; DLLM_ESIZE (workspace too small); DLLM_EUNSUPPORTED for FP8 caches,
- * for an update with S above 16384 and for S * head_dim of 2^31 or more. */
+ * Errors: DLLM_EINVAL; DLLM_ESIZE (workspace too small); DLLM_EUNSUPPORTED for an update
+ * with S above 16384 and for S * head_dim of 2^31 or more. */
+DLLM_API size_t dllm_track_buffer_bytes(const dllm_cache_desc *d, int32_t num_q_heads, int32_t k);
 DLLM_API size_t dllm_drift_workspace_bytes(int32_t batch);
 DLLM_API dllm_status dllm_drift_check(const dllm_cache *c, int32_t num_q_heads, int32_t k, float gamma,
                              int32_t *track_idx, void *track_buf, const float *attn_mass,

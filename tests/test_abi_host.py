@@ -135,7 +135,13 @@ def test_attention_and_drift_reject_bad_arguments_on_host():
                                              kw.get("wb", 0), None)
     assert dr(c, k=0) == dkv.DLLM_EINVAL and dr(c, k=65) == dkv.DLLM_EINVAL
     assert dr(c, hq=3) == dkv.DLLM_EINVAL
-    assert dr(_fake_cache(dt=dkv.DLLM_FP8_E4M3)) == dkv.DLLM_EUNSUPPORTED
+    # FP8 caches are tracked too: the buffer holds the codes, then one fp32 scale per row
+    f8 = _fake_cache(dt=dkv.DLLM_FP8_E4M3)
+    assert dr(f8, k=0) == dkv.DLLM_EINVAL
+    for dt, per in ((dkv.DLLM_F32, 64 * 4), (dkv.DLLM_BF16, 64 * 2), (dkv.DLLM_FP8_E4M3, 64 + 4)):
+        dd = _desc(B=3, D=64, dt=dt, group=64 if dt == dkv.DLLM_FP8_E4M3 else 0)
+        assert L.dllm_track_buffer_bytes(ctypes.byref(dd), 5, 7) == 3 * 5 * 7 * 2 * per
+    assert L.dllm_track_buffer_bytes(ctypes.byref(_desc()), 0, 7) == 0
     # the decision's workspace: one 128-byte line per sequence, 8-byte aligned
     dws = L.dllm_drift_workspace_bytes(c.desc.batch)
     assert dws == 128 * c.desc.batch and L.dllm_drift_workspace_bytes(0) == 0

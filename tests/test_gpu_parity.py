@@ -426,6 +426,98 @@ def test_drift_stagewise(name, update, same_launch):
                     np.testing.assert_array_equal(bg[b, h, t, 1], vc[b, h // G, j])
 
 
+DRIFT_FP8_CASES = {
+    "fp8_gqa": dict(B=3, Hq=6, Hkv=2, S=300, D=128, k=32),
+    "fp8_d64_k64": dict(B=2, Hq=4, Hkv=4, S=500, D=64, k=64),
+    "fp8_S_below_k": dict(B=2, Hq=2, Hkv=1, S=20, D=128, k=32),
+    # rows past 4096 keys (64 mass values per thread), k = 1
+    "fp8_long_k1": dict(B=2, Hq=2, Hkv=2, S=6000, D=128, k=1),
+}
+
+
+@pytest.mark.parametrize("name", list(DRIFT_FP8_CASES))
+@pytest.mark.parametrize("update", [True, False])
+@pytest.mark.parametrize("same_launch", [False, True])
+def test_drift_fp8(name, update, same_launch):
+    """Drift test on an FP8 cache: the tracked rows are E4M3 codes with one fp32 scale per
+    row, compared as code * scale in fp64 (the oracle's drift on the decoded values); the new
+    set exact, the buffer refilled with the cache's codes and scales bitwise."""
+    p = DRIFT_FP8_CASES[name]
+    say(f"[drift fp8] {name} update={update} same_launch={same_launch}")
+    B, Hq, Hkv, S, D, k = p["B"], p["Hq"], p["Hkv"], p["S"], p["D"], p["k"]
+    G = Hq // Hkv
+    rng = np.random.default_rng(90 + len(name))
+    kcod, ksc, kdq = oracle.fp8_quantize_rows(rng.standard_normal((B, Hkv, S, D)) * 0.7)
+    vcod, vsc, vdq = oracle.fp8_quantize_rows(rng.standard_normal((B, Hkv, S, D)) * 1.3)
+    T = -np.ones((B, Hq, k), np.int32)
+    rows = np.zeros((B, Hq, k, 2, D))
+    for b in range(B):
+        for h in range(Hq):
+            if b == 0 and h == 0:
+                continue                                   # empty tracking set
+            take = min(k, S) - (1 if (b, h) == (1, 1) and min(k, S) > 1 else 0)
+            pos = np.sort(rng.choice(S, size=take, replace=False)).astype(np.int32)
+            T[b, h, :take] = pos
+            alpha = rng.uniform(0.3, 1.0)
+            for t, j in enumerate(pos):
+                base = np.stack([kdq[b, h // G, j], vdq[b, h // G, j]])
+                rows[b, h, t] = alpha * base + math.sqrt(1 - alpha * alpha) * \
+                    rng.standard_normal((2, D))
+    bcod, bsc, bdq = oracle.fp8_quantize_rows(rows)
+    bdq[T < 0] = 0.0
+    mass = synth.uniform_mass(rng, (B, Hq, S), ties=S // 5)
+
+    cache = dkv.Cache(B, Hkv, S, D, dkv.DLLM_FP8_E4M3)
+    cache.k.copy_(torch.from_numpy(kcod))
+    cache.v.copy_(torch.from_numpy(vcod))
+    cache.k_scale.copy_(torch.from_numpy(ksc))
+    cache.v_scale.copy_(torch.from_numpy(vsc))
+    nb = dkv.track_buffer_bytes(cache, Hq, k)
+    ncod = B * Hq * k * 2 * D
+    assert nb == ncod + B * Hq * k * 2 * 4
+    buf_d = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    buf_d[:ncod].copy_(torch.from_numpy(bcod.reshape(-1)))
+    buf_d[ncod:].view(torch.float32).copy_(torch.from_numpy(bsc.reshape(-1)))
+    T_d = torch.from_numpy(T).cuda()
+    mass_d = torch.from_numpy(mass).cuda()
+    sigma = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    refresh = torch.empty((B,), dtype=torch.uint8, device="cuda")
+    gamma = float(np.float32(0.9))
+    dws = dkv.drift_workspace(B) if same_launch else None
+    dkv.dllm_drift_check(cache, Hq, k, gamma, T_d, buf_d, mass_d if update else None, sigma,
+                         refresh, dws)
+    torch.cuda.synchronize()
+    if same_launch:
+        assert not dws.any()
+
+    s_ref, r_ref = oracle.drift(bdq, T, kdq, vdq, gamma)
+    np.testing.assert_allclose(sigma.cpu().numpy(), s_ref, rtol=0, atol=2e-7)
+    assert sigma[0, 0].item() == 1.0
+    decided = np.abs(s_ref.min(axis=1) - gamma) >= 1e-5
+    np.testing.assert_array_equal(refresh.cpu().numpy()[decided], r_ref[decided])
+    assert (sigma.cpu().numpy() < gamma).any(axis=1).astype(np.uint8).tolist() == \
+        refresh.cpu().numpy().tolist()
+    if not update:
+        assert torch.equal(T_d.cpu(), torch.from_numpy(T))
+        assert torch.equal(buf_d[:ncod].cpu(), torch.from_numpy(bcod.reshape(-1)))
+        return
+    T_ref = oracle.topk(mass.astype(np.float64), k)
+    np.testing.assert_array_equal(T_d.cpu().numpy(), T_ref)
+    codes = buf_d[:ncod].cpu().numpy().reshape(B, Hq, k, 2, D)
+    scales = buf_d[ncod:].view(torch.float32).cpu().numpy().reshape(B, Hq, k, 2)
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(k):
+                j = T_ref[b, h, t]
+                if j < 0:
+                    assert not codes[b, h, t].any() and not scales[b, h, t].any()
+                else:
+                    np.testing.assert_array_equal(codes[b, h, t, 0], kcod[b, h // G, j])
+                    np.testing.assert_array_equal(codes[b, h, t, 1], vcod[b, h // G, j])
+                    assert scales[b, h, t, 0] == ksc[b, h // G, j]
+                    assert scales[b, h, t, 1] == vsc[b, h // G, j]
+
+
 @pytest.mark.parametrize("scale", [1.0, 0.0123, 3.7])
 def test_fp8_codec_matches_oracle(scale):
     say(f"[fp8 codec] scale={scale}")
