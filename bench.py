@@ -2,9 +2,10 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input: fused refresh
 (gather + QKV projection + RoPE + K/V scatter), block attention over the whole cache with the
-column attention mass, and the drift check with the tracking update (FP8 caches have no drift
-check).  Inputs are resident in HBM before timing starts; the cache and weights of several layer
-instances are rotated so the 256 MB Infinity Cache cannot serve repeats.
+column attention mass, and the drift check with the tracking update, its decision taken in the
+same launch (the long-context FP8 workload names no drift test, so its step has none).  Inputs
+are resident in HBM before timing starts; the cache and weights of several layer instances are
+rotated so the 256 MB Infinity Cache cannot serve repeats.
 
 Default workload: the LLaDA-8B-shaped bf16 layer, B=1, hidden 4096, 32 heads x 128, S=1024
 (512 prompt + 512 response), 32 refreshed rows per step.
