@@ -688,16 +688,20 @@ def measure_unfused_and_hbm_paths(args):
             f"{drift_b[tag]['achieved_GBs']} GB/s")
         del c, masses, T, buf
         torch.cuda.empty_cache()
-    # attainable rates beside the datasheet peaks: a device copy, and a loop of independent
-    # MFMAs on register operands
+    # attainable rates beside the datasheet peaks: a device copy, a read-only stream, and a loop
+    # of independent MFMAs on register operands
     nb = 1 << 30
     src = torch.empty(nb, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     cp_us = burst_us(torch, lambda _: dst.copy_(src), 10, [None])
-    del src, dst
+    rwg = 4096
+    rout = torch.empty(rwg, dtype=torch.int32, device=dev)
+    rd_us = burst_us(torch, lambda _: dkv.dllm_read_rate_probe(src, rwg, rout), 10, [None])
+    del src, dst, rout
     wgs, iters = 256 * 8, 2048
     out = torch.empty(wgs * 4, dtype=torch.float32, device=dev)
-    attain = {"copy_GBs": round(2 * nb / (cp_us * 1e-6) / 1e9, 1)}
+    attain = {"copy_GBs": round(2 * nb / (cp_us * 1e-6) / 1e9, 1),
+              "read_GBs": round(nb / (rd_us * 1e-6) / 1e9, 1)}
     for kind, name, tile, flops in ((dkv.DLLM_BF16, "bf16_16x16x32", 16, 2 * 16 * 16 * 32 * 8),
                                     (dkv.DLLM_BF16, "bf16_32x32x16", 32, 2 * 32 * 32 * 16 * 4),
                                     (dkv.DLLM_FP8_E4M3, "fp8_16x16x128", 16, 2 * 16 * 16 * 128 * 8),
@@ -708,7 +712,7 @@ def measure_unfused_and_hbm_paths(args):
         tf = wgs * 4 * iters * flops / (us * 1e-6) / 1e12
         attain[f"mfma_{name}_TFLOPs"] = round(tf, 1)
         attain[f"mfma_{name}_frac_of_peak"] = round(tf / MFMA_PEAK_TFLOPS[name[:4].rstrip("_")], 4)
-    log("[bench] attainable: copy {} GB/s; ".format(attain["copy_GBs"]) +
+    log("[bench] attainable: copy {} GB/s, read {} GB/s; ".format(attain["copy_GBs"], attain["read_GBs"]) +
         ", ".join(f"{k[5:-7]} {v} TFLOP/s" for k, v in attain.items() if k.endswith("TFLOPs")))
     return ab, {"row_scatter": scatter, "drift_batched": drift_b, "attainable": attain}
 

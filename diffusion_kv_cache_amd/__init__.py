@@ -35,7 +35,7 @@ EXPORTS = ("dllm_cache_bytes", "dllm_cache_alloc", "dllm_refresh_qkv_rope_scatte
            "dllm_layer_step_workspace_bytes", "dllm_elastic_layer_step",
            "dllm_fp8_quantize_weight", "dllm_fp8_quantize_activations",
            "dllm_fp8_linear_workspace_bytes", "dllm_fp8_linear", "dllm_rope_rows",
-           "dllm_scatter_kv_rows", "dllm_mfma_rate_probe", "dllm_last_error")
+           "dllm_scatter_kv_rows", "dllm_mfma_rate_probe", "dllm_read_rate_probe", "dllm_last_error")
 DLLM_OPT_DEBUG, DLLM_OPT_WIDE_OFFSETS = 1, 2
 DLLM_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -139,6 +139,8 @@ def _load():
     lib.dllm_scatter_kv_rows.argtypes = [ctypes.POINTER(CCache), P, i32, i32, i32, P, i32, P]
     lib.dllm_mfma_rate_probe.restype = i32
     lib.dllm_mfma_rate_probe.argtypes = [i32, i32, i32, i32, P, P]
+    lib.dllm_read_rate_probe.restype = i32
+    lib.dllm_read_rate_probe.argtypes = [P, i64, i32, P, P]
     lib.dllm_drift_check.restype = i32
     lib.dllm_track_buffer_bytes.restype = ctypes.c_size_t
     lib.dllm_track_buffer_bytes.argtypes = [ctypes.POINTER(CacheDesc), i32, i32]
@@ -656,6 +658,16 @@ def dllm_mfma_rate_probe(kind: int, tile: int, workgroups: int, iters: int, out:
     """out [workgroups * 4] fp32; tile 16 or 32."""
     _expect(out, "out", (workgroups * 4,), torch.float32)
     _check(lib.dllm_mfma_rate_probe(kind, tile, workgroups, iters, _ptr(out), _stream(stream)))
+
+
+def dllm_read_rate_probe(buf: torch.Tensor, workgroups: int, out: torch.Tensor, stream=None):
+    """Reads every byte of the contiguous device tensor buf once; out [workgroups] int32 gets
+    the XOR of the 32-bit words each workgroup read."""
+    if not buf.is_contiguous() or buf.device.type != "cuda":
+        raise DllmError(DLLM_EINVAL, "buf: expected a contiguous cuda tensor")
+    _expect(out, "out", (workgroups,), torch.int32)
+    _check(lib.dllm_read_rate_probe(_ptr(buf), buf.numel() * buf.element_size(), workgroups,
+                                    _ptr(out), _stream(stream)))
 
 
 def dllm_fp8_e4m3_roundtrip(x: torch.Tensor, scale: float, codes: torch.Tensor,

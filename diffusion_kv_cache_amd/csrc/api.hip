@@ -962,6 +962,17 @@ dllm_status dllm_mfma_rate_probe(int32_t kind, int32_t tile, int32_t workgroups,
   return finish(dllm::launch_mfma_probe(kind, tile == 32, workgroups, iters, out, s), s, "mfma probe");
 }
 
+dllm_status dllm_read_rate_probe(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* out,
+                                 void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(DLLM_EINVAL, "bytes must be a non-negative multiple of 16");
+  if (bytes > 0 && !buf) return fail(DLLM_EINVAL, "null buf");
+  if ((uintptr_t)buf % 16) return fail(DLLM_EINVAL, "buf must be 16-byte aligned");
+  if (workgroups <= 0) return fail(DLLM_EINVAL, "workgroups must be positive");
+  if (!out) return fail(DLLM_EINVAL, "null out");
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dllm::launch_read_probe(buf, (size_t)bytes, workgroups, out, s), s, "read probe");
+}
+
 dllm_status dllm_fp8_e4m3_roundtrip(const float* x, int64_t n, float scale, uint8_t* codes,
                                     float* decoded, void* stream) {
   if (n < 0) return fail(DLLM_EINVAL, "n < 0");

@@ -194,5 +194,7 @@ hipError_t launch_scatter_kv_rows(const void* y, int ld, int k_col, int v_col, v
 
 // Attainable matrix-core rate (a loop of independent MFMAs on register operands).
 hipError_t launch_mfma_probe(int kind, int big, int workgroups, int iters, float* out, hipStream_t s);
+// Attainable read-only stream rate (bytes a multiple of 16, buf 16-byte aligned).
+hipError_t launch_read_probe(const void* buf, size_t bytes, int workgroups, uint32_t* out, hipStream_t s);
 
 }  // namespace dllm

@@ -5,7 +5,8 @@
 //   rope_rows        rotates the Q and K head columns of y in place at each row's position;
 //   scatter_kv_rows  copies each row's K and V head columns into the flat cache at
 //                    (b, g, position), 16-byte chunks, every other cache row untouched.
-// Also the attainable matrix-core rate microbenchmark of the roofline report (mfma_probe).
+// Also the attainable matrix-core rate and read-stream rate microbenchmarks of the roofline
+// report (mfma_probe, read_probe).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -137,7 +138,34 @@ __global__ __launch_bounds__(256) void mfma_probe(int iters, float* out) {
   if ((t & 63) == 0) out[blockIdx.x * 4 + (t >> 6)] = sum;
 }
 
+// Read-only stream: workgroups stride over the buffer in 16 KB steps (each thread four 16-byte
+// loads 4 KB apart, all issued before they are combined), XOR-folding every 32-bit word;
+// each workgroup writes the fold of the words it read.
+__global__ __launch_bounds__(256) void read_probe(const u32x4* __restrict__ p, size_t n, uint32_t* out) {
+  const int t = threadIdx.x;
+  uint32_t x = 0;
+  const size_t stride = (size_t)gridDim.x * 1024;
+  for (size_t i = (size_t)blockIdx.x * 1024 + t; i < n; i += stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (i + u * 256 < n) ? p[i + u * 256] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x ^= (v[u][0] ^ v[u][1]) ^ (v[u][2] ^ v[u][3]);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x ^= (uint32_t)__shfl_xor((int)x, m, kWave);
+  __shared__ uint32_t w[4];
+  if ((t & 63) == 0) w[t >> 6] = x;
+  __syncthreads();
+  if (t == 0) out[blockIdx.x] = (w[0] ^ w[1]) ^ (w[2] ^ w[3]);
+}
+
 }  // namespace
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, int workgroups, uint32_t* out, hipStream_t s) {
+  read_probe<<<workgroups, 256, 0, s>>>((const u32x4*)buf, bytes / 16, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_probe(int kind, int big, int workgroups, int iters, float* out, hipStream_t s) {
   if (kind == kCacheFP8) {

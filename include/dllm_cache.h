@@ -499,6 +499,15 @@ DLLM_API dllm_status dllm_scatter_kv_rows(const dllm_cache *c, const void *y, in
 DLLM_API dllm_status dllm_mfma_rate_probe(int32_t kind, int32_t tile, int32_t workgroups,
                                           int32_t iters, float *out, void *stream);
 
+/* Attainable read-only stream rate, the bandwidth counterpart of the probe above: reads the
+ * `bytes` bytes at buf once (device memory, 16-byte aligned, bytes a non-negative multiple of
+ * 16) with `workgroups` workgroups of 256 threads and writes no more than
+ * out[0 .. workgroups): device, the XOR of the 32-bit words each workgroup read (so the XOR
+ * of all of out is the XOR of every word of the buffer, and the read can be checked).
+ * Errors: DLLM_EINVAL, DLLM_ELAUNCH. */
+DLLM_API dllm_status dllm_read_rate_probe(const void *buf, int64_t bytes, int32_t workgroups,
+                                          uint32_t *out, void *stream);
+
 /* FP8 codec of the cache, exposed so the conversion can be checked element by element:
  * codes[i] = e4m3(x[i] / scale) (nearest even, saturating to +-448, NaN -> NaN) and
  * decoded[i] = decode(codes[i]) * scale.  x, codes, decoded: device arrays of n elements;

@@ -202,3 +202,22 @@ def test_schedule_calls_reject_bad_arguments_on_host():
     assert cp(2, 10, 24, F, F, F, F, 20, None) == EINVAL
     assert cp(2, 10, 32, None, F, F, F, 20, None) == EINVAL
     assert cp(2, 10, 32, F, F, F, F, 0, None) == dkv.DLLM_OK
+
+
+def test_probes_reject_bad_arguments_on_host():
+    lib = dkv.lib
+    F = ctypes.c_void_p(1 << 40)                     # never dereferenced
+    EINVAL = dkv.DLLM_EINVAL
+    rd = lib.dllm_read_rate_probe
+    # buf, bytes, workgroups, out, stream
+    assert rd(F, 15, 4, F, None) == EINVAL                      # not a multiple of 16
+    assert rd(F, -16, 4, F, None) == EINVAL
+    assert rd(None, 16, 4, F, None) == EINVAL
+    assert rd(ctypes.c_void_p((1 << 40) + 8), 16, 4, F, None) == EINVAL   # misaligned
+    assert rd(F, 16, 0, F, None) == EINVAL
+    assert rd(F, 16, 4, None, None) == EINVAL
+    mp = lib.dllm_mfma_rate_probe
+    assert mp(dkv.DLLM_F32, 16, 4, 4, F, None) == EINVAL
+    assert mp(dkv.DLLM_BF16, 8, 4, 4, F, None) == EINVAL
+    assert mp(dkv.DLLM_BF16, 16, 0, 4, F, None) == EINVAL
+    assert mp(dkv.DLLM_BF16, 16, 4, 4, None, None) == EINVAL

@@ -92,6 +92,34 @@ def test_unfused_scatter_debug_mode_rejects_a_bad_list():
         dkv.dllm_set_options(prev)
 
 
+@pytest.mark.parametrize("words,wgs", [(0, 4), (4 * 1000003, 37), (4 * 1024 * 64, 8)])
+def test_read_rate_probe_reads_every_word_once(words, wgs):
+    """The XOR of the per-workgroup folds equals the XOR of every 32-bit word of the buffer
+    (a ragged tail, more workgroups than chunks, and the empty buffer)."""
+    g = torch.Generator().manual_seed(words + wgs)
+    host = torch.randint(-2**31, 2**31 - 1, (words,), dtype=torch.int32, generator=g)
+    buf = host.cuda()
+    out = torch.full((wgs,), 12345, dtype=torch.int32, device="cuda")
+    dkv.dllm_read_rate_probe(buf, wgs, out)
+    torch.cuda.synchronize()
+    folds = out.cpu().numpy().view(np.uint32)
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32)) if words else np.uint32(0)
+    assert np.bitwise_xor.reduce(folds) == want
+    if words == 0:
+        assert not folds.any()
+
+
+def test_read_rate_probe_rejects_bad_arguments():
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    buf = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dkv.DllmError):
+        dkv.dllm_read_rate_probe(buf[:60], 4, out)          # not a multiple of 16 bytes
+    with pytest.raises(dkv.DllmError):
+        dkv.dllm_read_rate_probe(buf[4:52], 4, out)         # not 16-byte aligned
+    with pytest.raises(dkv.DllmError):
+        dkv.dllm_read_rate_probe(buf, 0, out)               # out shape does not match
+
+
 def test_mfma_rate_probe_runs_and_writes_every_wave():
     for kind in (dkv.DLLM_BF16, dkv.DLLM_FP8_E4M3):
         for tile in (16, 32):
