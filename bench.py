@@ -202,28 +202,22 @@ def measure(args, wl):
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    sp0 = torch.cuda.Event(enable_timing=True)
-    sp1 = torch.cuda.Event(enable_timing=True)
-    sp0.record()
-    torch.cuda._sleep(1 << 20)
-    sp1.record()
-    torch.cuda.synchronize()
-    spin_per_ms = (1 << 20) / sp0.elapsed_time(sp1)
+    per_ms = spin_rate(torch)
     # The K steps are timed between two events on the launch stream.  A spin kernel ahead of
     # the first event keeps the GPU busy while Python enqueues the steps (about as long as the
     # GPU runs them on the small workloads), so the interval is the GPU's, not the launcher's.
-    # The rate with the launcher in the loop is reported beside it.
-    def timed_steps(spin):
-        if spin:
-            torch.cuda._sleep(int(spin_per_ms * (2.0 * host_step_ms * args.steps + 0.2)))
+    # The rate with the launcher in the loop is timed first and reported beside it.
+    def timed_steps(spin_len_ms):
+        if spin_len_ms:
+            torch.cuda._sleep(int(per_ms * spin_len_ms))
         start.record()
         for s_ in range(args.steps):
             step(layers[(args.warmup + s_) % L])
         end.record()
         torch.cuda.synchronize()
         return start.elapsed_time(end) / args.steps
-    ms_per_step_host = timed_steps(False)
-    ms_per_step = timed_steps(True)
+    ms_per_step_host = timed_steps(0.0)
+    ms_per_step = timed_steps(spin_ms(host_step_ms * args.steps, ms_per_step_host * args.steps))
     value = M / (ms_per_step * 1e-3)
 
     # Average duration of each call: the call alone, `burst` times back to back on the launch
@@ -233,27 +227,7 @@ def measure(args, wl):
     # burst, so host-side launch cost does not show in the interval (short calls would
     # otherwise be timed at the rate the host issues them).
     burst = max(10, args.steps)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    torch.cuda._sleep(1 << 20)
-    e1.record()
-    torch.cuda.synchronize()
-    spin_per_ms = (1 << 20) / e0.elapsed_time(e1)
-    per = {}
-    for nm in names:
-        t0 = time.perf_counter()
-        for r in range(burst):
-            calls[nm](layers[r % L])
-        host_ms = (time.perf_counter() - t0) * 1e3
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(spin_per_ms * (2.0 * host_ms + 0.2)))
-        e0.record()
-        for r in range(burst):
-            calls[nm](layers[r % L])
-        e1.record()
-        torch.cuda.synchronize()
-        per[nm] = e0.elapsed_time(e1) / burst * 1e3
+    per = {nm: burst_us(torch, calls[nm], burst, layers) for nm in names}
     log(f"[bench] {wl.name}: {args.steps} steps: {ms_per_step * 1e3:.1f} us/step "
         f"({ms_per_step_host * 1e3:.1f} with the Python launcher in the loop, "
         f"{host_step_ms * 1e3:.1f} us of host time per step); per call (us, "
@@ -288,23 +262,42 @@ def measure(args, wl):
     return rec, inp
 
 
-def burst_us(torch, fn, count, layers):
-    """Average duration of fn(layer), `count` calls back to back with the layers rotating,
-    between two events on the launch stream; a spin kernel ahead of the first event keeps the
-    GPU busy while the host enqueues (host launch cost stays out of the interval)."""
+def spin_ms(host_ms: float, gpu_ms: float) -> float:
+    """Length of the spin kernel queued ahead of a timed region whose host enqueue takes host_ms
+    and whose GPU work takes about gpu_ms: a 0.5 ms head start, plus twice the time by which the
+    host would fall behind the GPU.  Where the host enqueues faster than the GPU runs, the
+    spin stays short: a long near-idle spin lets the chip lower its clocks, and the work after
+    it then starts slow (measured: 2-3% on the MFMA-bound workloads)."""
+    return 0.5 + 2.0 * max(0.0, host_ms - 0.5 * gpu_ms)
+
+
+def spin_rate(torch):
+    """Spin-kernel cycles per millisecond on this GPU."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     torch.cuda._sleep(1 << 20)
     e1.record()
     torch.cuda.synchronize()
-    spin_per_ms = (1 << 20) / e0.elapsed_time(e1)
+    return (1 << 20) / e0.elapsed_time(e1)
+
+
+def burst_us(torch, fn, count, layers):
+    """Average duration of fn(layer), `count` calls back to back with the layers rotating,
+    between two events on the launch stream; a spin kernel ahead of the first event keeps the
+    GPU busy while the host enqueues (host launch cost stays out of the interval)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    per_ms = spin_rate(torch)
     t0 = time.perf_counter()
+    e0.record()
     for r in range(count):
         fn(layers[r % len(layers)])
+    e1.record()
     host_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(spin_per_ms * (2.0 * host_ms + 0.2)))
+    gpu_ms = e0.elapsed_time(e1)                 # with the launcher in the loop: an upper bound
+    torch.cuda._sleep(int(per_ms * spin_ms(host_ms, gpu_ms)))
     e0.record()
     for r in range(count):
         fn(layers[r % len(layers)])
@@ -836,8 +829,8 @@ def cpu_baseline(wl, inp, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2", choices=sorted(synth.WORKLOADS),
                     help="the headline workload of the JSON line")
     ap.add_argument("--also", default="c3,c4,c5",

@@ -19,8 +19,8 @@ typedef uint16_t bf16_t;  // raw bf16 bits in memory
 
 constexpr int kWave = 64;
 // Fixed number of K-partitions of the projection: every output element is
-// (((0 + P0) + P1) + ... + P7), each Pp an MFMA chain over its partition in ascending k.
-constexpr int kKSplit = 8;
+// (((0 + P0) + P1) + P2) + P3, each Pp an MFMA chain over its partition in ascending k.
+constexpr int kKSplit = 4;
 
 enum CacheKind : int { kCacheF32 = DLLM_F32, kCacheBF16 = DLLM_BF16, kCacheFP8 = DLLM_FP8_E4M3 };
 

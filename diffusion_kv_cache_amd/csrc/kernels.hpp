@@ -33,8 +33,8 @@ struct RefreshArgs {
 
 // Rows (B * n) up to which a bf16 refresh takes the split-K path.
 constexpr int kSplitKMaxRows = 64;
-// Largest hidden size of the split-K path (its LDS slice is 32 x H/8 bf16).
-constexpr int kSplitKMaxHidden = 16384;
+// Largest hidden size of the split-K path (its LDS slice is 32 x H/4 bf16, 128 KB at most).
+constexpr int kSplitKMaxHidden = 8192;
 bool refresh_uses_splitk(int act, int M, int H);
 size_t refresh_workspace_bytes(int act, int M, int N, int H);
 size_t splitk_workspace_bytes(int M, int N);

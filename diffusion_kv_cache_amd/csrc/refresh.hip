@@ -9,8 +9,8 @@
 // RoPECache holds post-projection, post-RoPE states; Methodology 2 -- 1 x 128 FP8 groups.
 //
 // Reduction order (identical here and in the split-K path, for any M and tiling): each output
-// element is (((0 + P0) + P1) + ... + P7), where Pp is the chain of 16x16 MFMAs over the p-th
-// eighth of H in ascending k, each MFMA taking k0..k0+31 (bf16) or k0..k0+3 (fp32) with lane
+// element is (((0 + P0) + P1) + P2) + P3, where Pp is the chain of 16x16 MFMAs over the p-th
+// quarter of H in ascending k, each MFMA taking k0..k0+31 (bf16) or k0..k0+3 (fp32) with lane
 // group l/16 holding the slots k0 + 8(l/16) .. +7 (bf16) or k0 + l/16 (fp32).  A row's
 // result is therefore independent of n and of the other rows: a step stores exactly what a
 // refresh of all S rows would.
@@ -485,45 +485,31 @@ hipError_t launch_gemm(const RefreshArgs& a, hipStream_t s) {
 }
 
 template <typename T, int KIND, int D, int BKC>
-hipError_t launch_tiled(const RefreshArgs& a, int tm, hipStream_t s) {
-  const int heads = a.Hq + 2 * a.Hkv;
-  if (tm == 128) {
-    dim3 grid(heads, (a.M + 127) / 128);
-    refresh_tiled<T, KIND, 128, D, BKC><<<grid, 256, 0, s>>>(a);
-  } else {
-    dim3 grid(heads, (a.M + 63) / 64);
-    refresh_tiled<T, KIND, 64, D, BKC><<<grid, 256, 0, s>>>(a);
-  }
+hipError_t launch_tiled(const RefreshArgs& a, hipStream_t s) {
+  dim3 grid(a.Hq + 2 * a.Hkv, (a.M + 63) / 64);
+  refresh_tiled<T, KIND, 64, D, BKC><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
-}
-
-template <typename T, int KIND, int D>
-hipError_t launch_tiled_bk(const RefreshArgs& a, int tm, hipStream_t s) {
-  const int part = a.H / kKSplit;
-  constexpr int EPC = 16 / (int)sizeof(T);
-  if (part % (8 * EPC) == 0) return launch_tiled<T, KIND, D, 8>(a, tm, s);
-  return launch_tiled<T, KIND, D, 4>(a, tm, s);
 }
 
 template <int D>
 hipError_t launch_d(const RefreshArgs& a, hipStream_t s) {
-  if (a.act == DLLM_F32) return launch_tiled_bk<float, kCacheF32, D>(a, 64, s);
+  // H is a multiple of 256 (checked at the boundary), so each of the four partitions holds
+  // whole 64-wide k stages (32-wide for fp32).
+  if ((a.H / kKSplit) % 64) return hipErrorInvalidValue;
+  if (a.act == DLLM_F32) return launch_tiled<float, kCacheF32, D, 8>(a, s);
   // 128 rows x one head per workgroup, eight waves of 32 rows x half the head's column pairs.
   // Small M streams W at the HBM rate and wants a third stage in flight; large M wants the
   // occupancy of two stages.
   // At most 256 rows (two row tiles, fewer workgroups than compute units, one per CU) run
   // sixteen waves of 16 rows for D = 128: the extra waves hide the stage latency (49.2 against
   // 50.2 us on a 256-row, 4096-hidden step); with more rows two 8-wave workgroups share a CU.
-  const bool bk8 = (a.H / kKSplit) % 64 == 0;
   const bool deep = a.M <= 512;
   const bool wide = D == 128 && a.M <= 256;
   constexpr int WW = D == 128 ? 8 : 4;
   if (a.kind == kCacheFP8) {
-    if (!bk8) return launch_gemm<kCacheFP8, 128, D, 4, 2, (D == 64 ? 2 : 4)>(a, s);
     if (wide) return launch_gemm<kCacheFP8, 128, D, 8, 3, WW>(a, s);
     return deep ? launch_gemm<kCacheFP8, 128, D, 8, 3, 4>(a, s) : launch_gemm<kCacheFP8, 128, D, 8, 2, 4>(a, s);
   }
-  if (!bk8) return launch_gemm<kCacheBF16, 128, D, 4, 2, (D == 64 ? 2 : 4)>(a, s);
   if (wide) return launch_gemm<kCacheBF16, 128, D, 8, 3, WW>(a, s);
   return deep ? launch_gemm<kCacheBF16, 128, D, 8, 3, 4>(a, s) : launch_gemm<kCacheBF16, 128, D, 8, 2, 4>(a, s);
 }

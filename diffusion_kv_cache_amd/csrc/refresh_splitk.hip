@@ -1,14 +1,14 @@
 // Refresh for small M (a block step of one or a few sequences): the weight stream dominates,
-// so the projection is split over the eight fixed K-partitions across workgroups.
+// so the projection is split over the four fixed K-partitions across workgroups.
 //
-//   refresh_partial: workgroup (128 output columns, partition p, 32 rows).  The 32 x H/8 slice
+//   refresh_partial: workgroup (192 output columns, partition p, 32 rows).  The 32 x H/4 slice
 //     of the gathered hidden rows is staged once in LDS with coalesced 16-byte loads; each of
-//     the eight waves streams 16 W rows of that partition from global memory with a deep
+//     the twelve waves streams 16 W rows of that partition from global memory with a deep
 //     register prefetch and chains 16x16x32 MFMAs over the partition in ascending k.  The
 //     partition's fp32 tile goes to the workspace as whole rows (staged in LDS).
-//   refresh_reduce: adds the eight partitions in order ((0 + P0) + P1) + ... + P7 -- exactly the
-//     arithmetic of the tiled kernel -- rotates the Q and K pairs (i, i + D/2), and writes Q,
-//     K and V rows (bf16, or per-row FP8 with its fp32 scale).
+//   refresh_reduce: adds the four partitions in order (((0 + P0) + P1) + P2) + P3 -- exactly
+//     the arithmetic of the tiled kernel -- rotates the Q and K pairs (i, i + D/2), and writes
+//     Q, K and V rows (bf16, or per-row FP8 with its fp32 scale).
 //
 // What it computes: Flash-dLLM news summary (skillfed.io), memory paragraph -- projection,
 // RoPE and cache write of the refreshed rows; LaCache (gist.science), Technical Summary,
@@ -22,11 +22,15 @@ namespace dllm {
 namespace {
 
 constexpr int kPrefetch = 8;   // k-steps of W in flight per wave
-constexpr int kPartLd = 132;   // floats per staged partial row (128 + 4: no bank conflicts)
+constexpr int kPartWaves = 12;                 // waves per workgroup, 16 columns each
+constexpr int kPartCols = 16 * kPartWaves;     // output columns per workgroup
+constexpr int kPartLd = kPartCols + 4;         // floats per staged partial row (no bank conflicts)
 
-// Three workgroups per CU (6 waves per SIMD) keep all 768 workgroups of a 4096-hidden,
-// 12288-column step resident at once.
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6)))
+// A 4096-hidden, 12288-column step is 4 x 64 workgroups: one per CU, three waves per SIMD,
+// each wave streaming 32 KB of W.  (Eight partitions of 128-column workgroups, three per CU,
+// took 27.0 against 25.1 us for the pair of kernels on that step: the partials they write and
+// read back are twice as large.)  Up to 64 rows, two workgroups share a CU.
+__global__ __launch_bounds__(64 * kPartWaves) __attribute__((amdgpu_waves_per_eu(6)))
 void refresh_partial(RefreshArgs a, float* part) {
   extern __shared__ u32x4 As[];                  // [32 rows][cpr chunks], swizzled
   // Rows present (a variable-length batch may hold fewer than its capacity): they set the
@@ -45,7 +49,7 @@ void refresh_partial(RefreshArgs a, float* part) {
   // the 32 row positions, then the gathered A slice global -> LDS by DMA (each lane fetches
   // the source chunk that lands, swizzled, at its LDS slot).  Rows past M gather the last
   // valid row: their accumulators are never stored.
-  const int col = blockIdx.y * 128 + wave * 16 + l16;  // columns past N compute, not stored
+  const int col = blockIdx.y * kPartCols + wave * 16 + l16;  // columns past N compute, not stored
   const bf16_t* wr = (const bf16_t*)a.w + (size_t)min(col, N - 1) * a.H + kb + lg * 8;
   const int steps = Lp / 32;
   u32x4 wv[kPrefetch];
@@ -59,7 +63,7 @@ void refresh_partial(RefreshArgs a, float* part) {
   lds_barrier();
   const bf16_t* hid = (const bf16_t*)a.hidden;
   const int nblk = 32 * cpr / 64;                // 1 KB DMA blocks of the A slice
-  for (int blk = wave; blk < nblk; blk += 8) {
+  for (int blk = wave; blk < nblk; blk += kPartWaves) {
     const int P = blk * 64 + lane;               // chunk slot in As
     const int r = P / cpr, j = P % cpr;
     const bf16_t* src = hid + (size_t)s_row[r] * a.H + kb + (j ^ (r & mask)) * 8;
@@ -93,8 +97,8 @@ void refresh_partial(RefreshArgs a, float* part) {
   for (int u = 0; u < kPrefetch; ++u)
     if (s0 + u < steps) step(s0 + u, wv[u]);
 
-  // The 32 x 128 partial tile goes out as whole rows: staged in LDS (over the A slice, which
-  // every wave is done reading), then 16-byte stores of 512-byte row segments.
+  // The 32 x 192 partial tile goes out as whole rows: staged in LDS (over the A slice, which
+  // every wave is done reading), then 16-byte stores of 768-byte row segments.
   __syncthreads();
   float* T = (float*)As;                         // [32][kPartLd]
 #pragma unroll
@@ -102,10 +106,11 @@ void refresh_partial(RefreshArgs a, float* part) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) T[(rt * 16 + lg * 4 + v) * kPartLd + wave * 16 + l16] = acc[rt][v];
   __syncthreads();
+  constexpr int V4 = kPartCols / 4;              // 16-byte vectors per staged row
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int id = u * 512 + t, r = id >> 5, c4 = (id & 31) * 4;
-    const int m = m0 + r, cc = blockIdx.y * 128 + c4;
+  for (int u = 0; u < 32 * V4 / (64 * kPartWaves); ++u) {
+    const int id = u * 64 * kPartWaves + t, r = id / V4, c4 = (id % V4) * 4;
+    const int m = m0 + r, cc = blockIdx.y * kPartCols + c4;
     if (m < a.M && cc < N)
       *(float4*)(part + ((size_t)p * a.M + m) * N + cc) = *(const float4*)(T + r * kPartLd + c4);
   }
@@ -218,10 +223,10 @@ size_t splitk_workspace_bytes(int M, int N) { return (size_t)kKSplit * M * N * s
 
 hipError_t launch_refresh_splitk(const RefreshArgs& a, float* part, hipStream_t s) {
   const int N = (a.Hq + 2 * a.Hkv) * a.D;
-  dim3 grid(kKSplit, (N + 127) / 128, (a.M + 31) / 32);
+  dim3 grid(kKSplit, (N + kPartCols - 1) / kPartCols, (a.M + 31) / 32);
   const size_t lds = std::max((size_t)32 * (a.H / kKSplit) * sizeof(bf16_t),
                               (size_t)32 * kPartLd * sizeof(float));
-  refresh_partial<<<grid, 512, lds, s>>>(a, part);
+  refresh_partial<<<grid, 64 * kPartWaves, lds, s>>>(a, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return a.D == 128 ? launch_reduce<128>(a, part, s) : launch_reduce<64>(a, part, s);

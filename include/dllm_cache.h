@@ -120,9 +120,9 @@ DLLM_API dllm_status dllm_cache_alloc(const dllm_cache_desc *d, void *base, size
  *   q_out        device, [B, n, Hq, D] of act_dtype: rotated queries of the refreshed rows
  *   workspace    device scratch of ws_bytes >= dllm_refresh_workspace_bytes(...) (may be NULL
  *                when that is 0): small steps split the projection over K across workgroups
- *                and keep the eight partial sums here; contents need no initialisation
+ *                and keep the four partial sums here; contents need no initialisation
  * Writes exactly the K/V rows (b, :, refresh_idx[b, i], :) (and their scales) and q_out;
- * every other cache row is left untouched.  Each output element is the fp32 sum of eight
+ * every other cache row is left untouched.  Each output element is the fp32 sum of four
  * fixed, equal K-partitions of H, each accumulated in ascending order and added in
  * partition order, so a row's result does not depend on n or on which other rows are
  * refreshed: a step reproduces, bit for bit, what a full refresh of all rows would store.

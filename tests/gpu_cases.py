@@ -193,15 +193,15 @@ def elem_rel_err(gpu: np.ndarray, ref: np.ndarray, keep_axes, floor: float = 1e-
 # error of the fp32 projection over H terms, so a code is compared as the correct rounding of
 # SOME value within delta of the oracle's exact value, delta being a first-order bound on that
 # fp32 error, element by element:
-#   delta = depth(H) * 2^-24 * sum_k |x_k| |w_k|,   depth(H) = H / 256 + 15,
+#   delta = depth(H) * 2^-24 * sum_k |x_k| |w_k|,   depth(H) = H / 128 + 11,
 # the number of roundings along the kernel's fixed reduction order (each product of two bf16
-# values is exact in fp32): at most 6 inside one 32-deep MFMA, H/256 - 1 chained MFMAs per
-# eighth of H, 8 partition adds, and 2 for the rotation; for K the rotation mixes the pair
+# values is exact in fp32): at most 6 inside one 32-deep MFMA, H/128 - 1 chained MFMAs per
+# quarter of H, 4 partition adds, and 2 for the rotation; for K the rotation mixes the pair
 # (i, i + D/2), so the two elements' sums are added.  The encoder itself is pinned bit for
 # bit by the codec sweep (test_fp8_codec_matches_oracle), where RNE ties and saturation are
 # exercised directly.
 def fp8_depth(hidden: int) -> int:
-    return hidden // 256 + 15
+    return hidden // 128 + 11
 
 
 def kv_abs_sums(wl, x_rows: np.ndarray, w: np.ndarray, part: str, heads=None) -> np.ndarray:

@@ -104,10 +104,10 @@ def test_refresh_rejects_bad_arguments_on_host():
     assert _refresh(c, n=0) == dkv.DLLM_OK                         # nothing to do, no launch
     assert dkv.lib.dllm_refresh_qkv_rope_scatter(None, ADDR, 256, 1, ADDR, 4, ADDR, 4, 1e4, ADDR,
                                                  None, 0, None) == dkv.DLLM_EINVAL
-    # small bf16 steps split K over workgroups and need 8 fp32 partials per output
+    # small bf16 steps split K over workgroups and need 4 fp32 partials per output
     L = dkv.lib
     need = L.dllm_refresh_workspace_bytes(ctypes.byref(c.desc), 256, dkv.DLLM_BF16, 4, 4)
-    assert need == 8 * (2 * 4) * ((4 + 2 * 4) * 128) * 4
+    assert need == 4 * (2 * 4) * ((4 + 2 * 4) * 128) * 4
     assert _refresh(c, ws_bytes=need - 1) == dkv.DLLM_ESIZE
     assert _refresh(c, ws=None, ws_bytes=need) == dkv.DLLM_EINVAL
     # large steps and fp32 run as one fused kernel: no workspace

@@ -58,11 +58,11 @@ REFRESH_CASES = {
     "splitk_d128_33_heads": C(batch=2, hidden=256, q_heads=33, kv_heads=33, head_dim=128,
                               seq=48, prompt=24, block_start=24, block_len=16, seed=25),
     # a hidden size past the split-K limit: ten rows through the tiled GEMM
-    "gemm_few_rows_h16896": C(batch=1, hidden=16896, q_heads=1, kv_heads=1, head_dim=64,
+    "gemm_few_rows_h8448": C(batch=1, hidden=8448, q_heads=1, kv_heads=1, head_dim=64,
                               seq=40, prompt=20, block_start=20, block_len=10, seed=26),
     # the largest hidden size of the split-K path (its LDS slice is largest here)
-    "splitk_h16384_m64": C(batch=2, hidden=16384, q_heads=1, kv_heads=1, head_dim=128, seq=48,
-                           prompt=16, block_start=16, block_len=32, seed=28),
+    "splitk_h8192_m64": C(batch=2, hidden=8192, q_heads=1, kv_heads=1, head_dim=128, seq=48,
+                          prompt=16, block_start=16, block_len=32, seed=28),
     # 256 rows, D = 128: the sixteen-wave GEMM form, two row tiles
     "gemm_wide_m256_fp8": C(batch=8, hidden=512, q_heads=2, kv_heads=2, head_dim=128, seq=64,
                             prompt=32, cache="fp8", block_start=32, block_len=32, seed=27),
@@ -129,8 +129,8 @@ def test_refresh_parity_and_untouched_rows(name):
                                   "tiled64_bf16_ragged", "fp8_tiled_d128", "f32_d64",
                                   "f32_d128_gqa", "splitk_fp8_h768_m64", "splitk_bf16_h768_d64",
                                   "splitk_gqa_d64", "splitk_d64_129_heads",
-                                  "splitk_d128_33_heads", "splitk_h16384_m64",
-                                  "gemm_few_rows_h16896",
+                                  "splitk_d128_33_heads", "splitk_h8192_m64",
+                                  "gemm_few_rows_h8448",
                                   "gemm_wide_m256_fp8"])
 def test_step_reproduces_full_refresh_bitwise(name):
     """Cached step (prefill on H_prev, refresh of R on H_cur) stores exactly what a full
