@@ -6,7 +6,10 @@
 //   fp8_gemm          y[m, n] = sum_kb sx[m, kb] sw[n / 128, kb] sum_{k in kb} qx[m, k] qw[n, k]
 //                     One 16x16x128 MFMA covers exactly one 128-group of k, so each group's
 //                     product leaves the matrix core unscaled and is scaled and added in fp32
-//                     (tot = part * (sx sw) + tot), groups in ascending order.
+//                     (tot = part * (sx sw) + tot), groups in ascending order.  The MFMA forms
+//                     the transposed tile (weight rows as its A operand): a lane then holds one
+//                     activation row and four consecutive output columns, so it needs one row
+//                     scale per 16-row tile and stores its columns with one vector store.
 //   fp8_splitk_reduce the fixed split-K form: partial sums of contiguous group ranges added in
 //                     split order.
 #include <algorithm>
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fp8_gemm(Fp8GemmArgs a) {
       const float* Sx = (const float*)(Bt + B_BYTES);
       const float swv = s_sw[s];
       i32x8 af[RT], bfr[CT];
-      f32x4 sr[RT];
+      float sr[RT];                              // scale of this lane's row in each row tile
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int r = wm * (TM / WM) + rt * 16 + l16;
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fp8_gemm(Fp8GemmArgs a) {
         const u32x4 hi = *(const u32x4*)(A + r * kGroup + (((2 * lg + 1) ^ (r & 7)) << 4));
         af[rt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        sr[rt] = *(const f32x4*)(Sx + wm * (TM / WM) + rt * 16 + lg * 4) * swv;
+        sr[rt] = Sx[r] * swv;
       }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -225,35 +228,41 @@ __global__ __launch_bounds__(64 * WM * WN) void fp8_gemm(Fp8GemmArgs a) {
       }
       // Every product of the group first (independent MFMAs back to back, each into its own
       // registers), then the scaled adds: no add waits on the MFMA issued just before it.
+      // p[rt][ct][v]: activation row rt * 16 + l16, weight row (output column) ct * 16 + 4 lg + v.
       f32x4 p[RT][CT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) p[rt][ct] = mfma_fp8(af[rt], bfr[ct]);
+        for (int ct = 0; ct < CT; ++ct) p[rt][ct] = mfma_fp8(bfr[ct], af[rt]);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) tot[rt][ct][v] = fmaf(p[rt][ct][v], sr[rt][v], tot[rt][ct][v]);
+          for (int v = 0; v < 4; ++v) tot[rt][ct][v] = fmaf(p[rt][ct][v], sr[rt], tot[rt][ct][v]);
     }
   }
 
-  // Out: bf16 y (one split) or the fp32 partial of this split.
+  // Out: bf16 y (one split) or the fp32 partial of this split, four consecutive columns per
+  // store (N is a multiple of 128, y 8-byte and the partials 16-byte aligned).
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int rt = 0; rt < RT; ++rt) {
+    const int m = m0 + wm * (TM / WM) + rt * 16 + l16;
+    if (m >= a.M) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = m0 + wm * (TM / WM) + rt * 16 + lg * 4 + v;
-      if (m >= a.M) continue;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int n = n0 + wn * (TN / WN) + ct * 16 + l16;
-        if (n >= a.N) continue;
-        if (a.part) a.part[((size_t)split * a.M + m) * a.N + n] = tot[rt][ct][v];
-        else ((bf16_t*)a.y)[(size_t)m * a.N + n] = f32_to_bf16(tot[rt][ct][v]);
+    for (int ct = 0; ct < CT; ++ct) {
+      const int n = n0 + wn * (TN / WN) + ct * 16 + lg * 4;
+      if (n >= a.N) continue;
+      if (a.part) {
+        *(f32x4*)(a.part + ((size_t)split * a.M + m) * a.N + n) = tot[rt][ct];
+      } else {
+        uint2 o;
+        o.x = pack_bf16x2(tot[rt][ct][0], tot[rt][ct][1]);
+        o.y = pack_bf16x2(tot[rt][ct][2], tot[rt][ct][3]);
+        *(uint2*)((bf16_t*)a.y + (size_t)m * a.N + n) = o;
       }
     }
+  }
 }
 
 // y = bf16(((P0 + P1) + ...) + P_{splits-1}), four columns per thread.
