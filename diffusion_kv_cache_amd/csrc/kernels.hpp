@@ -26,7 +26,7 @@ struct RefreshArgs {
   int act;               // DLLM_F32 / DLLM_BF16
   int kind;              // cache dtype
   double rope_base;
-  float* ws;             // split-K partials [8][M][N] (small-M path only)
+  float* ws;             // split-K partials [4][M][N] (small-M path only)
   const int32_t* cu;     // [B + 1] row offsets of a variable-length batch, or null (n rows each);
                          // with cu, M is the capacity and cu[B] (read on the device) the rows
 };

@@ -39,7 +39,7 @@ void refresh_partial(RefreshArgs a, float* part) {
   if ((int)blockIdx.z * 32 >= a.M) return;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
   const int N = (a.Hq + 2 * a.Hkv) * a.D;
-  const int p = blockIdx.x;                      // partitions fastest: the eight workgroups
+  const int p = blockIdx.x;                      // partitions fastest: the four workgroups
   const int m0 = blockIdx.z * 32;                // of a column tile are dispatched together
   const int Lp = a.H / kKSplit, kb = p * Lp;
   const int cpr = Lp / 8;                        // 16-byte chunks per staged row
